@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the decode-step GEMV, shared by the oracle and the HIP path.
+
+This module draws random numbers and encodes them into the storage formats the
+two sides consume (int8 codes, IEEE binary16 bits, bf16 bits, f32). It holds
+none of the method's arithmetic: no quantization of activations, no dot
+products, no scaling. The stored bits it returns are the truth for both sides.
+
+Value distributions follow the decode workloads of "Filling in the blanks:
+Inference using Phobos" (§Fast Decode: Q8_0 weights, one scale per 32-element
+block, activation quantized once) and "One level down: #002 the same compiler
+on a GPU" (§Emitting for a GPU: the bf16 gate+up projection, 1024->7168 on the
+0.8B model, 2560->18432 on the 4B model):
+
+* Q8_0 weight codes: uniform integers in [-127, 127].
+* Q8_0 weight scales: |N(0, 1)| * 0.02 / 127 in f32, then rounded to binary16.
+* Q8_0 activation: N(0, 1) in f32 (quantized later by the method itself).
+* bf16 weights: N(0, 1) * 0.02 in f32, rounded to bf16 (nearest, ties to even).
+* bf16 activation: N(0, 1) in f32, rounded to bf16.
+* residual: N(0, 1) in f32.
+
+Every matrix j of workload `tag` draws from
+``np.random.default_rng(np.random.SeedSequence([tag, j]))`` in the order
+weights, scales, activation, residual.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+QBLOCK = 32  # elements per Q8_0 block
+
+# Workload tags (first SeedSequence word).
+TAG_Q8_GATEUP = 0
+TAG_BF16_GATEUP = 1
+TAG_Q8_STACK = 2
+TAG_BF16_4B_GATEUP = 3
+TAG_Q8_HEAD = 4
+TAG_TEST = 100
+
+
+def rng_for(tag: int, j: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(tag), int(j)]))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round f32 values to bf16 storage bits, nearest with ties to even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (r >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round f32 values to IEEE binary16 storage bits (numpy's nearest-even cast)."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def q8_weights(rng: np.random.Generator, n: int, k: int):
+    """(codes int8 [n, k], scale bits uint16 [n, k/32])."""
+    if k % QBLOCK:
+        raise ValueError("k must be a multiple of 32")
+    qw = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    s = np.abs(rng.standard_normal((n, k // QBLOCK), dtype=np.float32))
+    s *= np.float32(0.02 / 127.0)
+    return qw, f32_to_f16_bits(s)
+
+
+def activation_f32(rng: np.random.Generator, k: int) -> np.ndarray:
+    return rng.standard_normal(k, dtype=np.float32)
+
+
+def bf16_weights(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    w = rng.standard_normal((n, k), dtype=np.float32)
+    w *= np.float32(0.02)
+    return f32_to_bf16_bits(w)
+
+
+def bf16_activation(rng: np.random.Generator, k: int) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(k, dtype=np.float32))
+
+
+def residual_f32(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.standard_normal(n, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Workload shapes
+
+
+@dataclasses.dataclass(frozen=True)
+class Gemv:
+    """One projection of a decode step: ``parts`` output-row counts sharing one input of length k."""
+
+    name: str
+    parts: tuple
+    k: int
+    residual: bool = False
+
+    @property
+    def n(self) -> int:
+        return int(sum(self.parts))
+
+
+def q8_stack_08b(layers: int = 24, hidden: int = 1024, vocab: int = 151936):
+    """The 0.8B-shaped Q8_0 decode stack: per layer QKV 1024->4096 (stacked 2048/1024/1024),
+    out 2048->1024, gate+up 1024->7168 (stacked 3584/3584), down 3584->1024 with the residual
+    folded in; then the output head 1024->151936."""
+    ops = []
+    for l in range(layers):
+        ops.append(Gemv(f"L{l}.qkv", (2048, 1024, 1024), hidden))
+        ops.append(Gemv(f"L{l}.out", (hidden,), 2048))
+        ops.append(Gemv(f"L{l}.gateup", (3584, 3584), hidden))
+        ops.append(Gemv(f"L{l}.down", (hidden,), 3584, residual=True))
+    ops.append(Gemv("head", (vocab,), hidden))
+    return ops
+
+
+def q8_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
+    """Algorithmic HBM bytes of one Q8_0 GEMV: codes + scales + quantized activation + f32 out (+ residual)."""
+    b = n * k + n * (k // QBLOCK) * 2 + k + (k // QBLOCK) * 2 + n * 4
+    return b + (n * 4 if residual else 0)
+
+
+def q8_quantize_bytes(k: int) -> int:
+    """Algorithmic bytes of one activation quantize: f32 in, int8 codes + binary16 scales out."""
+    return 4 * k + k + (k // QBLOCK) * 2
+
+
+def bf16_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
+    b = 2 * n * k + 2 * k + 4 * n
+    return b + (n * 4 if residual else 0)

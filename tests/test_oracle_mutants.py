@@ -1,0 +1,66 @@
+"""Planted mistakes in the oracle: every one must be caught by at least one pin.
+
+Each mutant is a copy of oracle/oracle.c with one plausible error (a dropped term, a
+wrong sign, index, exponent or rounding rule), compiled into a temporary directory
+on the CPU. None of them touches memory outside the arrays the pins pass in.
+"""
+import os
+
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = [
+    ("f16_subnormal_exponent", "ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    ("f16_normal_exponent", "ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
+    ("f16_dropped_hidden_bit", "ldexp((double)(1024 + f), e - 25)", "ldexp((double)f, e - 25)"),
+    ("bf16_exponent", "ldexp((double)(128 + f), e - 134)", "ldexp((double)(128 + f), e - 133)"),
+    ("bf16_sign", "return sign ? -v : v;\n}\n\n/* Round", "return v;\n}\n\n/* Round"),
+    ("f16_encode_truncates", "double q = nearbyint(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));"),
+    ("f16_encode_ties_away_subnormal", "double q = nearbyint(ldexp(a, 24));", "double q = round(ldexp(a, 24));"),
+    ("f16_encode_ties_away_normal", "double q = nearbyint(ldexp(a, 10 - E));", "double q = round(ldexp(a, 10 - E));"),
+    ("quant_divisor_128", "float d = amax / 127.0f;", "float d = amax / 128.0f;"),
+    ("quant_ties_away", "float r = rintf(t);", "float r = roundf(t);"),
+    ("quant_truncates", "float r = rintf(t);", "float r = truncf(t);"),
+    ("quant_reciprocal", "float t = xb[i] / d;", "float t = xb[i] * (1.0f / d);"),
+    ("quant_uses_f16_scale", "float t = xb[i] / d;", "float t = xb[i] / (float)orc_f16_value(orc_f32_to_f16(d));"),
+    ("quant_zero_block_scale", "dx[b] = 0;\n            continue;", "dx[b] = 0x3c00;\n            continue;"),
+    ("quant_amax_signed", "float a = fabsf(xb[i]);", "float a = xb[i];"),
+    ("isum_wrong_x_index", "(int32_t)qx[b * ORC_QBLOCK + i];\n            isum", "(int32_t)qx[i];\n            isum"),
+    ("gemv_wrong_dx_index", "orc_f16_value(dx[b]);", "orc_f16_value(dx[0]);"),
+    ("gemv_reversed_dw", "orc_f16_value(dw[n * nb + b])", "orc_f16_value(dw[n * nb + (nb - 1 - b)])"),
+    ("gemv_unsigned_weights", "int32_t p = (int32_t)qw[n * K + b * ORC_QBLOCK + i]",
+     "int32_t p = (int32_t)(uint8_t)qw[n * K + b * ORC_QBLOCK + i]"),
+    ("gemv_residual_sign", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- bf16",
+     "acc -= (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- bf16"),
+    ("gemv_magnitude_signed", "sa += p < 0 ? -p : p;", "sa += p;"),
+    ("gemv_dropped_last_block", "for (int64_t b = 0; b < nb; ++b) {\n            int32_t s = 0, sa = 0;",
+     "for (int64_t b = 0; b < nb - 1; ++b) {\n            int32_t s = 0, sa = 0;"),
+    ("bf16_wrong_x_index", "orc_bf16_value(x[k]);", "orc_bf16_value(x[0]);"),
+    ("bf16_reversed_row", "orc_bf16_value(w[n * K + k])", "orc_bf16_value(w[n * K + (K - 1 - k)])"),
+    ("bf16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row",
+     "mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row"),
+    ("threads_drop_row", "jobs[t].n1 = N * (t + 1) / nthreads;", "jobs[t].n1 = N * (t + 1) / nthreads - (t == 0);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = oracle.build(force=True, out=str(tmp_path / "mutant.so"), src=str(path))
+    o = oracle.Oracle(oracle.load(so))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
