@@ -1,0 +1,476 @@
+#!/usr/bin/env python3
+"""Decode-step GEMV benchmark on one MI355X.
+
+Metric: achieved HBM GB/s (and % of the 8 TB/s peak) of the Q8_0 / bf16 decode GEMV
+path, with equivalent decode tokens/s. A step is one decode token of the workload.
+
+Default workload, q8-stack-0.8b: the 0.8B-shaped Q8_0 decode stack, hidden 1024, 24
+layers of [QKV 1024->4096 (stacked 2048/1024/1024), out 2048->1024, gate+up 1024->7168
+(stacked 3584/3584), down 3584->1024 with the residual folded in], then the output head
+1024->151936. 97 activation quantizes + 97 GEMV launches per token, 609,613,952
+algorithmic bytes per token (weights, scales, activations in and out, residual).
+
+Other workloads (per-call figures; a step is one call):
+  q8-gateup-7168x1024   Q8_0 7168x1024, rotating over >= 1 GiB of distinct copies
+  bf16-gateup-7168x1024 bf16 7168x1024 as two stacked 3584-row halves, rotating copies
+  bf16-gateup-18432x2560-x36  bf16 18432x2560 over 36 independent matrices, round-robin
+  q8-head-131072x5120   Q8_0 131072x5120, cold cache (1 GiB flush before every call)
+
+Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
+then K timed steps between two synchronizations, measured with HIP events on the
+stream the kernels run on. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
+WORKLOADS = ["q8-stack-0.8b", "q8-gateup-7168x1024", "bf16-gateup-7168x1024", "bf16-gateup-18432x2560-x36",
+             "q8-head-131072x5120"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_weight_q8_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != kernel_source_digest():
+        return None
+    return t.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+
+def probe_gbps(q8, torch, gib=2, reps=10):
+    """Same-session pure-read ceiling: stream-read a 2 GiB buffer with 16-byte loads."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    q8.flush(buf, 0x5A5A5A5A)
+    sink = torch.empty(q8.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        q8.probe_read(buf, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        q8.probe_read(buf, sink)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    del buf
+    times.sort()
+    return (gib << 30) / times[len(times) // 2] / 1e9
+
+
+def cpu_threads():
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))  # one GPU's share of the host
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ----------------------------------------------------------------------------- the stack
+
+
+def run_stack(args, torch, q8, np):
+    import synth
+    from block_quantized_weight_q8_amd.stack import Q8DecodeStack
+
+    ops = synth.q8_stack_08b()
+    t0 = time.time()
+    host = synth.q8_stack_inputs(ops)
+    log(f"[bench] generated {len(ops)} projections in {time.time() - t0:.1f}s")
+    stack = Q8DecodeStack(ops, host)
+    torch.cuda.synchronize()
+    bytes_gemv = [synth.q8_gemv_bytes(op.n, op.k, op.residual) for op in ops]
+    bytes_quant = [synth.q8_quantize_bytes(op.k) for op in ops]
+    step_bytes = sum(bytes_gemv) + sum(bytes_quant)
+
+    # parity gate on sampled rows of every projection before any timing
+    import oracle
+
+    orc = oracle.get()
+    stack.step()
+    torch.cuda.synchronize()
+    g = np.random.default_rng(12345)
+    worst = 0.0
+    for i, (op, h) in enumerate(zip(ops, host)):
+        b = stack.bufs[i]
+        rq, rd = orc.quantize_act(h["x"])
+        if not (np.array_equal(b["qx"].cpu().numpy(), rq)
+                and np.array_equal(b["dx"].cpu().view(torch.int16).numpy().view(np.uint16), rd)):
+            raise SystemExit(f"parity: quantized activation of {op.name} differs from the oracle")
+        rows = np.unique(np.concatenate([[0, op.n - 1], g.integers(0, op.n, 16 if op.n < 100000 else 256)]))
+        yr, S = orc.q8_gemv(h["qw"][rows], h["dw"][rows], rq, rd, h["r"][rows] if op.residual else None)
+        yg = b["y"].cpu().numpy()[rows].astype(np.float64)
+        rel = np.abs(yg - yr) / S
+        worst = max(worst, float(rel.max()))
+        if not np.all(rel <= 1e-5):
+            raise SystemExit(f"parity: {op.name} rows off by {rel.max():.2e} * S")
+    log(f"[bench] parity on sampled rows of all {len(ops)} projections: worst |err|/S = {worst:.2e}")
+
+    probe = probe_gbps(q8, torch)
+    log(f"[bench] pure-read probe: {probe:.0f} GB/s")
+
+    # (a) launch per projection, the step captured into a HIP graph and replayed
+    stack.capture()
+    for _ in range(args.warmup):
+        stack.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        stack.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_graph = e0.elapsed_time(e1) * 1e-3 / args.steps
+    log(f"[bench] launch per projection, graph replay: {t_graph * 1e6:.1f} us/token")
+    ref = [b["y"].clone() for b in stack.bufs]
+
+    # (a') one launch per projection, activation quantized inside the GEMV launch
+    for b in stack.bufs:
+        b["y"].fill_(float("nan"))
+    stack.capture(fused=True)
+    for _ in range(args.warmup):
+        stack.replay()
+    torch.cuda.synchronize()
+    for i, b in enumerate(stack.bufs):
+        if not torch.equal(b["y"], ref[i]):
+            raise SystemExit(f"parity: fused output of {ops[i].name} differs from quantize + gemv")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        stack.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_fused = e0.elapsed_time(e1) * 1e-3 / args.steps
+    log(f"[bench] fused quantize+GEMV per projection, graph replay: {t_fused * 1e6:.1f} us/token")
+
+    # (b) the whole token as one q8_decode_stack launch
+    for b in stack.bufs:
+        b["y"].fill_(float("nan"))
+    stack.make_plan()
+    for _ in range(max(1, args.warmup)):
+        stack.step_persistent()
+    torch.cuda.synchronize()
+    if stack.plan.error_flag() != 0:
+        raise SystemExit("q8_decode_stack gave up waiting at a barrier")
+    for i, b in enumerate(stack.bufs):
+        if not torch.equal(b["y"], ref[i]):
+            raise SystemExit(f"parity: q8_decode_stack output of {ops[i].name} differs from gemv_stacked")
+    log("[bench] q8_decode_stack outputs bit-identical to launch per projection")
+    evs = []
+    for _ in range(args.steps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        stack.step_persistent()
+        a1.record()
+        evs.append((a0, a1))
+    torch.cuda.synchronize()
+    durs = sorted(x.elapsed_time(y) * 1e-3 for x, y in evs)
+    t_persist = sum(durs) / len(durs)
+    if stack.plan.error_flag() != 0:
+        raise SystemExit("q8_decode_stack gave up waiting at a barrier")
+    log(f"[bench] q8_decode_stack: {t_persist * 1e6:.1f} us/token (min {durs[0] * 1e6:.1f}, "
+        f"max {durs[-1] * 1e6:.1f})")
+
+    if args.breakdown:
+        eager_breakdown(stack, ops, q8, torch, bytes_gemv, bytes_quant)
+
+    if t_persist <= min(t_graph, t_fused):
+        mode, t_step = "q8_decode_stack", t_persist
+        kname = "stack_kernel (q8_decode_stack)"
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(step_bytes / t_persist / 1e9, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(step_bytes / t_persist / 1e9 / HBM_PEAK_GBPS, 4),
+                    "avg_launch_us": round(t_persist * 1e6, 2), "bytes_per_launch": step_bytes,
+                    "traffic": traffic_for(kname)}
+    elif t_fused <= t_graph:
+        mode, t_step = "hipGraph fused (97 launches)", t_fused
+        roofline = None
+    else:
+        mode, t_step = "hipGraph (194 launches)", t_graph
+        roofline = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_stack(ops, host, orc)
+
+    value = step_bytes / t_step / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "q8-stack-0.8b", "layers": 24, "hidden": 1024, "vocab": 151936,
+                   "projections_per_token": len(ops), "launches_per_token": 2 * len(ops),
+                   "bytes_per_step": step_bytes, "mode": mode, "accumulate": "int32 per block, f32"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tok_per_s": round(1.0 / t_step, 1),
+        "probe_GBps": round(probe, 1),
+        "pct_of_probe": round(100 * value / probe, 2),
+        "graph_ms_per_step": round(t_graph * 1e3, 4),
+        "graph_fused_ms_per_step": round(t_fused * 1e3, 4),
+        "decode_stack_ms_per_step": round(t_persist * 1e3, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    return out
+
+
+def eager_breakdown(stack, ops, q8, torch, bytes_gemv, bytes_quant, steps=10):
+    """Diagnostic: each launch of the launch-per-projection step bracketed by HIP events
+    (durations include the event and dispatch overhead of every launch)."""
+    kname = {}
+    for i, op in enumerate(ops):
+        r, w = q8.gemv_config(q8.Q8G_Q8_0, op.n, op.k)
+        kname[i] = f"q8_gemv[rows_per_wave={r},waves={w}]"
+    ksum = {}
+    for _ in range(steps):
+        evs = []
+        for i in range(len(ops)):
+            b = stack.bufs[i]
+            eq = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            eg = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            eq[0].record()
+            q8.q8_quantize_act(b["x"], b["qx"], b["dx"])
+            eq[1].record()
+            eg[0].record()
+            if len(b["parts"]) == 1:
+                p = b["parts"][0]
+                q8.q8_gemv(p["w"], p["dw"], b["qx"], b["dx"], y=p["y"], residual=p["residual"])
+            else:
+                q8.gemv_stacked(b["parts"], b["qx"], b["dx"])
+            eg[1].record()
+            evs.append((i, eq, eg))
+        torch.cuda.synchronize()
+        for i, eq, eg in evs:
+            for name, pair, nbytes in (("q8_quantize_act", eq, bytes_quant[i]), (kname[i], eg, bytes_gemv[i])):
+                d = ksum.setdefault(name, [0, 0.0, 0])
+                d[0] += 1
+                d[1] += pair[0].elapsed_time(pair[1]) * 1e-3
+                d[2] += nbytes
+    for name, (cnt, tsum, bsum) in sorted(ksum.items(), key=lambda kv: -kv[1][1]):
+        log(f"[bench] eager {name}: {cnt // steps} launches/token, avg {tsum / cnt * 1e6:.2f} us, "
+            f"{bsum / tsum / 1e9:.0f} GB/s algorithmic")
+
+
+def cpu_baseline_stack(ops, host, orc, min_seconds=10.0):
+    """The oracle as it stands, on the host cores, over whole tokens of the same
+    stack inputs (quantize + GEMV for all 97 projections), repeated until about
+    `min_seconds` of CPU work has been timed."""
+    import synth
+
+    nth = cpu_threads()
+    nbytes, tokens = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for op, h in zip(ops, host):
+            qx, dx = orc.quantize_act(h["x"])
+            orc.q8_gemv(h["qw"], h["dw"], qx, dx, h["r"] if op.residual else None, nthreads=nth)
+            nbytes += synth.q8_gemv_bytes(op.n, op.k, op.residual) + synth.q8_quantize_bytes(op.k)
+        tokens += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    gbps = nbytes / dt / 1e9
+    log(f"[bench] oracle on {nth} host threads ({cpu_model()}): {gbps:.2f} GB/s, {tokens} tokens in {dt:.1f}s")
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"{tokens} whole tokens of the 0.8B-shaped stack (97 quantizes + 97 GEMVs each), "
+                      f"{nbytes} algorithmic bytes in {dt:.1f} s",
+            "tok_per_s": round(tokens / dt, 2), "cpu": cpu_model()}
+
+
+# ----------------------------------------------------------------------------- per-call workloads
+
+
+def run_single(args, torch, q8, np):
+    import oracle
+    import synth
+
+    orc = oracle.get()
+    wl = args.workload
+    cold = wl == "q8-head-131072x5120"
+    if wl == "q8-gateup-7168x1024":
+        n, k, dt, tag = 7168, 1024, "q8", synth.TAG_Q8_GATEUP
+        per = synth.q8_gemv_bytes(n, k)
+    elif wl == "bf16-gateup-7168x1024":
+        n, k, dt, tag = 7168, 1024, "bf16", synth.TAG_BF16_GATEUP
+        per = synth.bf16_gemv_bytes(n, k)
+    elif wl == "bf16-gateup-18432x2560-x36":
+        n, k, dt, tag = 18432, 2560, "bf16", synth.TAG_BF16_4B_GATEUP
+        per = synth.bf16_gemv_bytes(n, k)
+    else:
+        n, k, dt, tag = 131072, 5120, "q8", synth.TAG_Q8_HEAD
+        per = synth.q8_gemv_bytes(n, k)
+    wbytes = n * k * (1 if dt == "q8" else 2)
+    copies = 36 if "x36" in wl else (1 if cold else max(2, -(-(1 << 30) // wbytes)))
+    mats = []
+    t0 = time.time()
+    first = None
+    for j in range(copies):
+        gr = synth.rng_for(tag, j)
+        if dt == "q8":
+            qw, dw = synth.q8_weights(gr, n, k)
+            x = synth.activation_f32(gr, k)
+            m = {"w": torch.from_numpy(qw).cuda(),
+                 "dw": torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16),
+                 "x": torch.from_numpy(x).cuda()}
+            if j == 0:
+                first = (qw, dw, x)
+        else:
+            w = synth.bf16_weights(gr, n, k)
+            x = synth.bf16_activation(gr, k)
+            m = {"w": torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16),
+                 "x": torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)}
+            if j == 0:
+                first = (w, x)
+        m["y"] = torch.empty(n, dtype=torch.float32, device="cuda")
+        mats.append(m)
+    log(f"[bench] {copies} matrices generated and uploaded in {time.time() - t0:.1f}s")
+    if dt == "q8":
+        for m in mats:
+            m["qx"], m["dx"] = q8.q8_quantize_act(m["x"])
+
+    def call(m):
+        if dt == "q8":
+            q8.q8_gemv(m["w"], m["dw"], m["qx"], m["dx"], y=m["y"])
+        else:
+            h = n // 2
+            q8.gemv_stacked([{"w": m["w"][:h], "y": m["y"][:h]}, {"w": m["w"][h:], "y": m["y"][h:]}], m["x"])
+
+    call(mats[0])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(7).integers(0, n, 512)]))
+    if dt == "q8":
+        qw, dw, x = first
+        rq, rd = orc.quantize_act(x)
+        yr, S = orc.q8_gemv(qw[rows], dw[rows], rq, rd)
+    else:
+        w, x = first
+        yr, S = orc.bf16_gemv(w[rows], x)
+    rel = np.abs(mats[0]["y"].cpu().numpy()[rows].astype(np.float64) - yr) / S
+    if not np.all(rel <= 1e-5):
+        raise SystemExit(f"parity: sampled rows off by {rel.max():.2e} * S")
+    log(f"[bench] parity on {len(rows)} sampled rows: worst |err|/S = {rel.max():.2e}")
+    probe = probe_gbps(q8, torch)
+    log(f"[bench] pure-read probe: {probe:.0f} GB/s")
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if cold else None
+    for j in range(args.warmup):
+        call(mats[j % copies])
+    torch.cuda.synchronize()
+    times = []
+    if cold:
+        for j in range(args.steps):
+            q8.flush(flush_buf, j)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call(mats[0])
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        t = sorted(times)[len(times) // 2]
+    else:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for j in range(args.steps):
+            call(mats[j % copies])
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / args.steps
+    gbps = per / t / 1e9
+    r, w_ = q8.gemv_config(q8.Q8G_Q8_0 if dt == "q8" else q8.Q8G_BF16, n, k)
+    kname = f"{'q8_gemv' if dt == 'q8' else 'bf16_gemv'}[rows_per_wave={r},waves={w_}]"
+    stack_bytes = 609613952 if dt == "q8" else 1143991808
+    return {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8" if dt == "q8" else "bf16", "data": "synthetic",
+        "config": {"workload": wl, "n": n, "k": k, "copies": copies, "cold_cache": cold, "bytes_per_call": per},
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
+        "pct_of_probe": round(100 * gbps / probe, 2),
+        "equiv_tok_per_s": round(gbps * 1e9 / stack_bytes, 1),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 3),
+                     "bytes_per_launch": per, "traffic": traffic_for(kname)},
+        "cpu_baseline": None,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="eager per-launch timing of the per-projection path")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this decode GEMV path has no multi-GPU mode "
+              "(the sharding design is described in the design notes); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("RANK", "0")) != 0:
+        return
+    import numpy as np
+    import torch
+
+    import block_quantized_weight_q8_amd as q8
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    q8.load_library()
+    log(f"[bench] device: {torch.cuda.get_device_name(0)}; workload {args.workload}; "
+        f"kernel source {kernel_source_digest()}")
+    if args.workload == "q8-stack-0.8b":
+        out = run_stack(args, torch, q8, np)
+    else:
+        out = run_single(args, torch, q8, np)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

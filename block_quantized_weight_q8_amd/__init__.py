@@ -1,0 +1,304 @@
+"""Python binding of libq8gemv: decode-step GEMV for Q8_0 and bf16 weights on MI355X.
+
+The entry points mirror the C ABI of include/q8gemv.h one for one. This module only
+checks and marshals arguments (torch tensors in device memory, the current torch
+stream); every step of the computation runs in the HIP kernels of the library.
+There is no fallback: if the library is missing, every call raises.
+
+Storage conventions (as in the C header):
+  * Q8_0 weights: codes int8 [N, K], scales as binary16 bits [N, K/32] (torch.float16,
+    torch.int16 or torch.uint16 tensors are all accepted as 16-bit storage);
+  * quantized activation: codes int8 [K], scales binary16 bits [K/32];
+  * bf16 weights / activation: torch.bfloat16 (or 16-bit integer storage of the bits);
+  * outputs and residuals: torch.float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8gemv.so")
+
+Q8G_Q8_0 = 0
+Q8G_BF16 = 1
+Q8G_Q8_0_F32 = 2
+FUSED_MAX_K = 16384
+MAX_PARTS = 4
+PROBE_SINK_WORDS = 16384
+
+_STATUS = {
+    0: "Q8G_OK",
+    1: "Q8G_ERR_NULL",
+    2: "Q8G_ERR_SHAPE",
+    3: "Q8G_ERR_ALIGN",
+    4: "Q8G_ERR_ARG",
+    5: "Q8G_ERR_LAUNCH",
+    6: "Q8G_ERR_OVERLAP",
+}
+
+
+class Q8GemvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class _Part(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("dw", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("y", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p),
+    ]
+
+
+class _StackOp(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("qx", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p),
+        ("K", ctypes.c_int64),
+        ("nparts", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("parts", _Part * 4),
+    ]
+
+
+STACK_SYNC_WORDS = 64 + 16 * 1024
+STACK_ERR_WORD = 16
+STACK_MAX_K = 16384
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libq8gemv.so (built by __graft_entry__.build()). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.q8_quantize_act.argtypes = [_P, _P, _P, _I64, _P]
+    lib.q8_gemv.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _P]
+    lib.bf16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+    lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
+    lib.q8g_status_str.argtypes = [ctypes.c_int]
+    lib.q8g_status_str.restype = ctypes.c_char_p
+    lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
+    lib.q8g_flush.argtypes = [_P, _I64, ctypes.c_uint32, _P]
+    lib.q8_decode_stack.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
+    lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
+                                    ctypes.POINTER(ctypes.c_int)]
+    for fn in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "gemv_stacked", "q8g_probe_read", "q8g_flush",
+               "q8g_gemv_config", "q8_decode_stack"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise Q8GemvError(fn, status, load_library().q8g_status_str(status).decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t, name, dtypes, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t.data_ptr() if t.numel() else None
+
+
+_I8 = (torch.int8,)
+_H16 = (torch.float16, torch.int16, torch.uint16)
+_B16 = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+
+
+def q8_quantize_act(x, qx=None, dx=None, stream=None):
+    """Quantize f32 x [K] into Q8_0 codes qx int8 [K] and binary16 scales dx [K/32]."""
+    k = x.shape[0] if x.dim() == 1 else -1
+    if k < 0 or k % 32:
+        raise ValueError("x must be 1-D with a length that is a multiple of 32")
+    if qx is None:
+        qx = torch.empty(k, dtype=torch.int8, device=x.device)
+    if dx is None:
+        dx = torch.empty(k // 32, dtype=torch.float16, device=x.device)
+    st = load_library().q8_quantize_act(_ptr(x, "x", _F32), _ptr(qx, "qx", _I8, (k,)),
+                                        _ptr(dx, "dx", _H16, (k // 32,)), k, _stream(stream))
+    _check("q8_quantize_act", st)
+    return qx, dx
+
+
+def q8_gemv(qw, dw, qx, dx, y=None, residual=None, stream=None):
+    """y = Q8_0(qw, dw) · (qx, dx) (+ residual). Returns y (f32 [N])."""
+    if qw.dim() != 2:
+        raise ValueError("qw must be [N, K]")
+    n, k = qw.shape
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=qw.device)
+    st = load_library().q8_gemv(
+        _ptr(qw, "qw", _I8), _ptr(dw, "dw", _H16, (n, k // 32)), _ptr(qx, "qx", _I8, (k,)),
+        _ptr(dx, "dx", _H16, (k // 32,)), _ptr(residual, "residual", _F32, (n,), optional=True),
+        _ptr(y, "y", _F32, (n,)), n, k, _stream(stream))
+    _check("q8_gemv", st)
+    return y
+
+
+def q8_gemv_f32(qw, dw, x, y=None, residual=None, stream=None):
+    """y = Q8_0(qw, dw) · quantize(x) (+ residual) with x f32 [K], quantized inside the
+    launch exactly as q8_quantize_act would (one launch instead of two)."""
+    if qw.dim() != 2:
+        raise ValueError("qw must be [N, K]")
+    return gemv_stacked([{"w": qw, "dw": dw, "y": y, "residual": residual}], x, stream=stream)[0]
+
+
+def bf16_gemv(w, x, y=None, residual=None, stream=None):
+    """y = w · x with bf16 inputs and f32 accumulation (+ residual). Returns y (f32 [N])."""
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w.device)
+    st = load_library().bf16_gemv(
+        _ptr(w, "w", _B16), _ptr(x, "x", _B16, (k,)),
+        _ptr(residual, "residual", _F32, (n,), optional=True), _ptr(y, "y", _F32, (n,)), n, k,
+        _stream(stream))
+    _check("bf16_gemv", st)
+    return y
+
+
+def gemv_stacked(parts, x, dx=None, stream=None):
+    """One launch over 1..4 matrices sharing the input.
+
+    parts: sequence of dicts with keys w (int8 [n, K] for Q8_0, bf16 [n, K]), dw (Q8_0
+    scales, omitted for bf16), y (f32 [n], allocated if absent), residual (optional).
+    x: int8 codes [K] with dx binary16 scales [K/32] (Q8_0); or f32 [K] for Q8_0 weights
+    (quantized inside the launch, dx None); or bf16 [K] (dx None).
+    Returns the list of outputs.
+    """
+    if not 1 <= len(parts) <= MAX_PARTS:
+        raise ValueError("1 to 4 parts")
+    q8 = parts[0]["w"].dtype == torch.int8
+    fused = q8 and x.dtype == torch.float32
+    k = x.shape[0]
+    arr = (_Part * len(parts))()
+    outs = []
+    for i, p in enumerate(parts):
+        w = p["w"]
+        if w.dim() != 2 or w.shape[1] != k:
+            raise ValueError(f"part {i}: w must be [n, {k}]")
+        n = w.shape[0]
+        y = p.get("y")
+        if y is None:
+            y = torch.empty(n, dtype=torch.float32, device=w.device)
+        outs.append(y)
+        arr[i].w = _ptr(w, f"parts[{i}].w", _I8 if q8 else _B16)
+        arr[i].dw = _ptr(p.get("dw"), f"parts[{i}].dw", _H16, (n, k // 32), optional=not q8) if q8 else None
+        arr[i].n = n
+        arr[i].y = _ptr(y, f"parts[{i}].y", _F32, (n,))
+        arr[i].residual = _ptr(p.get("residual"), f"parts[{i}].residual", _F32, (n,), optional=True)
+    px = _ptr(x, "x", _F32 if fused else (_I8 if q8 else _B16), (k,))
+    pdx = _ptr(dx, "dx", _H16, (k // 32,)) if (q8 and not fused) else None
+    dt = Q8G_Q8_0_F32 if fused else (Q8G_Q8_0 if q8 else Q8G_BF16)
+    st = load_library().gemv_stacked(dt, arr, len(parts), px, pdx, k, _stream(stream))
+    _check("gemv_stacked", st)
+    return outs
+
+
+def probe_read(buf, sink, stream=None):
+    """Stream-read every byte of `buf` once (the measured read ceiling)."""
+    st = load_library().q8g_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                       _stream(stream))
+    _check("q8g_probe_read", st)
+
+
+def flush(buf, value: int = 0, stream=None):
+    """Overwrite `buf` (evicts the caches before a cold-cache timing)."""
+    st = load_library().q8g_flush(buf.data_ptr(), buf.numel() * buf.element_size(), value & 0xFFFFFFFF,
+                                  _stream(stream))
+    _check("q8g_flush", st)
+
+
+def gemv_config(dtype: int, n_total: int, k: int):
+    """(rows per wave, waves per workgroup) the library launches a GEMV of n_total rows with."""
+    r, w = ctypes.c_int(), ctypes.c_int()
+    _check("q8g_gemv_config", load_library().q8g_gemv_config(dtype, n_total, k, ctypes.byref(r), ctypes.byref(w)))
+    return r.value, w.value
+
+
+class DecodeStackPlan:
+    """Descriptors of a sequence of stacked Q8_0 projections for q8_decode_stack.
+
+    ops: sequence of dicts with keys x (f32 [K]), parts (list of dicts with w, dw, y and
+    optional residual, as for gemv_stacked), and optional qx / dx (outputs for the codes
+    and scales). The host descriptor array, its device copy and the synchronization
+    workspace (zero-filled here) are kept by the plan; tensors must stay alive with it.
+    """
+
+    def __init__(self, ops, device="cuda"):
+        n = len(ops)
+        arr = (_StackOp * max(1, n))()
+        self._keep = []
+        for i, op in enumerate(ops):
+            x = op["x"]
+            k = x.shape[0]
+            arr[i].x = _ptr(x, f"ops[{i}].x", _F32, (k,))
+            arr[i].qx = _ptr(op.get("qx"), f"ops[{i}].qx", _I8, (k,), optional=True)
+            arr[i].dx = _ptr(op.get("dx"), f"ops[{i}].dx", _H16, (k // 32,), optional=True)
+            arr[i].K = k
+            parts = op["parts"]
+            if not 1 <= len(parts) <= MAX_PARTS:
+                raise ValueError("1 to 4 parts per op")
+            arr[i].nparts = len(parts)
+            arr[i].reserved = 0
+            for j, p in enumerate(parts):
+                w = p["w"]
+                nrow = w.shape[0]
+                arr[i].parts[j].w = _ptr(w, f"ops[{i}].parts[{j}].w", _I8, (nrow, k))
+                arr[i].parts[j].dw = _ptr(p["dw"], f"ops[{i}].parts[{j}].dw", _H16, (nrow, k // 32))
+                arr[i].parts[j].n = nrow
+                arr[i].parts[j].y = _ptr(p["y"], f"ops[{i}].parts[{j}].y", _F32, (nrow,))
+                arr[i].parts[j].residual = _ptr(p.get("residual"), f"ops[{i}].parts[{j}].residual", _F32, (nrow,),
+                                                optional=True)
+            self._keep.append(op)
+        self.nops = n
+        self.host = arr
+        raw = bytes(memoryview(arr))[: n * ctypes.sizeof(_StackOp)] if n else b"\0"
+        self.dev = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
+        self.sync = torch.zeros(STACK_SYNC_WORDS, dtype=torch.int32, device=device)
+
+    def run(self, stream=None):
+        """Enqueue one launch of all projections."""
+        st = load_library().q8_decode_stack(self.host, self.dev.data_ptr(), self.nops, self.sync.data_ptr(),
+                                            _stream(stream))
+        _check("q8_decode_stack", st)
+
+    def error_flag(self) -> int:
+        """Nonzero if a launch gave up waiting at a barrier (synchronizes)."""
+        return int(self.sync[STACK_ERR_WORD].item())

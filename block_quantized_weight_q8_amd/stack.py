@@ -1,0 +1,120 @@
+"""A decode step of stacked Q8_0 projections, run through the C ABI.
+
+"Filling in the blanks: Inference using Phobos", section Fast Decode, lists the
+launch-level steps of a fast decode pass: record the pass once and replay it as a
+graph, never allocate while recording, quantize an activation once and share it,
+stack projections that read the same input, fold the residual add into the matmul.
+This module lays one step out two ways over the same buffers, allocated up front:
+  * per projection one q8_quantize_act and one gemv_stacked (or q8_gemv) launch on
+    one stream, in dependency order; the step can be captured into a HIP graph;
+  * per projection one gemv_stacked launch that quantizes the f32 input itself;
+  * the whole step as one q8_decode_stack launch (persistent workgroups, a device-wide
+    barrier between projections, the next projection's weights fetched during it).
+All three produce bit-identical outputs.
+
+Each projection's input is its own buffer: the layers in between (norms, attention,
+activations) are not part of this path, so the inputs are seeded synthetic vectors.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import DecodeStackPlan, gemv_stacked, q8_gemv, q8_quantize_act
+
+
+def _dev(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class Q8DecodeStack:
+    """Device-resident weights, inputs and outputs for a list of projections.
+
+    ops: sequence of objects with .name, .parts (row counts sharing one input), .k,
+    .residual (bool). host: per op a dict with "qw" int8 [n, k], "dw" uint16 [n, k/32],
+    "x" f32 [k], and "r" f32 [n] when the op folds in a residual.
+    """
+
+    def __init__(self, ops, host, device="cuda"):
+        self.ops = list(ops)
+        self.device = torch.device(device)
+        self.bufs = []
+        for op, h in zip(self.ops, host):
+            n, k = op.n, op.k
+            b = {
+                "qw": _dev(h["qw"], self.device),
+                "dw": _dev(h["dw"].view(np.int16), self.device).view(torch.float16),
+                "x": _dev(h["x"], self.device),
+                "qx": torch.empty(k, dtype=torch.int8, device=self.device),
+                "dx": torch.empty(k // 32, dtype=torch.float16, device=self.device),
+                "y": torch.empty(n, dtype=torch.float32, device=self.device),
+                "r": _dev(h["r"], self.device) if op.residual else None,
+            }
+            parts, off = [], 0
+            for s in op.parts:
+                parts.append({
+                    "w": b["qw"][off:off + s],
+                    "dw": b["dw"][off:off + s],
+                    "y": b["y"][off:off + s],
+                    "residual": b["r"][off:off + s] if b["r"] is not None else None,
+                })
+                off += s
+            b["parts"] = parts
+            self.bufs.append(b)
+        self.graph = None
+        self.plan = None
+
+    def make_plan(self):
+        """Descriptors for the one-launch executor (q8_decode_stack) over the same buffers."""
+        ops = []
+        for b in self.bufs:
+            ops.append({"x": b["x"], "qx": b["qx"], "dx": b["dx"], "parts": b["parts"]})
+        self.plan = DecodeStackPlan(ops, device=self.device)
+        return self.plan
+
+    def step_persistent(self, stream=None):
+        """One token as a single launch of q8_decode_stack."""
+        if self.plan is None:
+            self.make_plan()
+        self.plan.run(stream)
+
+    def launch_op(self, i, stream=None):
+        """Quantize op i's input once, then one launch over its stacked parts."""
+        b = self.bufs[i]
+        q8_quantize_act(b["x"], b["qx"], b["dx"], stream=stream)
+        if len(b["parts"]) == 1:
+            p = b["parts"][0]
+            q8_gemv(p["w"], p["dw"], b["qx"], b["dx"], y=p["y"], residual=p["residual"], stream=stream)
+        else:
+            gemv_stacked(b["parts"], b["qx"], b["dx"], stream=stream)
+
+    def launch_op_fused(self, i, stream=None):
+        """One launch for op i: the f32 input is quantized inside the GEMV launch."""
+        b = self.bufs[i]
+        gemv_stacked(b["parts"], b["x"], stream=stream)
+
+    def step(self, stream=None, fused=False):
+        for i in range(len(self.ops)):
+            if fused:
+                self.launch_op_fused(i, stream)
+            else:
+                self.launch_op(i, stream)
+
+    def capture(self, fused=False):
+        """Record one step into a HIP graph (nothing is allocated while recording)."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            self.step(fused=fused)  # warm: loads the code objects before recording
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(fused=fused)
+        torch.cuda.synchronize(self.device)
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+

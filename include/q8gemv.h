@@ -1,0 +1,173 @@
+/*
+ * q8gemv — decode-step matrix-vector products y = W·x on AMD Instinct MI355X
+ * (CDNA4, gfx950), for Q8_0 block-quantized weights and for bf16 weights.
+ *
+ * Sources (by page title and section):
+ *   [P] "Filling in the blanks: Inference using Phobos", section "Fast Decode":
+ *       decode reads every weight once per token with one multiply and one add
+ *       per weight; a Q8_0 block is 32 int8 values carrying their own scale;
+ *       the block math runs end to end in int8; an activation is quantized once
+ *       and shared; projections reading the same input are stacked; the
+ *       residual add is folded into the matmul.
+ *   [H] "One level down: #002 the same compiler on a GPU", sections "Emitting
+ *       for a GPU" (gate and up computed in one go; a weight row read as
+ *       16-byte chunks of eight bf16; the last row index guards the tail) and
+ *       "The numerical contract" (bf16 weights and activations, f32
+ *       accumulators).
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers owned by the caller. The one exception
+ *     is the `parts` array of gemv_stacked, which is host memory read during
+ *     the call only.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously; nothing is synchronized, allocated or freed, and no
+ *     environment variable is read. The library holds no mutable global
+ *     state, so calls are thread-safe and may be captured into a HIP graph.
+ *   - Q8_0 data is stored as two planes: codes int8 [N][K] row-major and scale
+ *     bits (IEEE binary16) [N][K/32] row-major; scale b of row n covers codes
+ *     32b..32b+31 of that row. A quantized activation is codes int8 [K] plus
+ *     binary16 scale bits [K/32].
+ *   - bf16 data is the upper 16 bits of an IEEE binary32, stored as uint16.
+ *   - All validation happens on the host before anything is enqueued; on any
+ *     error nothing is written. N == 0 is a valid empty call (returns Q8G_OK
+ *     and enqueues nothing). K == 0 gives y = 0 (+ residual).
+ *   - Alignment: weight planes (`qw`, `w`), `qx`, bf16 `x` and f32 `x` need
+ *     16-byte alignment; scale planes 2 bytes; `y` and `residual` 4 bytes.
+ *   - Aliasing: `y` may be the same pointer as `residual` (each element is read
+ *     once, then written once, by the same lane). No other overlap between an
+ *     output and any other argument is allowed (Q8G_ERR_OVERLAP).
+ *   - NaN or Inf inputs and binary16 overflow of a scale are outside the
+ *     contract: results are unspecified but nothing faults.
+ */
+#ifndef Q8GEMV_H
+#define Q8GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8G_OK = 0,
+    Q8G_ERR_NULL = 1,    /* a required pointer is NULL */
+    Q8G_ERR_SHAPE = 2,   /* negative size, K not a multiple of 32 (Q8_0) or 8 (bf16), size overflow */
+    Q8G_ERR_ALIGN = 3,   /* a pointer is not aligned as stated above */
+    Q8G_ERR_ARG = 4,     /* bad enum value or part count */
+    Q8G_ERR_LAUNCH = 5,  /* the HIP runtime refused the kernel launch */
+    Q8G_ERR_OVERLAP = 6  /* an output overlaps an input or another output */
+} q8g_status;
+
+/* Q8G_Q8_0_F32: Q8_0 weights with an f32 activation that the launch itself
+ * quantizes (exactly as q8_quantize_act) before the dot products; K <= 16384. */
+typedef enum { Q8G_Q8_0 = 0, Q8G_BF16 = 1, Q8G_Q8_0_F32 = 2 } q8g_dtype;
+
+/* Quantize an activation once into the Q8_0 block format ([P] Fast Decode).
+ * For each block b of 32 consecutive values of x (f32 [K]):
+ *   d = fl32(max_i |x_i| / 127)            (one IEEE f32 division)
+ *   d == 0: codes 0, scale bits 0
+ *   else:   q_i = rint(fl32(x_i / d))      (round half to even; |q_i| <= 127)
+ *           dx[b] = binary16(d)            (round to nearest even, subnormals kept)
+ * The f32 d quantizes; the binary16 d is what the dot products use.
+ * K % 32 == 0. qx: int8 [K]; dx: uint16 [K/32]. Neither may overlap x. */
+q8g_status q8_quantize_act(const float *x, int8_t *qx, uint16_t *dx, int64_t K, void *stream);
+
+/* Q8_0 GEMV ([P] Fast Decode):
+ *   isum[n][b] = sum_{i<32} qw[n][32b+i] * qx[32b+i]          (exact int32)
+ *   y[n] = sum_b float(isum[n][b]) * (f16(dw[n][b]) * f16(dx[b]))  (f32 accumulate)
+ *          (+ residual[n], added once after the dot; residual may be NULL)
+ * qw int8 [N][K], dw uint16 [N][K/32], qx int8 [K], dx uint16 [K/32],
+ * residual f32 [N] or NULL, y f32 [N]. K % 32 == 0. */
+q8g_status q8_gemv(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                   const float *residual, float *y, int64_t N, int64_t K, void *stream);
+
+/* bf16 GEMV ([H] The numerical contract):
+ *   y[n] = sum_k f32(w[n][k]) * f32(x[k])   (f32 accumulate) (+ residual[n])
+ * w uint16 (bf16) [N][K], x uint16 (bf16) [K], residual f32 [N] or NULL,
+ * y f32 [N]. K % 8 == 0 (a row is whole 16-byte chunks, [H] Emitting for a GPU). */
+q8g_status bf16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, float *y,
+                     int64_t N, int64_t K, void *stream);
+
+/* One matrix of a stacked projection. */
+typedef struct {
+    const void *w;         /* Q8_0: int8 codes [n][K]; bf16: uint16 [n][K] */
+    const uint16_t *dw;    /* Q8_0: binary16 scale bits [n][K/32]; bf16: ignored (may be NULL) */
+    int64_t n;             /* output rows of this part (>= 0) */
+    float *y;              /* f32 [n] */
+    const float *residual; /* f32 [n] or NULL; may equal y */
+} q8g_part;
+
+/* Stacked projection ([P] Fast Decode: stack projections that read the same
+ * input; [H] Emitting for a GPU: gate and up in one go). One launch computes
+ * every part against the shared input: Q8_0 takes x = int8 codes [K] and
+ * dx = binary16 scale bits [K/32]; bf16 takes x = bf16 [K] and ignores dx;
+ * Q8G_Q8_0_F32 takes x = f32 [K] (16-byte aligned, K <= 16384), quantizes it
+ * inside the launch, and ignores dx ([P] Fast Decode: quantize the activation
+ * once and share it, here once per launch for all of its parts).
+ * Part p's result is identical, bit for bit, to q8_gemv / bf16_gemv called on
+ * that part alone (for Q8G_Q8_0_F32: to q8_quantize_act then q8_gemv).
+ * 1 <= nparts <= 4. */
+q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, const void *x,
+                        const uint16_t *dx, int64_t K, void *stream);
+
+/* ---- a whole decode step in one launch ------------------------------------
+ * "Filling in the blanks: Inference using Phobos", section Fast Decode, lists
+ * the launch-level steps of a fast decode pass: replay the pass as one unit,
+ * quantize an activation once and share it, stack projections that read the
+ * same input, fold the residual add into the matmul. q8_decode_stack runs a
+ * sequence of stacked Q8_0 projections as ONE cooperative launch: projection
+ * i starts reading its activation only after every output of projection i-1
+ * is written (a device-wide barrier), while the weights of the next
+ * projection, which depend on no activation, are already being fetched.
+ * Each projection quantizes its f32 input exactly as q8_quantize_act does and
+ * computes each output row with the same instructions as gemv_stacked, so
+ * every output is bit-identical to q8_quantize_act + gemv_stacked on the same
+ * inputs. */
+typedef struct {
+    const float *x;     /* f32 [K] input of this projection (16-byte aligned) */
+    int8_t *qx;         /* optional: the quantized codes int8 [K] are also written here (or NULL) */
+    uint16_t *dx;       /* optional: binary16 scale bits [K/32] written here (or NULL) */
+    int64_t K;          /* 32 <= K <= Q8G_STACK_MAX_K, K % 32 == 0 */
+    int32_t nparts;     /* 1..4 */
+    int32_t reserved;   /* must be 0 */
+    q8g_part parts[4];  /* as for gemv_stacked; unused slots ignored */
+} q8g_stack_op;
+
+#define Q8G_STACK_MAX_K 16384
+/* uint32 words of the synchronization workspace: 64 + 16 per workgroup, for
+ * up to 1024 workgroups (one per compute unit). */
+#define Q8G_STACK_SYNC_WORDS (64 + 16 * 1024)
+/* word of the workspace that is nonzero if a launch gave up waiting (its
+ * outputs are then incomplete; zero the workspace before the next launch). */
+#define Q8G_STACK_ERR_WORD 16
+
+/* Run nops projections in order in one launch.
+ * ops:     host array, validated here (same rules as gemv_stacked per op; no
+ *          output may overlap any weight, scale or activation input of any op,
+ *          or another output).
+ * ops_dev: device copy of the same nops descriptors (same bytes), read by the
+ *          kernel; the caller keeps it alive until the launch completes.
+ * sync:    device workspace of Q8G_STACK_SYNC_WORDS uint32, zero-filled by the
+ *          caller before its first use; it carries a launch counter between
+ *          launches, so launches sharing it must be ordered (one stream).
+ * The launch needs one resident workgroup per compute unit (cooperative
+ * launch); if the device cannot guarantee that, Q8G_ERR_LAUNCH is returned
+ * and nothing runs. */
+q8g_status q8_decode_stack(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, int nops, uint32_t *sync,
+                           void *stream);
+
+/* Launch configuration the library picks for a GEMV over n_total rows of K
+ * (all parts of a stacked call together): output rows per wave and waves per
+ * workgroup. Pure host query; nothing is enqueued. Lets a profiler's per-kernel
+ * statistics be matched to the calls that produced them. */
+q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows_per_wave,
+                           int *waves_per_group);
+
+/* A static, human-readable name for a status code. */
+const char *q8g_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8GEMV_H */

@@ -129,3 +129,16 @@ def q8_quantize_bytes(k: int) -> int:
 def bf16_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
     b = 2 * n * k + 2 * k + 4 * n
     return b + (n * 4 if residual else 0)
+
+
+def q8_stack_inputs(ops, tag: int = TAG_Q8_STACK):
+    """Seeded host inputs for each projection j of a stack: codes, scale bits, f32 input,
+    and a residual where the projection folds one in."""
+    host = []
+    for j, op in enumerate(ops):
+        g = rng_for(tag, j)
+        qw, dw = q8_weights(g, op.n, op.k)
+        x = activation_f32(g, op.k)
+        r = residual_f32(g, op.n) if op.residual else None
+        host.append({"qw": qw, "dw": dw, "x": x, "r": r})
+    return host

@@ -1,0 +1,201 @@
+"""The C-ABI library without a GPU: exports and host-side validation.
+
+Every call here fails validation on the host before anything is enqueued, so the
+fake device addresses passed in are never dereferenced and no kernel is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_quantized_weight_q8_amd", "libq8gemv.so")
+INCLUDE = os.path.join(ROOT, "include")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ARG, ERR_LAUNCH, ERR_OVERLAP = range(7)
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(INCLUDE)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(INCLUDE, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libq8gemv.so not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+
+    class Part(ctypes.Structure):
+        _fields_ = [("w", P), ("dw", P), ("n", I64), ("y", P), ("residual", P)]
+
+    L.Part = Part
+    L.q8_quantize_act.argtypes = [P, P, P, I64, P]
+    L.q8_gemv.argtypes = [P, P, P, P, P, P, I64, I64, P]
+    L.bf16_gemv.argtypes = [P, P, P, P, I64, I64, P]
+    L.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(Part), ctypes.c_int, P, P, I64, P]
+    L.q8g_status_str.argtypes = [ctypes.c_int]
+    L.q8g_status_str.restype = ctypes.c_char_p
+    L.q8g_probe_read.argtypes = [P, I64, P, P]
+    L.q8g_flush.argtypes = [P, I64, ctypes.c_uint32, P]
+    return L
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    for expected in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "gemv_stacked", "q8g_status_str",
+                     "q8g_probe_read", "q8g_flush"):
+        assert expected in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.q8g_status_str(s)
+    assert lib.q8g_status_str(99) == b"unknown status"
+
+
+# fake, 256-byte aligned, non-overlapping device addresses (never dereferenced)
+A = 0x7F0000000000
+W, DW, QX, DX, Y, R, X = (A + i * 0x10000000 for i in range(7))
+
+
+def test_quantize_validation(lib):
+    q = lib.q8_quantize_act
+    assert q(X, QX, DX, 33, None) == ERR_SHAPE
+    assert q(X, QX, DX, -32, None) == ERR_SHAPE
+    assert q(None, None, None, 0, None) == OK  # empty: nothing enqueued
+    assert q(None, QX, DX, 64, None) == ERR_NULL
+    assert q(X + 4, QX, DX, 64, None) == ERR_ALIGN
+    assert q(X, QX + 1, DX, 64, None) == ERR_ALIGN
+    assert q(X, QX, DX + 1, 64, None) == ERR_ALIGN
+    assert q(X, X + 16, DX, 64, None) == ERR_OVERLAP  # codes inside x
+    assert q(X, QX, QX + 32, 64, None) == ERR_OVERLAP  # scales inside codes
+
+
+def test_q8_gemv_validation(lib):
+    g = lib.q8_gemv
+    assert g(W, DW, QX, DX, None, Y, 8, 48, None) == ERR_SHAPE  # K % 32
+    assert g(W, DW, QX, DX, None, Y, -1, 64, None) == ERR_SHAPE
+    assert g(W, DW, QX, DX, None, Y, 1 << 40, 1 << 30, None) == ERR_SHAPE  # N*K overflow guard
+    assert g(None, None, None, None, None, None, 0, 64, None) == OK  # N == 0
+    assert g(None, DW, QX, DX, None, Y, 8, 64, None) == ERR_NULL
+    assert g(W, None, QX, DX, None, Y, 8, 64, None) == ERR_NULL
+    assert g(W, DW, None, DX, None, Y, 8, 64, None) == ERR_NULL
+    assert g(W, DW, QX, DX, None, None, 8, 64, None) == ERR_NULL
+    assert g(W + 8, DW, QX, DX, None, Y, 8, 64, None) == ERR_ALIGN
+    assert g(W, DW + 1, QX, DX, None, Y, 8, 64, None) == ERR_ALIGN
+    assert g(W, DW, QX + 8, DX, None, Y, 8, 64, None) == ERR_ALIGN
+    assert g(W, DW, QX, DX, R + 2, Y, 8, 64, None) == ERR_ALIGN
+    assert g(W, DW, QX, DX, None, Y + 2, 8, 64, None) == ERR_ALIGN
+    # outputs overlapping inputs
+    assert g(W, DW, QX, DX, None, W + 64, 8, 64, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, None, DW, 8, 64, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, None, QX, 8, 64, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, None, DX, 8, 64, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, Y + 4, Y, 8, 64, None) == ERR_OVERLAP  # partial residual alias
+
+
+def test_bf16_gemv_validation(lib):
+    g = lib.bf16_gemv
+    assert g(W, X, None, Y, 8, 12, None) == ERR_SHAPE  # K % 8
+    assert g(W, X, None, Y, -3, 16, None) == ERR_SHAPE
+    assert g(None, X, None, Y, 8, 16, None) == ERR_NULL
+    assert g(W, None, None, Y, 8, 16, None) == ERR_NULL
+    assert g(W + 2, X, None, Y, 8, 16, None) == ERR_ALIGN
+    assert g(W, X + 2, None, Y, 8, 16, None) == ERR_ALIGN
+    assert g(W, X, None, X, 8, 16, None) == ERR_OVERLAP
+    assert g(None, None, None, None, 0, 16, None) == OK
+
+
+def test_stacked_validation(lib):
+    Part = lib.Part
+    s = lib.gemv_stacked
+
+    def parts(*ps):
+        arr = (Part * max(1, len(ps)))()
+        for i, p in enumerate(ps):
+            arr[i] = Part(*p)
+        return arr
+
+    one = parts((W, DW, 8, Y, None))
+    assert s(0, one, 0, QX, DX, 64, None) == ERR_ARG
+    assert s(0, one, 5, QX, DX, 64, None) == ERR_ARG
+    assert s(7, one, 1, QX, DX, 64, None) == ERR_ARG
+    assert s(0, None, 1, QX, DX, 64, None) == ERR_NULL
+    assert s(0, parts((W, DW, -1, Y, None)), 1, QX, DX, 64, None) == ERR_SHAPE
+    assert s(0, one, 1, QX, None, 64, None) == ERR_NULL  # Q8_0 needs dx
+    assert s(0, parts((W, None, 8, Y, None)), 1, QX, DX, 64, None) == ERR_NULL  # Q8_0 needs dw
+    # two parts writing overlapping outputs
+    two = parts((W, DW, 8, Y, None), (W + 0x100000, DW + 0x100000, 8, Y + 16, None))
+    assert s(0, two, 2, QX, DX, 64, None) == ERR_OVERLAP
+    # a part's output over another part's weights
+    two = parts((W, DW, 8, Y, None), (W + 0x100000, DW + 0x100000, 8, W, None))
+    assert s(0, two, 2, QX, DX, 64, None) == ERR_OVERLAP
+    # residual of one part aliasing another part's output
+    two = parts((W, DW, 8, Y, Y + 4096), (W + 0x100000, DW + 0x100000, 8, Y + 4096, None))
+    assert s(0, two, 2, QX, DX, 64, None) == ERR_OVERLAP
+    # all parts empty: nothing to do
+    assert s(1, parts((None, None, 0, None, None), (None, None, 0, None, None)), 2, None, None, 16, None) == OK
+
+
+def test_probe_validation(lib):
+    assert lib.q8g_probe_read(X, 17, Y, None) == ERR_SHAPE
+    assert lib.q8g_probe_read(None, 16, Y, None) == ERR_NULL
+    assert lib.q8g_probe_read(X + 8, 16, Y, None) == ERR_ALIGN
+    assert lib.q8g_flush(X, 15, 0, None) == ERR_SHAPE
+    assert lib.q8g_flush(None, 0, 0, None) == OK
+    assert lib.q8g_flush(X + 4, 16, 0, None) == ERR_ALIGN
+
+
+def test_decode_stack_validation(lib):
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    Part = lib.Part
+
+    class Op(ctypes.Structure):
+        _fields_ = [("x", P), ("qx", P), ("dx", P), ("K", I64), ("nparts", ctypes.c_int32),
+                    ("reserved", ctypes.c_int32), ("parts", Part * 4)]
+
+    assert ctypes.sizeof(Op) == 200
+    f = lib.q8_decode_stack
+    f.argtypes = [ctypes.POINTER(Op), P, ctypes.c_int, P, P]
+    f.restype = ctypes.c_int
+    SYNC, DEV = A + 0x70000000, A + 0x78000000
+
+    def ops(*specs):
+        arr = (Op * max(1, len(specs)))()
+        for i, (x, k, parts) in enumerate(specs):
+            arr[i].x, arr[i].K, arr[i].nparts = x, k, len(parts)
+            for j, p in enumerate(parts):
+                arr[i].parts[j] = Part(*p)
+        return arr
+
+    good = ops((X, 64, [(W, DW, 8, Y, None)]))
+    assert f(good, DEV, -1, SYNC, None) == ERR_ARG
+    assert f(good, DEV, 0, SYNC, None) == OK
+    assert f(good, None, 1, SYNC, None) == ERR_NULL
+    assert f(good, DEV, 1, None, None) == ERR_NULL
+    assert f(good, DEV, 1, SYNC + 4, None) == ERR_ALIGN
+    assert f(ops((X, 48, [(W, DW, 8, Y, None)])), DEV, 1, SYNC, None) == ERR_SHAPE  # K % 32
+    assert f(ops((X, 16384 + 32, [(W, DW, 8, Y, None)])), DEV, 1, SYNC, None) == ERR_SHAPE
+    assert f(ops((X, 64, [])), DEV, 1, SYNC, None) == ERR_ARG  # no parts
+    assert f(ops((X, 64, [(W, DW, 0, Y, None)])), DEV, 1, SYNC, None) == ERR_SHAPE  # no rows
+    assert f(ops((None, 64, [(W, DW, 8, Y, None)])), DEV, 1, SYNC, None) == ERR_NULL
+    assert f(ops((X + 4, 64, [(W, DW, 8, Y, None)])), DEV, 1, SYNC, None) == ERR_ALIGN
+    assert f(ops((X, 64, [(W, DW, 8, X, None)])), DEV, 1, SYNC, None) == ERR_OVERLAP  # y over x
+    # op 0 writes over op 1's weights
+    assert f(ops((X, 64, [(W, DW, 8, W + 0x100000, None)]), (X, 64, [(W + 0x100000, DW, 8, Y, None)])),
+             DEV, 2, SYNC, None) == ERR_OVERLAP
+    # two ops writing one buffer
+    assert f(ops((X, 64, [(W, DW, 8, Y, None)]), (X, 64, [(W, DW, 8, Y, None)])), DEV, 2, SYNC, None) == ERR_OVERLAP
+    # op 1 writing op 0's input (read before op 1 runs): a race-free chain is the other way round
+    assert f(ops((X, 64, [(W, DW, 8, Y, None)]), (X + 0x100000, 64, [(W, DW, 16, X, None)])), DEV, 2, SYNC,
+             None) == ERR_OVERLAP
