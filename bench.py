@@ -148,41 +148,69 @@ def run_stack(args, torch, q8, np):
     probe = probe_gbps(q8, torch)
     log(f"[bench] pure-read probe: {probe:.0f} GB/s")
 
-    # (a) launch per projection, the step captured into a HIP graph and replayed
-    stack.capture()
-    for _ in range(args.warmup):
-        stack.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        stack.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t_graph = e0.elapsed_time(e1) * 1e-3 / args.steps
-    log(f"[bench] launch per projection, graph replay: {t_graph * 1e6:.1f} us/token")
+    def time_graph(fn, reps):
+        """Capture fn (a sequence of launches) into a HIP graph; mean seconds per replay."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def time_cold(fn, reps=10):
+        """A few launches (too few to amortize the events): one graph replay after a
+        1 GiB cache-evicting write, bracketed by HIP events; median of reps."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        ts = []
+        for r in range(reps):
+            q8.flush(flush_buf, r)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+
+    # (a) per projection q8_quantize_act + gemv_stacked, the step replayed as a HIP graph
+    t_graph = time_graph(lambda: stack.step(fused=False), args.steps)
+    log(f"[bench] quantize + GEMV per projection (194 launches), graph replay: {t_graph * 1e6:.1f} us/token")
     ref = [b["y"].clone() for b in stack.bufs]
 
-    # (a') one launch per projection, activation quantized inside the GEMV launch
+    # (b) one launch per projection: the GEMV launch quantizes its f32 input itself
     for b in stack.bufs:
         b["y"].fill_(float("nan"))
-    stack.capture(fused=True)
-    for _ in range(args.warmup):
-        stack.replay()
-    torch.cuda.synchronize()
+    t_fused = time_graph(lambda: stack.step(fused=True), args.steps)
     for i, b in enumerate(stack.bufs):
         if not torch.equal(b["y"], ref[i]):
             raise SystemExit(f"parity: fused output of {ops[i].name} differs from quantize + gemv")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        stack.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t_fused = e0.elapsed_time(e1) * 1e-3 / args.steps
-    log(f"[bench] fused quantize+GEMV per projection, graph replay: {t_fused * 1e6:.1f} us/token")
+    log(f"[bench] fused quantize+GEMV per projection (97 launches), graph replay: {t_fused * 1e6:.1f} us/token; "
+        f"outputs bit-identical")
 
-    # (b) the whole token as one q8_decode_stack launch
+    # (c) the whole token as one q8_decode_stack launch
     for b in stack.bufs:
         b["y"].fill_(float("nan"))
     stack.make_plan()
@@ -194,7 +222,6 @@ def run_stack(args, torch, q8, np):
     for i, b in enumerate(stack.bufs):
         if not torch.equal(b["y"], ref[i]):
             raise SystemExit(f"parity: q8_decode_stack output of {ops[i].name} differs from gemv_stacked")
-    log("[bench] q8_decode_stack outputs bit-identical to launch per projection")
     evs = []
     for _ in range(args.steps):
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -203,29 +230,56 @@ def run_stack(args, torch, q8, np):
         a1.record()
         evs.append((a0, a1))
     torch.cuda.synchronize()
-    durs = sorted(x.elapsed_time(y) * 1e-3 for x, y in evs)
-    t_persist = sum(durs) / len(durs)
+    t_persist = sum(x.elapsed_time(y) for x, y in evs) * 1e-3 / len(evs)
     if stack.plan.error_flag() != 0:
         raise SystemExit("q8_decode_stack gave up waiting at a barrier")
-    log(f"[bench] q8_decode_stack: {t_persist * 1e6:.1f} us/token (min {durs[0] * 1e6:.1f}, "
-        f"max {durs[-1] * 1e6:.1f})")
+    log(f"[bench] one q8_decode_stack launch per token: {t_persist * 1e6:.1f} us/token; outputs bit-identical")
 
     if args.breakdown:
         eager_breakdown(stack, ops, q8, torch, bytes_gemv, bytes_quant)
 
-    if t_persist <= min(t_graph, t_fused):
-        mode, t_step = "q8_decode_stack", t_persist
+    # the step that is reported, and the roofline of its dominant kernel
+    best = min(("fused", t_fused), ("graph", t_graph), ("decode_stack", t_persist), key=lambda m: m[1])
+    mode, t_step = best
+    if mode == "decode_stack":
         kname = "stack_kernel (q8_decode_stack)"
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(step_bytes / t_persist / 1e9, 1),
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(step_bytes / t_persist / 1e9 / HBM_PEAK_GBPS, 4),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(step_bytes / t_persist / 1e9 / HBM_PEAK_GBPS, 4),
                     "avg_launch_us": round(t_persist * 1e6, 2), "bytes_per_launch": step_bytes,
-                    "traffic": traffic_for(kname)}
-    elif t_fused <= t_graph:
-        mode, t_step = "hipGraph fused (97 launches)", t_fused
-        roofline = None
+                    "launches_per_step": 1, "traffic": traffic_for(kname)}
     else:
-        mode, t_step = "hipGraph (194 launches)", t_graph
-        roofline = None
+        fused = mode == "fused"
+        dt = q8.Q8G_Q8_0_F32 if fused else q8.Q8G_Q8_0
+        groups = {}
+        for i, op in enumerate(ops):
+            r, w = q8.gemv_config(dt, op.n, op.k)
+            groups.setdefault((r, w), []).append(i)
+        kind = "Q8F32" if fused else "Q8"
+        per = {}
+        for (r, w), idx in groups.items():
+            name = f"gemv_kernel<{kind}, rows_per_wave={r}, waves={w}>"
+            if fused:
+                nbytes = [synth.q8_gemv_f32x_bytes(ops[i].n, ops[i].k, ops[i].residual) for i in idx]
+                fn = (lambda idx=idx: [stack.launch_op_fused(i) for i in idx])
+            else:
+                nbytes = [bytes_gemv[i] for i in idx]
+                fn = (lambda idx=idx: [stack.launch_op_gemv_only(i) for i in idx])
+            if len(idx) >= 8:
+                t = time_graph(fn, max(5, args.steps // 2)) / len(idx)
+            else:
+                t = time_cold(fn) / len(idx)
+            per[name] = [len(idx), t, sum(nbytes) / len(idx)]
+        for name, (c, t, nb) in sorted(per.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+            log(f"[bench] {name}: {c} launches/token, {t * 1e6:.2f} us each, {nb / t / 1e9:.0f} GB/s")
+        dname, (dc, dt_, db) = max(per.items(), key=lambda kv: kv[1][0] * kv[1][1])
+        roofline = {"bound": "hbm", "kernel": dname, "achieved": round(db / dt_ / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(db / dt_ / 1e9 / HBM_PEAK_GBPS, 4),
+                    "avg_launch_us": round(dt_ * 1e6, 3), "bytes_per_launch": round(db),
+                    "launches_per_step": dc, "traffic": traffic_for(dname)}
+    mode = {"fused": "hipGraph, one fused quantize+GEMV launch per projection (97 per token)",
+            "graph": "hipGraph, q8_quantize_act + GEMV per projection (194 launches per token)",
+            "decode_stack": "one q8_decode_stack launch per token"}[mode]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -252,9 +306,9 @@ def run_stack(args, torch, q8, np):
         "tok_per_s": round(1.0 / t_step, 1),
         "probe_GBps": round(probe, 1),
         "pct_of_probe": round(100 * value / probe, 2),
-        "graph_ms_per_step": round(t_graph * 1e3, 4),
-        "graph_fused_ms_per_step": round(t_fused * 1e3, 4),
-        "decode_stack_ms_per_step": round(t_persist * 1e3, 4),
+        "modes_ms_per_step": {"fused_graph": round(t_fused * 1e3, 4), "quantize_gemv_graph": round(t_graph * 1e3, 4),
+                              "decode_stack": round(t_persist * 1e3, 4)},
+
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -440,6 +494,27 @@ def run_single(args, torch, q8, np):
     }
 
 
+def pmc_workload(args, torch, q8, np):
+    """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
+    1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
+    decode steps of the fused per-projection path."""
+    import synth
+    from block_quantized_weight_q8_amd.stack import Q8DecodeStack
+
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(q8.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    q8.flush(buf, 0x5A5A5A5A)
+    q8.probe_read(buf, sink)
+    torch.cuda.synchronize()
+    ops = synth.q8_stack_08b()
+    stack = Q8DecodeStack(ops, synth.q8_stack_inputs(ops))
+    torch.cuda.synchronize()
+    for _ in range(2):
+        stack.step(fused=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_workload": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,6 +523,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="eager per-launch timing of the per-projection path")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="untimed run for rocprofv3 --pmc passes (calibration read/write + two decode steps)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this decode GEMV path has no multi-GPU mode "
@@ -465,6 +542,9 @@ def main():
     q8.load_library()
     log(f"[bench] device: {torch.cuda.get_device_name(0)}; workload {args.workload}; "
         f"kernel source {kernel_source_digest()}")
+    if args.pmc_workload:
+        pmc_workload(args, torch, q8, np)
+        return
     if args.workload == "q8-stack-0.8b":
         out = run_stack(args, torch, q8, np)
     else:

@@ -52,6 +52,7 @@ enum class Dt { Q8, BF16, Q8F32 };
 
 constexpr int kMaxFusedK = 16384;  // LDS bytes for the codes of a fused launch
 
+
 // Stacked parts. The kernel receives them as separate scalar arguments (see
 // PARTS_PARAMS): an aggregate argument selected by a row-dependent index gets
 // copied to scratch memory, while separate arguments stay in SGPRs. Parts are
@@ -102,52 +103,94 @@ struct RowRef {
         (out) = r_;                                                                                \
     } while (0)
 
-// Q8_0 arithmetic of one chunk for R rows, given this lane's weight codes and
-// scale bits, its activation codes and its activation scale (0 on odd and on
-// inactive lanes): one exact int32 block sum per row, scaled by dw*dx, one fma.
-template <int R>
-__device__ __forceinline__ void q8_chunk_compute(const int4 (&wv)[R], const uint16_t (&ws)[R], const int4 &xq,
-                                                 float xs, float (&acc)[R])
+// ---- batches of row-chunk items ------------------------------------------------
+// A wave's R rows times C chunks are visited chunk-major (chunk c of rows 0..R-1,
+// then chunk c+1), so every row sees its chunks in ascending order, which is the
+// order of its f32 accumulation. Items are loaded kBatch at a time with all of a
+// batch's loads in flight together, and the next batch is requested before the
+// current one is consumed: a multi-chunk row costs about one memory round trip,
+// not one per chunk.
+#ifndef Q8G_BATCH
+#define Q8G_BATCH 4
+#endif
+constexpr int kBatch = Q8G_BATCH;
+static_assert(kBatch == 4 || kBatch == 8, "a batch holds 4 or 8 items (a multiple of R)");
+
+struct Batch {
+    int4 w[kBatch];      // weight bytes of item j (16 per lane)
+    uint16_t s[kBatch];  // Q8_0: the weight block scale bits of item j
+    int4 x[kBatch];      // activation bytes of item j's chunk (items with j % R == 0)
+    uint16_t xs[kBatch]; // Q8_0: the activation block scale bits of that chunk
+};
+
+// Items j = 0..kBatch-1 of the batch starting at chunk c0: chunk c0 + j / R of
+// row j % R. Lanes past the row end load offset 0 (always in bounds) and are
+// masked when the batch is consumed. With XG the activation is read from global
+// memory here as well; otherwise it is read from LDS when consumed.
+template <Dt DT, int R, bool XG>
+__device__ __forceinline__ void load_batch(const RowRef (&rows)[R], const char *__restrict__ x,
+                                           const uint16_t *__restrict__ dx, int64_t c0, int64_t nchunk,
+                                           int64_t row_bytes, int64_t lane_off, Batch &b)
 {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int s = q8_block_sum(wv[r], xq);  // the block's exact int32 sum
-        acc[r] = __builtin_fmaf((float)s, f16_bits_to_f32(ws[r]) * xs, acc[r]);
+    for (int j = 0; j < kBatch; ++j) {
+        const int64_t c = c0 + j / R;
+        const int r = j % R;
+        if (c < nchunk) {  // wave-uniform
+            const int64_t off = c * kChunk + lane_off;
+            const int64_t o = off < row_bytes ? off : 0;
+            b.w[j] = load16_stream(rows[r].w + o);
+            if constexpr (DT != Dt::BF16) b.s[j] = load_u16_stream(rows[r].dw + (o >> 5));
+            if constexpr (XG) {
+                if (r == 0) {
+                    b.x[j] = load16(x + o);
+                    if constexpr (DT == Dt::Q8) b.xs[j] = dx[o >> 5];
+                }
+            }
+        }
     }
 }
 
-template <bool SCALES, int R>
-__device__ __forceinline__ void chunk_load(const RowRef (&rows)[R], int64_t off, int4 (&wv)[R], uint16_t (&ws)[R])
+// Consume a batch. Q8_0: one exact int32 block sum per item (v_dot4 + one DPP
+// add), scaled by dw*dx (exact in f32) with one fma; the odd lane of each block
+// pair and lanes past the row end add zero. bf16: eight exact products summed
+// into a chunk partial, then added to the row's accumulator.
+template <Dt DT, int R, bool XG>
+__device__ __forceinline__ void compute_batch(const Batch &b, const int8_t *__restrict__ s_qx,
+                                              const float *__restrict__ s_dx, int64_t c0, int64_t nchunk,
+                                              int64_t row_bytes, int64_t lane_off, float even, float (&acc)[R])
 {
+    int4 xq = make_int4(0, 0, 0, 0);
+    float xs = 0.0f;
+    float xf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < R; ++r) wv[r] = load16_stream(rows[r].w + off);
-    if constexpr (SCALES) {
+    for (int j = 0; j < kBatch; ++j) {
+        const int64_t c = c0 + j / R;
+        const int r = j % R;
+        if (c < nchunk) {
+            if (r == 0) {
+                const int64_t off = c * kChunk + lane_off;
+                const bool active = off < row_bytes;
+                const int64_t o = active ? off : 0;
+                if constexpr (DT == Dt::BF16) {
+                    bf16_unpack(b.x[j], xf);
 #pragma unroll
-        for (int r = 0; r < R; ++r) ws[r] = load_u16_stream(rows[r].dw + (off >> 5));
-    }
-}
-
-// One 1 KiB chunk of R rows: lane l covers bytes [off, off+16) of each row.
-// Inactive lanes (ragged tail) load in-bounds data and contribute zero.
-template <Dt DT, int R>
-__device__ __forceinline__ void chunk_step(const RowRef (&rows)[R], const void *__restrict__ xv,
-                                           const uint16_t *__restrict__ dx, int64_t off, bool active,
-                                           float even, float (&acc)[R])
-{
-    int4 wv[R];
-    uint16_t ws[R];
-    chunk_load<DT == Dt::Q8>(rows, off, wv, ws);
-    const int4 xq = load16(static_cast<const char *>(xv) + off);
-    if constexpr (DT == Dt::Q8) {
-        const float xs = active ? f16_bits_to_f32(dx[off >> 5]) * even : 0.0f;
-        q8_chunk_compute<R>(wv, ws, xq, xs, acc);
-    } else {
-        float xf[8];
-        bf16_unpack(xq, xf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xf[i] = active ? xf[i] : 0.0f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] += bf16_chunk_dot(wv[r], xf);
+                    for (int i = 0; i < 8; ++i) xf[i] = active ? xf[i] : 0.0f;
+                } else if constexpr (XG) {
+                    xq = b.x[j];
+                    xs = active ? f16_bits_to_f32(b.xs[j]) * even : 0.0f;
+                } else {
+                    xq = *reinterpret_cast<const int4 *>(s_qx + o);
+                    xs = active ? s_dx[o >> 5] * even : 0.0f;
+                }
+            }
+            if constexpr (DT == Dt::BF16) {
+                acc[r] += bf16_chunk_dot(b.w[j], xf);
+            } else {
+                const int s = q8_block_sum(b.w[j], xq);  // the block's exact int32 sum
+                acc[r] = __builtin_fmaf((float)s, f16_bits_to_f32(b.s[j]) * xs, acc[r]);
+            }
+        }
     }
 }
 
@@ -165,109 +208,94 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 }
 
 // y[rows] = W[rows] · x (+ residual) for the R rows owned by each wave.
+// Q8F32: x is f32; the workgroup first requests x (its loads return before the
+// weight loads issued after them: one wave's loads complete in issue order),
+// then its first weight batch, then quantizes x into LDS (the arithmetic of
+// q8_quantize_act) while the weights are in flight. Per row, the arithmetic and
+// its order are the same for all three kinds, so a Q8F32 launch is
+// bit-identical to q8_quantize_act followed by a Q8 launch.
 template <Dt DT, int R, int WAVES>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
                                                             const uint16_t *__restrict__ dx,
                                                             int64_t K, int64_t n_total)
 {
+    constexpr bool FUSED = DT == Dt::Q8F32;
+    constexpr int kThreadsPerGroup = WAVES * kWave;
+    constexpr int kXPasses = 4;  // f32 activation passes requested before the weights
+    __shared__ __align__(16) int8_t s_qx[FUSED ? kMaxFusedK : 16];
+    __shared__ float s_dx[FUSED ? kMaxFusedK / 32 : 4];
+
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform by construction; readfirstlane lets the compiler keep the
     // row bookkeeping and the part table in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R;
-    if (row0 >= n_total) return;  // wave-uniform
+    const bool has_rows = row0 < n_total;  // wave-uniform
+    if (!FUSED && !has_rows) return;
 
-    const int64_t row_bytes = DT == Dt::Q8 ? K : 2 * K;
+    const int64_t row_bytes = DT == Dt::BF16 ? 2 * K : K;
     const int64_t nb = K / 32;
+    const int64_t nchunk = (row_bytes + kChunk - 1) / kChunk;
+    constexpr int CB = kBatch / R;  // chunks per batch
+    const char *x = static_cast<const char *>(xv);
+    const int64_t lane_off = (int64_t)lane * 16;
+
+    float4 xin[kXPasses];
+    if constexpr (FUSED) {
+        const float *xf = static_cast<const float *>(xv);
+#pragma unroll
+        for (int p = 0; p < kXPasses; ++p) {
+            const int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)p * 4 * kThreadsPerGroup;
+            xin[p] = e < K ? *reinterpret_cast<const float4 *>(xf + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
 
     RowRef rows[R];
     bool valid[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         valid[r] = row0 + r < n_total;
-        LOCATE(valid[r] ? row0 + r : row0, row_bytes, nb, rows[r]);
+        LOCATE(valid[r] ? row0 + r : (has_rows ? row0 : 0), row_bytes, nb, rows[r]);
+    }
+
+    Batch cur, nxt;
+    if (has_rows && nchunk > 0) load_batch<DT, R, !FUSED>(rows, x, dx, 0, nchunk, row_bytes, lane_off, cur);
+
+    if constexpr (FUSED) {
+        const float *xf = static_cast<const float *>(xv);
+#pragma unroll
+        for (int p = 0; p < kXPasses; ++p) {
+            const int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)p * 4 * kThreadsPerGroup;
+            if (e - (int64_t)(threadIdx.x & 7) * 4 < K) {  // the 8-lane group of this block is in range
+                float d;
+                const uint32_t packed = quantize4(xin[p], &d);
+                if (e < K) {
+                    *reinterpret_cast<uint32_t *>(s_qx + e) = packed;
+                    if ((lane & 7) == 0) s_dx[e >> 5] = f16_bits_to_f32(scale_bits(d));
+                }
+            }
+        }
+        for (int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)kXPasses * 4 * kThreadsPerGroup; e < K;
+             e += 4 * kThreadsPerGroup) {
+            const float4 v = *reinterpret_cast<const float4 *>(xf + e);
+            float d;
+            const uint32_t packed = quantize4(v, &d);
+            *reinterpret_cast<uint32_t *>(s_qx + e) = packed;
+            if ((lane & 7) == 0) s_dx[e >> 5] = f16_bits_to_f32(scale_bits(d));
+        }
+        __syncthreads();
+        if (!has_rows) return;
     }
 
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    const float even = (lane & 1) ? 0.0f : 1.0f;  // Q8_0: the even lane of a pair applies the scale
 
-    // Q8_0: only the even lane of a block pair applies the block scale.
-    const float even = (lane & 1) ? 0.0f : 1.0f;
-
-    // Whole 1 KiB chunks need no masking. All loads of a chunk are issued
-    // before any of them is consumed, with no branch in between, so a wave
-    // keeps R+1 16-byte loads (and R+1 scale loads) in flight per chunk.
-    const int64_t full = row_bytes / kChunk;
-    for (int64_t c = 0; c < full; ++c)
-        chunk_step<DT, R>(rows, xv, dx, c * kChunk + (int64_t)lane * 16, true, even, acc);
-    // Ragged tail (K not a multiple of the chunk): lanes past the row end
-    // load from offset 0 of their row (always in bounds) and contribute zero.
-    if (full * kChunk < row_bytes) {
-        const int64_t off = full * kChunk + (int64_t)lane * 16;
-        const bool active = off < row_bytes;
-        chunk_step<DT, R>(rows, xv, dx, active ? off : 0, active, even, acc);
-    }
-
-    reduce_and_store<R>(acc, rows, valid, lane);
-}
-
-// y = Q8_0 W · quantize(x) (+ residual) with x in f32: every workgroup issues
-// its first chunk of weight loads, then quantizes x into LDS (the arithmetic
-// of q8_quantize_act) while they are in flight, then proceeds as gemv_kernel
-// does with the codes read from LDS. Bit-identical to q8_quantize_act followed
-// by the Q8 gemv_kernel.
-template <int R, int WAVES>
-__global__ __launch_bounds__(WAVES *kWave) void gemv_q8_f32x_kernel(PARTS_PARAMS, const void *__restrict__ xv,
-                                                                    const uint16_t *__restrict__ unused,
-                                                                    int64_t K, int64_t n_total)
-{
-    __shared__ __align__(16) int8_t s_qx[kMaxFusedK];
-    __shared__ float s_dx[kMaxFusedK / 32];
-    (void)unused;
-    const float *x = static_cast<const float *>(xv);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R;
-    const bool has_rows = row0 < n_total;  // wave-uniform; waves without rows still quantize
-    const int64_t nb = K / 32;
-
-    RowRef rows[R];
-    bool valid[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        valid[r] = row0 + r < n_total;
-        LOCATE(valid[r] ? row0 + r : (has_rows ? row0 : 0), K, nb, rows[r]);
-    }
-    const int64_t nchunk = (K + kChunk - 1) / kChunk;
-    int4 wv[R];
-    uint16_t ws[R];
-    const int64_t off0 = (int64_t)lane * 16;
-    const bool active0 = off0 < K;
-    if (has_rows && nchunk > 0) chunk_load<true>(rows, active0 ? off0 : 0, wv, ws);
-
-    for (int64_t e = (int64_t)threadIdx.x * 4; e < K; e += 4 * WAVES * kWave) {
-        const float4 v = *reinterpret_cast<const float4 *>(x + e);
-        float d;
-        const uint32_t packed = quantize4(v, &d);
-        *reinterpret_cast<uint32_t *>(s_qx + e) = packed;
-        if ((lane & 7) == 0) s_dx[e >> 5] = f16_bits_to_f32(scale_bits(d));
-    }
-    __syncthreads();
-    if (!has_rows) return;
-
-    const float even = (lane & 1) ? 0.0f : 1.0f;
-    float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-    for (int64_t c = 0; c < nchunk; ++c) {
-        const int64_t off = c * kChunk + off0;
-        const bool active = off < K;
-        const int64_t o = active ? off : 0;
-        if (c > 0) chunk_load<true>(rows, o, wv, ws);
-        const int4 xq = *reinterpret_cast<const int4 *>(s_qx + o);
-        const float xs = active ? s_dx[o >> 5] * even : 0.0f;
-        q8_chunk_compute<R>(wv, ws, xq, xs, acc);
+    for (int64_t c0 = 0; c0 < nchunk; c0 += CB) {
+        if (c0 + CB < nchunk) load_batch<DT, R, !FUSED>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);
+        compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
+        cur = nxt;
     }
     reduce_and_store<R>(acc, rows, valid, lane);
 }
@@ -320,17 +348,25 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, int64_
                     &pc.dw[3],  &pc.y[0],   &pc.y[1],   &pc.y[2],   &pc.y[3],   &pc.res[0], &pc.res[1],
                     &pc.res[2], &pc.res[3], &pc.end[0], &pc.end[1], &pc.end[2], &xc,       &dxc,
                     &kc,        &nc};
-    const void *fn;
-    if constexpr (DT == Dt::Q8F32)
-        fn = reinterpret_cast<const void *>(&gemv_q8_f32x_kernel<R, WAVES>);
-    else
-        fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(WAVES * kWave), args, 0, s);
 }
 
-// Rows per wave: as many as keep at least ~8 waves per CU in flight.
-constexpr int kWavesPerGroup = 4;
-constexpr int kWavesPerFusedGroup = 8;  // fewer, larger groups: each one quantizes x
+// Launch configuration by shape (measured on MI355X over the decode shapes):
+// rows per wave R as many as keep at least ~8 waves per compute unit busy;
+// 4 waves per workgroup, except fused launches over fewer than 32768 rows,
+// where 8 waves share the activation quantization.
+#ifndef Q8G_WAVES
+#define Q8G_WAVES 4
+#endif
+#ifndef Q8G_FUSED_WAVES
+#define Q8G_FUSED_WAVES 0  // 0: by shape
+#endif
+#ifndef Q8G_FUSED_ROWS
+#define Q8G_FUSED_ROWS 0  // 0: by shape
+#endif
+constexpr int kWavesPerGroup = Q8G_WAVES;
+constexpr int64_t kFusedWideRows = 32768;
 
 int rows_per_wave(int64_t n_total)
 {
@@ -340,16 +376,40 @@ int rows_per_wave(int64_t n_total)
     return 1;
 }
 
-template <Dt DT>
-hipError_t dispatch_gemv(const Parts &p, const void *x, const uint16_t *dx, int64_t K, int64_t n_total,
+struct Config {
+    int rows;
+    int waves;
+};
+
+Config pick_config(q8g_dtype dt, int64_t n_total)
+{
+    Config c{rows_per_wave(n_total), kWavesPerGroup};
+    if (dt == Q8G_Q8_0_F32) {
+        if (Q8G_FUSED_ROWS) c.rows = Q8G_FUSED_ROWS;
+        c.waves = Q8G_FUSED_WAVES ? Q8G_FUSED_WAVES : (n_total < kFusedWideRows ? 8 : 4);
+    }
+    return c;
+}
+
+template <Dt DT, int W>
+hipError_t dispatch_rows(int rows, const Parts &p, const void *x, const uint16_t *dx, int64_t K, int64_t n_total,
                          hipStream_t s)
 {
-    constexpr int W = DT == Dt::Q8F32 ? kWavesPerFusedGroup : kWavesPerGroup;
-    switch (rows_per_wave(n_total)) {
+    switch (rows) {
     case 4: return launch_gemv<DT, 4, W>(p, x, dx, K, n_total, s);
     case 2: return launch_gemv<DT, 2, W>(p, x, dx, K, n_total, s);
     default: return launch_gemv<DT, 1, W>(p, x, dx, K, n_total, s);
     }
+}
+
+template <Dt DT>
+hipError_t dispatch_gemv(Config c, const Parts &p, const void *x, const uint16_t *dx, int64_t K, int64_t n_total,
+                         hipStream_t s)
+{
+    if constexpr (DT == Dt::Q8F32) {
+        if (c.waves == 8) return dispatch_rows<DT, 8>(c.rows, p, x, dx, K, n_total, s);
+    }
+    return dispatch_rows<DT, kWavesPerGroup>(c.rows, p, x, dx, K, n_total, s);
 }
 
 // Validate parts and the shared input, build the kernel's part table.
@@ -433,9 +493,10 @@ q8g_status run(q8g_dtype dt, const q8g_part *parts, int nparts, const void *x, c
     const q8g_status st = prepare(dt, parts, nparts, x, dx, K, p, n_total);
     if (st != Q8G_OK || n_total == 0) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = dt == Q8G_Q8_0       ? dispatch_gemv<Dt::Q8>(p, x, dx, K, n_total, s)
-                         : dt == Q8G_Q8_0_F32 ? dispatch_gemv<Dt::Q8F32>(p, x, nullptr, K, n_total, s)
-                                              : dispatch_gemv<Dt::BF16>(p, x, dx, K, n_total, s);
+    const Config c = pick_config(dt, n_total);
+    const hipError_t e = dt == Q8G_Q8_0       ? dispatch_gemv<Dt::Q8>(c, p, x, dx, K, n_total, s)
+                         : dt == Q8G_Q8_0_F32 ? dispatch_gemv<Dt::Q8F32>(c, p, x, nullptr, K, n_total, s)
+                                              : dispatch_gemv<Dt::BF16>(c, p, x, dx, K, n_total, s);
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
 
@@ -491,8 +552,9 @@ q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *row
     if (dtype != Q8G_Q8_0 && dtype != Q8G_BF16 && dtype != Q8G_Q8_0_F32) return Q8G_ERR_ARG;
     if (n_total < 0 || K < 0) return Q8G_ERR_SHAPE;
     if (!rows || !waves) return Q8G_ERR_NULL;
-    *rows = rows_per_wave(n_total);
-    *waves = dtype == Q8G_Q8_0_F32 ? kWavesPerFusedGroup : kWavesPerGroup;
+    const Config c = pick_config(dtype, n_total);
+    *rows = c.rows;
+    *waves = c.waves;
     return Q8G_OK;
 }
 

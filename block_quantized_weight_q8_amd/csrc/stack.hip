@@ -15,10 +15,11 @@
 //    only, processed in groups of up to 4 with the standalone kernel's lane
 //    layout, chunk order and butterfly reduction (gemv_device.hpp). So every
 //    output is bit-identical to gemv_stacked.
-//  * The weights of a projection depend on no activation, so each wave issues
-//    the loads of its first kPrefetch 1 KiB items of projection i+1 before it
-//    waits for projection i-1 to finish: the barrier wait overlaps the weight
-//    stream instead of preceding it.
+//  * The weights of a projection depend on no activation, so as soon as a
+//    workgroup has published projection i, each wave requests its first
+//    kPrefetch 1 KiB items of projection i+1 and only then waits for the
+//    other workgroups: the barrier wait overlaps the weight stream instead of
+//    preceding it.
 //  * Barrier: after its outputs are written, workgroup g stores the count of
 //    projections it has finished (over all launches that used the workspace)
 //    into its own 64-byte flag line; wave 0 of every workgroup polls all flag
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(const q8g_stack_op *__r
     // flag line holds the same count, so each workgroup reads its own.
     const uint32_t done0 = ld_dev(flags + 16 * g);
 
-    Prefetch cur, nxt;
+    Prefetch cur;
     issue_prefetch(&ops[0], wave_slice(op_rows(&ops[0]), G, g, wave), lane, cur);
 
     for (int i = 0; i < nops; ++i) {
@@ -181,8 +182,6 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(const q8g_stack_op *__r
         const int64_t K = op->K;
         const int64_t n_total = op_rows(op);
         const Slice sl = wave_slice(n_total, G, g, wave);
-        if (i + 1 < nops)
-            issue_prefetch(&ops[i + 1], wave_slice(op_rows(&ops[i + 1]), G, g, wave), lane, nxt);
 
         // wait until every workgroup has finished projection i-1
         if (i > 0 && wave == 0) {
@@ -273,15 +272,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(const q8g_stack_op *__r
                     st_dev_f(rows[r].y, rows[r].res ? total + ld_dev_f(rows[r].res) : total);
         }
 
-        // publish: this workgroup's outputs of projection i are written
+        // publish: this workgroup's outputs of projection i are written. The
+        // wait covers only this projection's stores: the next projection's
+        // weights are requested after it, and arrive during the next barrier.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) st_dev(flags + 16 * g, done0 + (uint32_t)i + 1);
-#pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
-            cur.w[k] = nxt.w[k];
-            cur.s[k] = nxt.s[k];
-        }
+        if (i + 1 < nops) issue_prefetch(&ops[i + 1], wave_slice(op_rows(&ops[i + 1]), G, g, wave), lane, cur);
     }
 }
 

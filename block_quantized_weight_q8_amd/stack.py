@@ -88,6 +88,15 @@ class Q8DecodeStack:
         else:
             gemv_stacked(b["parts"], b["qx"], b["dx"], stream=stream)
 
+    def launch_op_gemv_only(self, i, stream=None):
+        """The GEMV launch of op i alone (its activation already quantized)."""
+        b = self.bufs[i]
+        if len(b["parts"]) == 1:
+            p = b["parts"][0]
+            q8_gemv(p["w"], p["dw"], b["qx"], b["dx"], y=p["y"], residual=p["residual"], stream=stream)
+        else:
+            gemv_stacked(b["parts"], b["qx"], b["dx"], stream=stream)
+
     def launch_op_fused(self, i, stream=None):
         """One launch for op i: the f32 input is quantized inside the GEMV launch."""
         b = self.bufs[i]

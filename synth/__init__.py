@@ -121,6 +121,13 @@ def q8_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
     return b + (n * 4 if residual else 0)
 
 
+def q8_gemv_f32x_bytes(n: int, k: int, residual: bool = False) -> int:
+    """Algorithmic HBM bytes of one Q8_0 GEMV that reads its activation as f32 and
+    quantizes it in the same launch: codes + scales + f32 activation + f32 out (+ residual)."""
+    b = n * k + n * (k // QBLOCK) * 2 + 4 * k + n * 4
+    return b + (n * 4 if residual else 0)
+
+
 def q8_quantize_bytes(k: int) -> int:
     """Algorithmic bytes of one activation quantize: f32 in, int8 codes + binary16 scales out."""
     return 4 * k + k + (k // QBLOCK) * 2

@@ -408,6 +408,12 @@ def test_empty_and_k0(q8, torch_mod):
     y = q8.bf16_gemv(torch.empty((3, 0), dtype=torch.bfloat16, device="cuda"),
                      torch.empty(0, dtype=torch.bfloat16, device="cuda"))
     assert np.array_equal(host(y), np.zeros(3, np.float32))
+    # fused f32 input with K == 0: every workgroup must still walk its row groups
+    r2 = torch.arange(70000, dtype=torch.float32, device="cuda")
+    y = q8.q8_gemv_f32(torch.empty((70000, 0), dtype=torch.int8, device="cuda"),
+                       torch.empty((70000, 0), dtype=torch.float16, device="cuda"),
+                       torch.empty(0, dtype=torch.float32, device="cuda"), residual=r2)
+    assert np.array_equal(host(y), host(r2))
 
 
 def test_misaligned_and_overlap_raise(q8, torch_mod):
@@ -431,7 +437,7 @@ def test_misaligned_and_overlap_raise(q8, torch_mod):
 
 
 @pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (300, 1024), (1025, 3584), (4096, 1024), (64, 1024 + 96),
-                                 (9, 16384), (8200, 1024)])
+                                 (9, 16384), (8200, 1024), (200003, 64), (40000, 2080)])
 def test_q8_fused_equals_quantize_then_gemv(q8, orc, n, k):
     """The f32-input launch (quantized inside) is bit-identical to q8_quantize_act + q8_gemv."""
     print_case("fused f32 gemv", n, k)
