@@ -68,8 +68,9 @@ def traffic_for(kernel: str):
 # ----------------------------------------------------------------------------- helpers
 
 
-def probe_gbps(q8, torch, gib=2, reps=10):
-    """Same-session pure-read ceiling: stream-read a 2 GiB buffer with 16-byte loads."""
+def probe_gbps(q8, torch, gib=4, reps=10):
+    """Same-session pure-read ceiling: stream-read a 4 GiB buffer with 16-byte
+    nontemporal loads (smaller buffers under-read: ramp and tail weigh more)."""
     buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
     q8.flush(buf, 0x5A5A5A5A)
     sink = torch.empty(q8.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
@@ -315,6 +316,31 @@ def run_stack(args, torch, q8, np):
     return out
 
 
+def cpu_baseline_single(dt, first, n, k, per, orc, np, min_seconds=10.0):
+    """The oracle on the host cores over whole copies of the first matrix (all rows),
+    repeated until about min_seconds have been timed; GB/s over the same algorithmic bytes."""
+    nth = cpu_threads()
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        if dt == "q8":
+            qw, dw, x = first
+            qx, dx = orc.quantize_act(x)
+            orc.q8_gemv(qw, dw, qx, dx, nthreads=nth)
+        else:
+            w, x = first
+            orc.bf16_gemv(w, x, nthreads=nth)
+        calls += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt_ = time.perf_counter() - t0
+    gbps = calls * per / dt_ / 1e9
+    log(f"[bench] oracle on {nth} host threads: {gbps:.2f} GB/s, {calls} calls in {dt_:.1f}s")
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"{calls} whole {n}x{k} calls, {calls * per} algorithmic bytes in {dt_:.1f} s",
+            "cpu": cpu_model()}
+
+
 def eager_breakdown(stack, ops, q8, torch, bytes_gemv, bytes_quant, steps=10):
     """Diagnostic: each launch of the launch-per-projection step bracketed by HIP events
     (durations include the event and dispatch overhead of every launch)."""
@@ -405,8 +431,17 @@ def run_single(args, torch, q8, np):
     mats = []
     t0 = time.time()
     first = None
+    tg = torch.Generator(device="cuda")
     for j in range(copies):
         gr = synth.rng_for(tag, j)
+        if dt == "bf16" and j > 0:
+            # timing-only copies (parity is checked on copy 0): the same distribution,
+            # drawn by a seeded device generator to keep set-up within seconds
+            tg.manual_seed(1000003 * tag + j)
+            w_dev = (torch.randn((n, k), device="cuda", generator=tg) * 0.02).to(torch.bfloat16)
+            x_dev = torch.randn(k, device="cuda", generator=tg).to(torch.bfloat16)
+            mats.append({"w": w_dev, "x": x_dev, "y": torch.empty(n, dtype=torch.float32, device="cuda")})
+            continue
         if dt == "q8":
             qw, dw = synth.q8_weights(gr, n, k)
             x = synth.activation_f32(gr, k)
@@ -452,12 +487,13 @@ def run_single(args, torch, q8, np):
     log(f"[bench] parity on {len(rows)} sampled rows: worst |err|/S = {rel.max():.2e}")
     probe = probe_gbps(q8, torch)
     log(f"[bench] pure-read probe: {probe:.0f} GB/s")
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if cold else None
-    for j in range(args.warmup):
-        call(mats[j % copies])
-    torch.cuda.synchronize()
-    times = []
     if cold:
+        # one call at a time, each after a 1 GiB write that evicts the caches
+        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for j in range(args.warmup):
+            call(mats[0])
+        torch.cuda.synchronize()
+        times = []
         for j in range(args.steps):
             q8.flush(flush_buf, j)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -466,31 +502,53 @@ def run_single(args, torch, q8, np):
             b.record()
             b.synchronize()
             times.append(a.elapsed_time(b) * 1e-3)
-        t = sorted(times)[len(times) // 2]
+        t = sum(times) / len(times)
+        calls = args.steps
     else:
+        # back-to-back calls rotating over copies that together exceed the last-level cache,
+        # captured once into a HIP graph (one pass over the copies) and replayed
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for m in mats:
+                call(m)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for m in mats:
+                call(m)
+        reps = max(1, -(-args.steps // copies))
+        for _ in range(max(1, -(-args.warmup // copies))):
+            graph.replay()
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for j in range(args.steps):
-            call(mats[j % copies])
+        for _ in range(reps):
+            graph.replay()
         b.record()
         torch.cuda.synchronize()
-        t = a.elapsed_time(b) * 1e-3 / args.steps
+        calls = reps * copies
+        t = a.elapsed_time(b) * 1e-3 / calls
+    cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np)
     gbps = per / t / 1e9
     r, w_ = q8.gemv_config(q8.Q8G_Q8_0 if dt == "q8" else q8.Q8G_BF16, n, k)
     kname = f"{'q8_gemv' if dt == 'q8' else 'bf16_gemv'}[rows_per_wave={r},waves={w_}]"
     stack_bytes = 609613952 if dt == "q8" else 1143991808
     return {
-        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": calls,
         "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8" if dt == "q8" else "bf16", "data": "synthetic",
-        "config": {"workload": wl, "n": n, "k": k, "copies": copies, "cold_cache": cold, "bytes_per_call": per},
+        "config": {"workload": wl, "n": n, "k": k, "copies": copies, "cold_cache": cold, "bytes_per_call": per,
+                   "call": "q8_gemv" if dt == "q8" else "gemv_stacked, two halves",
+                   "timing": "per call after a 1 GiB flush" if cold else "HIP graph over one pass of the copies"},
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
         "pct_of_probe": round(100 * gbps / probe, 2),
         "equiv_tok_per_s": round(gbps * 1e9 / stack_bytes, 1),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 3),
                      "bytes_per_launch": per, "traffic": traffic_for(kname)},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
 
 

@@ -353,9 +353,9 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, int64_
 }
 
 // Launch configuration by shape (measured on MI355X over the decode shapes):
-// rows per wave R as many as keep at least ~8 waves per compute unit busy;
-// 4 waves per workgroup, except fused launches over fewer than 32768 rows,
-// where 8 waves share the activation quantization.
+// rows per wave R as many as keep at least ~8 waves per compute unit busy (at
+// most 2 for bf16); 4 waves per workgroup, except fused launches over fewer
+// than 32768 rows, where 8 waves share the activation quantization.
 #ifndef Q8G_WAVES
 #define Q8G_WAVES 4
 #endif
@@ -364,6 +364,9 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, int64_
 #endif
 #ifndef Q8G_FUSED_ROWS
 #define Q8G_FUSED_ROWS 0  // 0: by shape
+#endif
+#ifndef Q8G_BF16_ROWS
+#define Q8G_BF16_ROWS 0  // 0: by shape
 #endif
 constexpr int kWavesPerGroup = Q8G_WAVES;
 constexpr int64_t kFusedWideRows = 32768;
@@ -384,6 +387,11 @@ struct Config {
 Config pick_config(q8g_dtype dt, int64_t n_total)
 {
     Config c{rows_per_wave(n_total), kWavesPerGroup};
+    if (dt == Q8G_BF16) {
+        // bf16 rows are twice as long: two rows per wave already keep 4 KiB in flight
+        if (c.rows > 2) c.rows = 2;
+        if (Q8G_BF16_ROWS) c.rows = Q8G_BF16_ROWS;
+    }
     if (dt == Q8G_Q8_0_F32) {
         if (Q8G_FUSED_ROWS) c.rows = Q8G_FUSED_ROWS;
         c.waves = Q8G_FUSED_WAVES ? Q8G_FUSED_WAVES : (n_total < kFusedWideRows ? 8 : 4);

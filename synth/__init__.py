@@ -46,8 +46,12 @@ def rng_for(tag: int, j: int) -> np.random.Generator:
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round f32 values to bf16 storage bits, nearest with ties to even (finite inputs)."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return (r >> np.uint32(16)).astype(np.uint16)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    return t.astype(np.uint16)
 
 
 def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
