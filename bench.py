@@ -13,6 +13,7 @@ algorithmic bytes per token (weights, scales, activations in and out, residual).
 Other workloads (per-call figures; a step is one call):
   q8-gateup-7168x1024   Q8_0 7168x1024, rotating over >= 1 GiB of distinct copies
   bf16-gateup-7168x1024 bf16 7168x1024 as two stacked 3584-row halves, rotating copies
+  f16-gateup-7168x1024  the same with IEEE binary16 weights and activation
   bf16-gateup-18432x2560-x36  bf16 18432x2560 over 36 independent matrices, round-robin
   q8-head-131072x5120   Q8_0 131072x5120, cold cache (1 GiB flush before every call)
 
@@ -35,8 +36,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
-WORKLOADS = ["q8-stack-0.8b", "q8-gateup-7168x1024", "bf16-gateup-7168x1024", "bf16-gateup-18432x2560-x36",
-             "q8-head-131072x5120"]
+WORKLOADS = ["q8-stack-0.8b", "q8-gateup-7168x1024", "bf16-gateup-7168x1024", "f16-gateup-7168x1024",
+             "bf16-gateup-18432x2560-x36", "q8-head-131072x5120"]
 
 
 def log(*a):
@@ -329,7 +330,7 @@ def cpu_baseline_single(dt, first, n, k, per, orc, np, min_seconds=10.0):
             orc.q8_gemv(qw, dw, qx, dx, nthreads=nth)
         else:
             w, x = first
-            orc.bf16_gemv(w, x, nthreads=nth)
+            (orc.f16_gemv if dt == "f16" else orc.bf16_gemv)(w, x, nthreads=nth)
         calls += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
@@ -420,6 +421,9 @@ def run_single(args, torch, q8, np):
     elif wl == "bf16-gateup-7168x1024":
         n, k, dt, tag = 7168, 1024, "bf16", synth.TAG_BF16_GATEUP
         per = synth.bf16_gemv_bytes(n, k)
+    elif wl == "f16-gateup-7168x1024":
+        n, k, dt, tag = 7168, 1024, "f16", synth.TAG_F16_GATEUP
+        per = synth.bf16_gemv_bytes(n, k)  # same byte count: 2-byte weights and activation
     elif wl == "bf16-gateup-18432x2560-x36":
         n, k, dt, tag = 18432, 2560, "bf16", synth.TAG_BF16_4B_GATEUP
         per = synth.bf16_gemv_bytes(n, k)
@@ -434,12 +438,13 @@ def run_single(args, torch, q8, np):
     tg = torch.Generator(device="cuda")
     for j in range(copies):
         gr = synth.rng_for(tag, j)
-        if dt == "bf16" and j > 0:
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        if dt != "q8" and j > 0:
             # timing-only copies (parity is checked on copy 0): the same distribution,
             # drawn by a seeded device generator to keep set-up within seconds
             tg.manual_seed(1000003 * tag + j)
-            w_dev = (torch.randn((n, k), device="cuda", generator=tg) * 0.02).to(torch.bfloat16)
-            x_dev = torch.randn(k, device="cuda", generator=tg).to(torch.bfloat16)
+            w_dev = (torch.randn((n, k), device="cuda", generator=tg) * 0.02).to(tdt)
+            x_dev = torch.randn(k, device="cuda", generator=tg).to(tdt)
             mats.append({"w": w_dev, "x": x_dev, "y": torch.empty(n, dtype=torch.float32, device="cuda")})
             continue
         if dt == "q8":
@@ -451,10 +456,12 @@ def run_single(args, torch, q8, np):
             if j == 0:
                 first = (qw, dw, x)
         else:
-            w = synth.bf16_weights(gr, n, k)
-            x = synth.bf16_activation(gr, k)
-            m = {"w": torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16),
-                 "x": torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)}
+            if dt == "f16":
+                w, x = synth.f16_weights(gr, n, k), synth.f16_activation(gr, k)
+            else:
+                w, x = synth.bf16_weights(gr, n, k), synth.bf16_activation(gr, k)
+            m = {"w": torch.from_numpy(w.view(np.int16)).cuda().view(tdt),
+                 "x": torch.from_numpy(x.view(np.int16)).cuda().view(tdt)}
             if j == 0:
                 first = (w, x)
         m["y"] = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -480,7 +487,7 @@ def run_single(args, torch, q8, np):
         yr, S = orc.q8_gemv(qw[rows], dw[rows], rq, rd)
     else:
         w, x = first
-        yr, S = orc.bf16_gemv(w[rows], x)
+        yr, S = (orc.f16_gemv if dt == "f16" else orc.bf16_gemv)(w[rows], x)
     rel = np.abs(mats[0]["y"].cpu().numpy()[rows].astype(np.float64) - yr) / S
     if not np.all(rel <= 1e-5):
         raise SystemExit(f"parity: sampled rows off by {rel.max():.2e} * S")
@@ -532,13 +539,13 @@ def run_single(args, torch, q8, np):
         t = a.elapsed_time(b) * 1e-3 / calls
     cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np)
     gbps = per / t / 1e9
-    r, w_ = q8.gemv_config(q8.Q8G_Q8_0 if dt == "q8" else q8.Q8G_BF16, n, k)
-    kname = f"{'q8_gemv' if dt == 'q8' else 'bf16_gemv'}[rows_per_wave={r},waves={w_}]"
+    r, w_ = q8.gemv_config({"q8": q8.Q8G_Q8_0, "bf16": q8.Q8G_BF16, "f16": q8.Q8G_F16}[dt], n, k)
+    kname = f"{dt if dt != 'q8' else 'q8'}_gemv[rows_per_wave={r},waves={w_}]"
     stack_bytes = 609613952 if dt == "q8" else 1143991808
     return {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": calls,
         "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8" if dt == "q8" else "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": {"q8": "int8", "bf16": "bf16", "f16": "f16"}[dt], "data": "synthetic",
         "config": {"workload": wl, "n": n, "k": k, "copies": copies, "cold_cache": cold, "bytes_per_call": per,
                    "call": "q8_gemv" if dt == "q8" else "gemv_stacked, two halves",
                    "timing": "per call after a 1 GiB flush" if cold else "HIP graph over one pass of the copies"},

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libq8gemv.so")
 Q8G_Q8_0 = 0
 Q8G_BF16 = 1
 Q8G_Q8_0_F32 = 2
+Q8G_F16 = 3
 FUSED_MAX_K = 16384
 MAX_PARTS = 4
 PROBE_SINK_WORDS = 16384
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH):
     lib.q8_quantize_act.argtypes = [_P, _P, _P, _I64, _P]
     lib.q8_gemv.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _P]
     lib.bf16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+    lib.f16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
     lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
@@ -96,7 +98,7 @@ def load_library(path: str = LIB_PATH):
     lib.q8_decode_stack.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
     lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
                                     ctypes.POINTER(ctypes.c_int)]
-    for fn in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "gemv_stacked", "q8g_probe_read", "q8g_flush",
+    for fn in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "f16_gemv", "gemv_stacked", "q8g_probe_read", "q8g_flush",
                "q8g_gemv_config", "q8_decode_stack"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -193,18 +195,35 @@ def bf16_gemv(w, x, y=None, residual=None, stream=None):
     return y
 
 
+def f16_gemv(w, x, y=None, residual=None, stream=None):
+    """y = w · x with IEEE binary16 inputs and f32 accumulation (+ residual). Returns y (f32 [N])."""
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w.device)
+    st = load_library().f16_gemv(
+        _ptr(w, "w", _H16), _ptr(x, "x", _H16, (k,)),
+        _ptr(residual, "residual", _F32, (n,), optional=True), _ptr(y, "y", _F32, (n,)), n, k,
+        _stream(stream))
+    _check("f16_gemv", st)
+    return y
+
+
 def gemv_stacked(parts, x, dx=None, stream=None):
     """One launch over 1..4 matrices sharing the input.
 
     parts: sequence of dicts with keys w (int8 [n, K] for Q8_0, bf16 [n, K]), dw (Q8_0
     scales, omitted for bf16), y (f32 [n], allocated if absent), residual (optional).
     x: int8 codes [K] with dx binary16 scales [K/32] (Q8_0); or f32 [K] for Q8_0 weights
-    (quantized inside the launch, dx None); or bf16 [K] (dx None).
+    (quantized inside the launch, dx None); or bf16 [K] / float16 [K] for bf16 / float16
+    weights (dx None). The weight dtype selects the kind.
     Returns the list of outputs.
     """
     if not 1 <= len(parts) <= MAX_PARTS:
         raise ValueError("1 to 4 parts")
     q8 = parts[0]["w"].dtype == torch.int8
+    f16 = parts[0]["w"].dtype == torch.float16
     fused = q8 and x.dtype == torch.float32
     k = x.shape[0]
     arr = (_Part * len(parts))()
@@ -218,14 +237,14 @@ def gemv_stacked(parts, x, dx=None, stream=None):
         if y is None:
             y = torch.empty(n, dtype=torch.float32, device=w.device)
         outs.append(y)
-        arr[i].w = _ptr(w, f"parts[{i}].w", _I8 if q8 else _B16)
+        arr[i].w = _ptr(w, f"parts[{i}].w", _I8 if q8 else ((torch.float16,) if f16 else _B16))
         arr[i].dw = _ptr(p.get("dw"), f"parts[{i}].dw", _H16, (n, k // 32), optional=not q8) if q8 else None
         arr[i].n = n
         arr[i].y = _ptr(y, f"parts[{i}].y", _F32, (n,))
         arr[i].residual = _ptr(p.get("residual"), f"parts[{i}].residual", _F32, (n,), optional=True)
-    px = _ptr(x, "x", _F32 if fused else (_I8 if q8 else _B16), (k,))
+    px = _ptr(x, "x", _F32 if fused else (_I8 if q8 else ((torch.float16,) if f16 else _B16)), (k,))
     pdx = _ptr(dx, "dx", _H16, (k // 32,)) if (q8 and not fused) else None
-    dt = Q8G_Q8_0_F32 if fused else (Q8G_Q8_0 if q8 else Q8G_BF16)
+    dt = Q8G_Q8_0_F32 if fused else (Q8G_Q8_0 if q8 else (Q8G_F16 if f16 else Q8G_BF16))
     st = load_library().gemv_stacked(dt, arr, len(parts), px, pdx, k, _stream(stream))
     _check("gemv_stacked", st)
     return outs

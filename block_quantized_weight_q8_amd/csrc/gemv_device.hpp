@@ -146,6 +146,29 @@ __device__ __forceinline__ float bf16_chunk_dot(const int4 &wv, const float (&xf
     return part;
 }
 
+// f16 ("One level down", The bench: the same engine in f16): eight binary16
+// values per lane, converted exactly to f32; each product of two binary16
+// values is exact in f32 (11 + 11 significant bits).
+__device__ __forceinline__ void f16_unpack(const int4 &v, float (&f)[8])
+{
+    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = f16_bits_to_f32((uint16_t)(w[i] & 0xFFFFu));
+        f[2 * i + 1] = f16_bits_to_f32((uint16_t)(w[i] >> 16));
+    }
+}
+
+__device__ __forceinline__ float f16_chunk_dot(const int4 &wv, const float (&xf)[8])
+{
+    float wf[8];
+    f16_unpack(wv, wf);
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part = __builtin_fmaf(wf[i], xf[i], part);
+    return part;
+}
+
 // Activation quantization of four consecutive values of one 32-value block
 // held by an aligned group of 8 lanes ("Filling in the blanks", Fast Decode:
 // quantize an activation once into the weights' block format):

@@ -47,8 +47,12 @@ using namespace q8g;
 constexpr int kMaxParts = 4;
 
 // Q8: x = int8 codes + binary16 scales; BF16: x = bf16; Q8F32: x = f32, quantized
-// by every workgroup into LDS before use (one launch instead of two).
-enum class Dt { Q8, BF16, Q8F32 };
+// by every workgroup into LDS before use (one launch instead of two); F16:
+// binary16 weights and activation.
+enum class Dt { Q8, BF16, Q8F32, F16 };
+
+// 16-bit float weights (no block scales), two bytes per element
+constexpr bool is_16bit(Dt dt) { return dt == Dt::BF16 || dt == Dt::F16; }
 
 constexpr int kMaxFusedK = 16384;  // LDS bytes for the codes of a fused launch
 
@@ -140,7 +144,7 @@ __device__ __forceinline__ void load_batch(const RowRef (&rows)[R], const char *
             const int64_t off = c * kChunk + lane_off;
             const int64_t o = off < row_bytes ? off : 0;
             b.w[j] = load16_stream(rows[r].w + o);
-            if constexpr (DT != Dt::BF16) b.s[j] = load_u16_stream(rows[r].dw + (o >> 5));
+            if constexpr (!is_16bit(DT)) b.s[j] = load_u16_stream(rows[r].dw + (o >> 5));
             if constexpr (XG) {
                 if (r == 0) {
                     b.x[j] = load16(x + o);
@@ -154,7 +158,7 @@ __device__ __forceinline__ void load_batch(const RowRef (&rows)[R], const char *
 // Consume a batch. Q8_0: one exact int32 block sum per item (v_dot4 + one DPP
 // add), scaled by dw*dx (exact in f32) with one fma; the odd lane of each block
 // pair and lanes past the row end add zero. bf16: eight exact products summed
-// into a chunk partial, then added to the row's accumulator.
+// into a chunk partial, then added to the row's accumulator (f16 the same).
 template <Dt DT, int R, bool XG>
 __device__ __forceinline__ void compute_batch(const Batch &b, const int8_t *__restrict__ s_qx,
                                               const float *__restrict__ s_dx, int64_t c0, int64_t nchunk,
@@ -172,8 +176,11 @@ __device__ __forceinline__ void compute_batch(const Batch &b, const int8_t *__re
                 const int64_t off = c * kChunk + lane_off;
                 const bool active = off < row_bytes;
                 const int64_t o = active ? off : 0;
-                if constexpr (DT == Dt::BF16) {
-                    bf16_unpack(b.x[j], xf);
+                if constexpr (is_16bit(DT)) {
+                    if constexpr (DT == Dt::BF16)
+                        bf16_unpack(b.x[j], xf);
+                    else
+                        f16_unpack(b.x[j], xf);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) xf[i] = active ? xf[i] : 0.0f;
                 } else if constexpr (XG) {
@@ -186,6 +193,8 @@ __device__ __forceinline__ void compute_batch(const Batch &b, const int8_t *__re
             }
             if constexpr (DT == Dt::BF16) {
                 acc[r] += bf16_chunk_dot(b.w[j], xf);
+            } else if constexpr (DT == Dt::F16) {
+                acc[r] += f16_chunk_dot(b.w[j], xf);
             } else {
                 const int s = q8_block_sum(b.w[j], xq);  // the block's exact int32 sum
                 acc[r] = __builtin_fmaf((float)s, f16_bits_to_f32(b.s[j]) * xs, acc[r]);
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     const bool has_rows = row0 < n_total;  // wave-uniform
     if (!FUSED && !has_rows) return;
 
-    const int64_t row_bytes = DT == Dt::BF16 ? 2 * K : K;
+    const int64_t row_bytes = is_16bit(DT) ? 2 * K : K;
     const int64_t nb = K / 32;
     const int64_t nchunk = (row_bytes + kChunk - 1) / kChunk;
     constexpr int CB = kBatch / R;  // chunks per batch
@@ -387,8 +396,8 @@ struct Config {
 Config pick_config(q8g_dtype dt, int64_t n_total)
 {
     Config c{rows_per_wave(n_total), kWavesPerGroup};
-    if (dt == Q8G_BF16) {
-        // bf16 rows are twice as long: two rows per wave already keep 4 KiB in flight
+    if (dt == Q8G_BF16 || dt == Q8G_F16) {
+        // 16-bit rows are twice as long: two rows per wave already keep 4 KiB in flight
         if (c.rows > 2) c.rows = 2;
         if (Q8G_BF16_ROWS) c.rows = Q8G_BF16_ROWS;
     }
@@ -424,11 +433,11 @@ hipError_t dispatch_gemv(Config c, const Parts &p, const void *x, const uint16_t
 q8g_status prepare(q8g_dtype dt, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx, int64_t K,
                    Parts &out, int64_t &n_total)
 {
-    if (dt != Q8G_Q8_0 && dt != Q8G_BF16 && dt != Q8G_Q8_0_F32) return Q8G_ERR_ARG;
+    if (dt != Q8G_Q8_0 && dt != Q8G_BF16 && dt != Q8G_Q8_0_F32 && dt != Q8G_F16) return Q8G_ERR_ARG;
     if (!parts) return Q8G_ERR_NULL;
     if (nparts < 1 || nparts > kMaxParts) return Q8G_ERR_ARG;
     if (K < 0 || K > kMaxElems) return Q8G_ERR_SHAPE;
-    const bool q8 = dt != Q8G_BF16;          // Q8_0 weights (codes + scales)
+    const bool q8 = dt == Q8G_Q8_0 || dt == Q8G_Q8_0_F32;  // Q8_0 weights (codes + scales)
     const bool fused = dt == Q8G_Q8_0_F32;   // x is f32, quantized in the launch
     if (q8 ? (K % 32) : (K % 8)) return Q8G_ERR_SHAPE;
     if (fused && K > kMaxFusedK) return Q8G_ERR_SHAPE;
@@ -504,6 +513,7 @@ q8g_status run(q8g_dtype dt, const q8g_part *parts, int nparts, const void *x, c
     const Config c = pick_config(dt, n_total);
     const hipError_t e = dt == Q8G_Q8_0       ? dispatch_gemv<Dt::Q8>(c, p, x, dx, K, n_total, s)
                          : dt == Q8G_Q8_0_F32 ? dispatch_gemv<Dt::Q8F32>(c, p, x, nullptr, K, n_total, s)
+                         : dt == Q8G_F16      ? dispatch_gemv<Dt::F16>(c, p, x, nullptr, K, n_total, s)
                                               : dispatch_gemv<Dt::BF16>(c, p, x, dx, K, n_total, s);
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
@@ -549,6 +559,14 @@ q8g_status bf16_gemv(const uint16_t *w, const uint16_t *x, const float *residual
     return run(Q8G_BF16, &part, 1, x, nullptr, K, stream);
 }
 
+q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, float *y, int64_t N, int64_t K,
+                    void *stream)
+{
+    if (N < 0) return Q8G_ERR_SHAPE;
+    const q8g_part part = {w, nullptr, N, y, residual};
+    return run(Q8G_F16, &part, 1, x, nullptr, K, stream);
+}
+
 q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx,
                         int64_t K, void *stream)
 {
@@ -557,7 +575,7 @@ q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, cons
 
 q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows, int *waves)
 {
-    if (dtype != Q8G_Q8_0 && dtype != Q8G_BF16 && dtype != Q8G_Q8_0_F32) return Q8G_ERR_ARG;
+    if (dtype != Q8G_Q8_0 && dtype != Q8G_BF16 && dtype != Q8G_Q8_0_F32 && dtype != Q8G_F16) return Q8G_ERR_ARG;
     if (n_total < 0 || K < 0) return Q8G_ERR_SHAPE;
     if (!rows || !waves) return Q8G_ERR_NULL;
     const Config c = pick_config(dtype, n_total);

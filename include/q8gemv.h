@@ -60,7 +60,8 @@ typedef enum {
 
 /* Q8G_Q8_0_F32: Q8_0 weights with an f32 activation that the launch itself
  * quantizes (exactly as q8_quantize_act) before the dot products; K <= 16384. */
-typedef enum { Q8G_Q8_0 = 0, Q8G_BF16 = 1, Q8G_Q8_0_F32 = 2 } q8g_dtype;
+/* Q8G_F16: IEEE binary16 weights and activation, f32 accumulation. */
+typedef enum { Q8G_Q8_0 = 0, Q8G_BF16 = 1, Q8G_Q8_0_F32 = 2, Q8G_F16 = 3 } q8g_dtype;
 
 /* Quantize an activation once into the Q8_0 block format ([P] Fast Decode).
  * For each block b of 32 consecutive values of x (f32 [K]):
@@ -88,10 +89,17 @@ q8g_status q8_gemv(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const
 q8g_status bf16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, float *y,
                      int64_t N, int64_t K, void *stream);
 
+/* f16 GEMV ([H] The bench: the same engine in f16, where f16 is the native
+ * 16-bit format): y[n] = sum_k f32(w[n][k]) * f32(x[k]) (f32 accumulate)
+ * (+ residual[n]), w and x IEEE binary16 bits. Every product of two binary16
+ * values is exact in f32. Same layout and rules as bf16_gemv. */
+q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, float *y,
+                    int64_t N, int64_t K, void *stream);
+
 /* One matrix of a stacked projection. */
 typedef struct {
-    const void *w;         /* Q8_0: int8 codes [n][K]; bf16: uint16 [n][K] */
-    const uint16_t *dw;    /* Q8_0: binary16 scale bits [n][K/32]; bf16: ignored (may be NULL) */
+    const void *w;         /* Q8_0: int8 codes [n][K]; bf16 / f16: uint16 [n][K] */
+    const uint16_t *dw;    /* Q8_0: binary16 scale bits [n][K/32]; bf16 / f16: ignored (may be NULL) */
     int64_t n;             /* output rows of this part (>= 0) */
     float *y;              /* f32 [n] */
     const float *residual; /* f32 [n] or NULL; may equal y */
@@ -100,7 +108,8 @@ typedef struct {
 /* Stacked projection ([P] Fast Decode: stack projections that read the same
  * input; [H] Emitting for a GPU: gate and up in one go). One launch computes
  * every part against the shared input: Q8_0 takes x = int8 codes [K] and
- * dx = binary16 scale bits [K/32]; bf16 takes x = bf16 [K] and ignores dx;
+ * dx = binary16 scale bits [K/32]; bf16 and f16 take x = bf16 / f16 [K] and
+ * ignore dx;
  * Q8G_Q8_0_F32 takes x = f32 [K] (16-byte aligned, K <= 16384), quantizes it
  * inside the launch, and ignores dx ([P] Fast Decode: quantize the activation
  * once and share it, here once per launch for all of its parts).

@@ -6,7 +6,7 @@ shares no code with the HIP library. Arrays are numpy; results are f64.
 
 What it computes is stated, with its sources, at the top of oracle.c:
 the Q8_0 activation quantizer, the per-block int32 dot, the Q8_0 GEMV and the
-bf16 GEMV of "Filling in the blanks: Inference using Phobos" (section Fast
+bf16 and f16 GEMVs of "Filling in the blanks: Inference using Phobos" (section Fast
 Decode) and "One level down: #002 the same compiler on a GPU" (sections
 Emitting for a GPU and The numerical contract).
 """
@@ -62,6 +62,10 @@ def _bind(lib):
     lib.orc_q8_gemv_mt.restype = ctypes.c_int
     lib.orc_bf16_gemv_mt.argtypes = [_P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int]
     lib.orc_bf16_gemv_mt.restype = ctypes.c_int
+    lib.orc_f16_gemv.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
+    lib.orc_f16_gemv.restype = None
+    lib.orc_f16_gemv_mt.argtypes = [_P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int]
+    lib.orc_f16_gemv_mt.restype = ctypes.c_int
     return lib
 
 
@@ -142,7 +146,13 @@ class Oracle:
             self.lib.orc_q8_gemv(pw, pdw, pq, pdx, pr, n, k, y.ctypes.data, s.ctypes.data)
         return y, s
 
+    def f16_gemv(self, w, x, residual=None, nthreads: int = 0):
+        return self._16bit_gemv("f16", w, x, residual, nthreads)
+
     def bf16_gemv(self, w, x, residual=None, nthreads: int = 0):
+        return self._16bit_gemv("bf16", w, x, residual, nthreads)
+
+    def _16bit_gemv(self, kind, w, x, residual, nthreads):
         w, pw = _c(w, np.uint16)
         x, px = _c(x, np.uint16)
         n, k = w.shape
@@ -153,12 +163,14 @@ class Oracle:
             assert residual.shape == (n,)
         y = np.empty(n, np.float64)
         s = np.empty(n, np.float64)
+        st = getattr(self.lib, f"orc_{kind}_gemv")
+        mt = getattr(self.lib, f"orc_{kind}_gemv_mt")
         if nthreads:
-            rc = self.lib.orc_bf16_gemv_mt(pw, px, pr, n, k, y.ctypes.data, s.ctypes.data, nthreads)
+            rc = mt(pw, px, pr, n, k, y.ctypes.data, s.ctypes.data, nthreads)
             if rc < 0:
                 raise MemoryError("oracle thread setup failed")
         else:
-            self.lib.orc_bf16_gemv(pw, px, pr, n, k, y.ctypes.data, s.ctypes.data)
+            st(pw, px, pr, n, k, y.ctypes.data, s.ctypes.data)
         return y, s
 
 
@@ -186,3 +198,7 @@ def q8_gemv(qw, dw, qx, dx, residual=None, nthreads: int = 0):
 
 def bf16_gemv(w, x, residual=None, nthreads: int = 0):
     return get().bf16_gemv(w, x, residual, nthreads)
+
+
+def f16_gemv(w, x, residual=None, nthreads: int = 0):
+    return get().f16_gemv(w, x, residual, nthreads)

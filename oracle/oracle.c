@@ -1,6 +1,6 @@
 /*
  * CPU oracle for the decode-step matrix-vector product y = W·x with Q8_0
- * block-quantized weights and with bf16 weights.
+ * block-quantized weights and with bf16 or f16 weights.
  *
  * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
  * statement of what the GPU path must compute. Only the test suite, the smoke
@@ -16,9 +16,9 @@
  *        is quantized once and shared; projections that read the same input are
  *        stacked; the residual add is folded into the matmul.
  *   [H]  "One level down: #002 the same compiler on a GPU", sections "Emitting
- *        for a GPU" (the bf16 gate+up matvec, rows of 16-byte chunks) and
+ *        for a GPU" (the bf16 gate+up matvec, rows of 16-byte chunks),
  *        "The numerical contract" (bf16 weights and activations, f32
- *        accumulators).
+ *        accumulators) and "The bench" (the same engine in f16).
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - weight and activation block scales are IEEE binary16;
@@ -29,7 +29,8 @@
  *   - the residual is added once, after the whole dot.
  *
  * Precision: every Q8_0 block term isum·dw·dx is exact in f64 (20 + 11 + 11
- * significant bits); every bf16 product is exact in f64 (8 + 8 bits). Sums are
+ * significant bits); every bf16 product is exact in f64 (8 + 8 bits), every
+ * f16 product too (11 + 11 bits). Sums are
  * taken in f64 in ascending index order. The quantizer works in f32, the
  * precision in which the method takes that integer decision.
  *
@@ -38,7 +39,7 @@
  * against numpy's cast; the quantizer against an independent numpy float32
  * quantizer and against closed forms (constant, one-hot, zero and tie
  * blocks); the block integer sums against Python-integer brute force and
- * closed forms; both GEMVs against exact rational arithmetic on tiny shapes,
+ * closed forms; the GEMVs against exact rational arithmetic on tiny shapes,
  * against a numpy f64 matmul of the dequantized operands, and against closed
  * forms and invariants.
  */
@@ -207,10 +208,31 @@ void orc_bf16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, 
     }
 }
 
+/* ---- f16 GEMV ([H] The bench: the same engine in f16): y[n] =
+ * sum_k f16(w[n][k])·f16(x[k]) (+ r[n]); each product exact in f64. --------- */
+void orc_f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, int64_t N, int64_t K,
+                  double *y, double *S)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = orc_f16_value(w[n * K + k]) * orc_f16_value(x[k]);
+            acc += p;
+            mag += fabs(p);
+        }
+        if (residual) {
+            acc += (double)residual[n];
+            mag += fabs((double)residual[n]);
+        }
+        y[n] = acc;
+        S[n] = mag;
+    }
+}
+
 /* ---- row-partitioned threading (same per-row arithmetic, so identical
  * results to the single-threaded calls) ------------------------------------ */
 typedef struct {
-    int bf16;
+    int bf16; /* 0: Q8_0, 1: bf16, 2: f16 */
     const void *w;
     const uint16_t *dw;
     const void *x;
@@ -227,9 +249,12 @@ static void *orc_run_job(void *arg)
     if (rows <= 0)
         return NULL;
     const float *r = j->residual ? j->residual + j->n0 : NULL;
-    if (j->bf16)
+    if (j->bf16 == 1)
         orc_bf16_gemv((const uint16_t *)j->w + j->n0 * j->K, (const uint16_t *)j->x, r, rows, j->K,
                       j->y + j->n0, j->S + j->n0);
+    else if (j->bf16 == 2)
+        orc_f16_gemv((const uint16_t *)j->w + j->n0 * j->K, (const uint16_t *)j->x, r, rows, j->K,
+                     j->y + j->n0, j->S + j->n0);
     else
         orc_q8_gemv((const int8_t *)j->w + j->n0 * j->K, j->dw + j->n0 * (j->K / ORC_QBLOCK),
                     (const int8_t *)j->x, j->dx, r, rows, j->K, j->y + j->n0, j->S + j->n0);
@@ -282,5 +307,12 @@ int orc_bf16_gemv_mt(const uint16_t *w, const uint16_t *x, const float *residual
                      int64_t K, double *y, double *S, int nthreads)
 {
     orc_job p = {1, w, NULL, x, NULL, residual, 0, 0, K, y, S};
+    return orc_run_threads(p, N, nthreads);
+}
+
+int orc_f16_gemv_mt(const uint16_t *w, const uint16_t *x, const float *residual, int64_t N,
+                    int64_t K, double *y, double *S, int nthreads)
+{
+    orc_job p = {2, w, NULL, x, NULL, residual, 0, 0, K, y, S};
     return orc_run_threads(p, N, nthreads);
 }

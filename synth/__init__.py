@@ -16,6 +16,7 @@ on a GPU" (§Emitting for a GPU: the bf16 gate+up projection, 1024->7168 on the
 * Q8_0 activation: N(0, 1) in f32 (quantized later by the method itself).
 * bf16 weights: N(0, 1) * 0.02 in f32, rounded to bf16 (nearest, ties to even).
 * bf16 activation: N(0, 1) in f32, rounded to bf16.
+* f16 weights / activation: as bf16, rounded to IEEE binary16 instead.
 * residual: N(0, 1) in f32.
 
 Every matrix j of workload `tag` draws from
@@ -36,6 +37,7 @@ TAG_BF16_GATEUP = 1
 TAG_Q8_STACK = 2
 TAG_BF16_4B_GATEUP = 3
 TAG_Q8_HEAD = 4
+TAG_F16_GATEUP = 5
 TAG_TEST = 100
 
 
@@ -81,6 +83,16 @@ def bf16_weights(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
 
 def bf16_activation(rng: np.random.Generator, k: int) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal(k, dtype=np.float32))
+
+
+def f16_weights(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    w = rng.standard_normal((n, k), dtype=np.float32)
+    w *= np.float32(0.02)
+    return f32_to_f16_bits(w)
+
+
+def f16_activation(rng: np.random.Generator, k: int) -> np.ndarray:
+    return f32_to_f16_bits(rng.standard_normal(k, dtype=np.float32))
 
 
 def residual_f32(rng: np.random.Generator, n: int) -> np.ndarray:
@@ -138,6 +150,7 @@ def q8_quantize_bytes(k: int) -> int:
 
 
 def bf16_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
+    """Algorithmic bytes of one 16-bit (bf16 or f16) GEMV."""
     b = 2 * n * k + 2 * k + 4 * n
     return b + (n * 4 if residual else 0)
 

@@ -390,6 +390,49 @@ def pin_bf16_residual(o):
     assert np.array_equal(y, r.astype(np.float64))
 
 
+# ----------------------------------------------------------------------------- f16 GEMV
+
+
+def pin_f16_integer_valued(o):
+    g = rng(20)
+    n, k = 29, 1024
+    wi = g.integers(-8, 9, (n, k))
+    xi = g.integers(-8, 9, k)
+    w = synth.f32_to_f16_bits(wi.astype(np.float32))
+    x = synth.f32_to_f16_bits(xi.astype(np.float32))
+    y, S = o.f16_gemv(w, x)
+    assert np.array_equal(y, (wi @ xi).astype(np.float64))
+    assert np.array_equal(S, (np.abs(wi) @ np.abs(xi)).astype(np.float64))
+
+
+def pin_f16_vs_dense(o):
+    for j, (n, k) in enumerate(((48, 1024), (19, 2560), (5, 8))):
+        g = rng(21 + j)
+        w = synth.f16_weights(g, n, k)
+        x = synth.f16_activation(g, k)
+        r = synth.residual_f32(g, n)
+        y, S = o.f16_gemv(w, x, r)
+        W = np_f16(w).reshape(n, k)
+        X = np_f16(x)
+        close_to(y, W @ X + r, S, k * 2.0**-52)
+        close_to(S, np.abs(W) @ np.abs(X) + np.abs(r), S, k * 2.0**-52)
+
+
+def pin_f16_exact_rational_subnormal(o):
+    """Tiny shape with binary16 subnormal weights: exact rational sum."""
+    g = rng(24)
+    n, k = 3, 16
+    w = g.integers(1, 0x400, (n, k)).astype(np.uint16) | (g.integers(0, 2, (n, k)).astype(np.uint16) << 15)
+    x = synth.f16_activation(g, k)
+    y, S = o.f16_gemv(w, x)
+    W = np_f16(w).reshape(n, k)
+    X = np_f16(x)
+    for row in range(n):
+        ex = sum(Fraction(float(W[row, i])) * Fraction(float(X[i])) for i in range(k))
+        assert abs(Fraction(y[row]) - ex) <= Fraction(k * 2.0**-53) * Fraction(S[row])
+    assert np.all(S > 0)
+
+
 # ----------------------------------------------------------------------------- threading
 
 
@@ -406,6 +449,12 @@ def pin_threads_match_single(o):
     y, S = o.bf16_gemv(w, xb)
     for t in (2, 7, 100):
         yt, St = o.bf16_gemv(w, xb, nthreads=t)
+        assert np.array_equal(yt, y) and np.array_equal(St, S)
+    wf = synth.f16_weights(g, 53, 256)
+    xf = synth.f16_activation(g, 256)
+    y, S = o.f16_gemv(wf, xf)
+    for t in (3, 64):
+        yt, St = o.f16_gemv(wf, xf, nthreads=t)
         assert np.array_equal(yt, y) and np.array_equal(St, S)
 
 

@@ -40,6 +40,7 @@ def lib():
     L.q8_quantize_act.argtypes = [P, P, P, I64, P]
     L.q8_gemv.argtypes = [P, P, P, P, P, P, I64, I64, P]
     L.bf16_gemv.argtypes = [P, P, P, P, I64, I64, P]
+    L.f16_gemv.argtypes = [P, P, P, P, I64, I64, P]
     L.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(Part), ctypes.c_int, P, P, I64, P]
     L.q8g_status_str.argtypes = [ctypes.c_int]
     L.q8g_status_str.restype = ctypes.c_char_p
@@ -50,7 +51,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    for expected in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "gemv_stacked", "q8g_status_str",
+    for expected in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "f16_gemv", "gemv_stacked", "q8g_status_str",
                      "q8g_probe_read", "q8g_flush"):
         assert expected in names
     for n in names:
@@ -104,8 +105,9 @@ def test_q8_gemv_validation(lib):
     assert g(W, DW, QX, DX, Y + 4, Y, 8, 64, None) == ERR_OVERLAP  # partial residual alias
 
 
-def test_bf16_gemv_validation(lib):
-    g = lib.bf16_gemv
+@pytest.mark.parametrize("name", ["bf16_gemv", "f16_gemv"])
+def test_16bit_gemv_validation(lib, name):
+    g = getattr(lib, name)
     assert g(W, X, None, Y, 8, 12, None) == ERR_SHAPE  # K % 8
     assert g(W, X, None, Y, -3, 16, None) == ERR_SHAPE
     assert g(None, X, None, Y, 8, 16, None) == ERR_NULL
@@ -113,6 +115,9 @@ def test_bf16_gemv_validation(lib):
     assert g(W + 2, X, None, Y, 8, 16, None) == ERR_ALIGN
     assert g(W, X + 2, None, Y, 8, 16, None) == ERR_ALIGN
     assert g(W, X, None, X, 8, 16, None) == ERR_OVERLAP
+    assert g(W, X, R + 2, Y, 8, 16, None) == ERR_ALIGN
+    assert g(W, X, None, Y + 2, 8, 16, None) == ERR_ALIGN
+    assert g(W, X, None, W + 16, 8, 16, None) == ERR_OVERLAP
     assert g(None, None, None, None, 0, 16, None) == OK
 
 
@@ -130,6 +135,9 @@ def test_stacked_validation(lib):
     assert s(0, one, 0, QX, DX, 64, None) == ERR_ARG
     assert s(0, one, 5, QX, DX, 64, None) == ERR_ARG
     assert s(7, one, 1, QX, DX, 64, None) == ERR_ARG
+    assert s(4, one, 1, QX, DX, 64, None) == ERR_ARG  # one past the last kind
+    assert s(3, parts((W, None, 8, Y, None)), 1, X, None, 20, None) == ERR_SHAPE  # f16: K % 8
+    assert s(3, parts((W + 2, None, 8, Y, None)), 1, X, None, 64, None) == ERR_ALIGN
     assert s(0, None, 1, QX, DX, 64, None) == ERR_NULL
     assert s(0, parts((W, DW, -1, Y, None)), 1, QX, DX, 64, None) == ERR_SHAPE
     assert s(0, one, 1, QX, None, 64, None) == ERR_NULL  # Q8_0 needs dx

@@ -292,6 +292,67 @@ def test_bf16_integer_valued_bit_exact(q8, orc, n, k):
     assert np.array_equal(y.astype(np.float64), yr)
 
 
+# --------------------------------------------------------------------------- f16 GEMV
+
+
+@pytest.mark.parametrize("n,k", BF16_SHAPES)
+@pytest.mark.parametrize("resid", [False, True])
+def test_f16_gemv_parity(q8, orc, n, k, resid):
+    print_case("f16_gemv", n, k, resid)
+    g = synth.rng_for(synth.TAG_TEST, 520 + n + k)
+    w = synth.f16_weights(g, n, k)
+    x = synth.f16_activation(g, k)
+    r = synth.residual_f32(g, n)
+    y = q8.f16_gemv(h16(w), h16(x), residual=dev(r) if resid else None)
+    yr, S = orc.f16_gemv(w, x, r if resid else None)
+    within(host(y), yr, S, f"f16 {n}x{k}")
+
+
+@pytest.mark.parametrize("n,k", [(7168, 1024), (129, 2560), (9, 8)])
+def test_f16_integer_valued_bit_exact(q8, orc, n, k):
+    print_case("f16 integer-valued", n, k)
+    g = synth.rng_for(synth.TAG_TEST, 521)
+    wi = g.integers(-8, 9, (n, k))
+    xi = g.integers(-8, 9, k)
+    w = synth.f32_to_f16_bits(wi.astype(np.float32))
+    x = synth.f32_to_f16_bits(xi.astype(np.float32))
+    y = host(q8.f16_gemv(h16(w), h16(x)))
+    yr, _ = orc.f16_gemv(w, x)
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+def test_f16_subnormal_weights(q8, orc):
+    """Weights in the binary16 subnormal range must decode to their values, not to zero."""
+    n, k = 77, 1024
+    print_case("f16 subnormal weights", n, k)
+    g = synth.rng_for(synth.TAG_TEST, 522)
+    w = g.integers(1, 0x400, (n, k)).astype(np.uint16) | (g.integers(0, 2, (n, k)).astype(np.uint16) << 15)
+    x = synth.f16_activation(g, k)
+    y = host(q8.f16_gemv(h16(w), h16(x)))
+    yr, S = orc.f16_gemv(w, x)
+    assert np.all(S > 0)
+    within(y, yr, S, "f16 subnormal")
+
+
+def test_f16_stacked_halves(q8, orc):
+    """The 1024 -> 7168 gate+up in binary16 as two 3584-row halves in one launch."""
+    n, k = 7168, 1024
+    print_case("f16 stacked halves", n, k)
+    g = synth.rng_for(synth.TAG_TEST, 523)
+    w = synth.f16_weights(g, n, k)
+    x = synth.f16_activation(g, k)
+    r = synth.residual_f32(g, n)
+    Wt, Xt, Rt = h16(w), h16(x), dev(r)
+    whole = host(q8.f16_gemv(Wt, Xt))
+    outs = q8.gemv_stacked([{"w": Wt[:3584]}, {"w": Wt[3584:], "residual": Rt[3584:]}], Xt)
+    lo, hi = host(outs[0]), host(outs[1])
+    assert np.array_equal(lo, whole[:3584])
+    assert np.array_equal(hi, host(q8.f16_gemv(Wt[3584:], Xt, residual=Rt[3584:])))
+    yr, S = orc.f16_gemv(w, x)
+    within(lo, yr[:3584], S[:3584], "f16 first half")
+    within(hi, yr[3584:] + r[3584:], S[3584:] + np.abs(r[3584:].astype(np.float64)), "f16 second half")
+
+
 # --------------------------------------------------------------------------- stacked
 
 

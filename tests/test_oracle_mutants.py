@@ -43,8 +43,15 @@ MUTANTS = [
      "for (int64_t b = 0; b < nb - 1; ++b) {\n            int32_t s = 0, sa = 0;"),
     ("bf16_wrong_x_index", "orc_bf16_value(x[k]);", "orc_bf16_value(x[0]);"),
     ("bf16_reversed_row", "orc_bf16_value(w[n * K + k])", "orc_bf16_value(w[n * K + (K - 1 - k)])"),
-    ("bf16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row",
+    ("bf16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- f16",
+     "mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- f16"),
+    ("f16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row",
      "mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row"),
+    ("f16_reversed_row", "orc_f16_value(w[n * K + k])", "orc_f16_value(w[n * K + (K - 1 - k)])"),
+    ("f16_decoded_as_bf16", "double p = orc_f16_value(w[n * K + k]) * orc_f16_value(x[k]);",
+     "double p = orc_bf16_value(w[n * K + k]) * orc_f16_value(x[k]);"),
+    ("threads_f16_as_bf16", "orc_job p = {2, w, NULL, x, NULL, residual, 0, 0, K, y, S};",
+     "orc_job p = {1, w, NULL, x, NULL, residual, 0, 0, K, y, S};"),
     ("threads_drop_row", "jobs[t].n1 = N * (t + 1) / nthreads;", "jobs[t].n1 = N * (t + 1) / nthreads - (t == 0);"),
 ]
 
