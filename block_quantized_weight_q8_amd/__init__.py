@@ -28,6 +28,7 @@ Q8G_Q8_0_F32 = 2
 Q8G_F16 = 3
 FUSED_MAX_K = 16384
 MAX_PARTS = 4
+BATCH_MAX = 16
 PROBE_SINK_WORDS = 16384
 
 _STATUS = {
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH):
     lib.q8_gemv.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _P]
     lib.bf16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
     lib.f16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+    lib.q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
     lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
@@ -169,6 +171,23 @@ def q8_gemv(qw, dw, qx, dx, y=None, residual=None, stream=None):
         _ptr(dx, "dx", _H16, (k // 32,)), _ptr(residual, "residual", _F32, (n,), optional=True),
         _ptr(y, "y", _F32, (n,)), n, k, _stream(stream))
     _check("q8_gemv", st)
+    return y
+
+
+def q8_gemv_batch(qw, dw, qx, dx, y=None, residual=None, stream=None):
+    """Small batch: y[b] = Q8_0(qw, dw) · (qx[b], dx[b]) (+ residual[b]) for B <= 16 activation
+    vectors sharing one pass over the weights. qx int8 [B, K], dx [B, K/32]; returns y (f32 [B, N])."""
+    if qw.dim() != 2 or qx.dim() != 2:
+        raise ValueError("qw must be [N, K] and qx [B, K]")
+    n, k = qw.shape
+    b = qx.shape[0]
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=qw.device)
+    st = load_library().q8_gemv_batch(
+        _ptr(qw, "qw", _I8), _ptr(dw, "dw", _H16, (n, k // 32)), _ptr(qx, "qx", _I8, (b, k)),
+        _ptr(dx, "dx", _H16, (b, k // 32)), _ptr(residual, "residual", _F32, (b, n), optional=True),
+        _ptr(y, "y", _F32, (b, n)), n, k, b, _stream(stream))
+    _check("q8_gemv_batch", st)
     return y
 
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq8gemv.so")
-SOURCES = ["q8gemv.hip", "stack.hip", "probe.hip"]
+SOURCES = ["q8gemv.hip", "batch.hip", "stack.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -22,6 +22,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep hipcc from forming packed-f32 arithmetic on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs (the batched GEMV scales them at
+    # once; accumulation registers would only add copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

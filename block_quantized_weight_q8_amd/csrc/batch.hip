@@ -1,0 +1,340 @@
+// Small-batch Q8_0 decode GEMV on the matrix cores (q8_gemv_batch in
+// include/q8gemv.h): B <= 16 activation vectors share one pass over the
+// weights, so each weight byte read from HBM serves B outputs.
+//
+// What is computed is the Q8_0 product of "Filling in the blanks: Inference
+// using Phobos", section Fast Decode (32 int8 codes per block with their own
+// scale, block math in integers), once per activation vector:
+//   y[b][n] = sum_blk isum(n, b, blk) * (f16(dw[n][blk]) * f16(dx[b][blk])) (+ residual[b][n]).
+// With B vectors the work is a skinny dense contraction, so the integer block
+// sums come from v_mfma_i32_16x16x64_i8 rather than from per-lane dot4:
+//
+//  * One MFMA tile is 16 activation vectors (M, zero beyond B) x 16 weight rows
+//    (N) x 64 k (two Q8_0 blocks). Operand lane l holds 16 contiguous bytes:
+//    row l % 16, k group l / 16 (groups 0-1 are the first block, 2-3 the
+//    second), so a wave's weight load is 16 rows x 64 contiguous bytes.
+//  * Each block needs its own exact int32 sum before its scales apply, so a
+//    step issues two MFMAs on the same weight operand, the first with the
+//    activation groups of the second block zeroed and the second with those of
+//    the first block zeroed. The MFMA work doubles; it stays far below the
+//    matrix cores' rate, and the weight stream is what bounds the kernel.
+//  * Lane l of the result holds vectors 4(l/16)..+3 of weight row l % 16, so
+//    a lane applies one weight scale and four activation scales per block,
+//    as float(isum) * (dw * dx) accumulated in f32 (the product of two
+//    binary16 values is exact in f32, and so is float(isum)).
+//  * The activation codes and scales of a tile of kTileK columns are copied
+//    into LDS with direct global-to-LDS loads (gfx950 global_load_lds): no
+//    registers hold them in flight and no wave waits on them before its
+//    weight stream is requested. Each lane picks its own source address, so
+//    the copy lays the codes out XOR-swizzled (16-byte chunk c of vector b at
+//    position c ^ b within its group of 16), which makes the 16 vectors' reads
+//    of one k group hit distinct banks, and gathers the scales transposed to
+//    [block][vector], so a lane reads its four vectors' scales in one load.
+//  * Each wave also copies its 16 rows' weight scales for the tile into LDS
+//    (two rows' 64-byte scale runs per load). Loading them per step instead
+//    would make every step's load touch 16 rows' scale lines for 4 useful
+//    bytes each: on MI355X that kept the address unit waiting on the L1 cache
+//    and held the kernel to well under half of the HBM rate.
+//  * Weights stream through registers in a rolling window of P steps per
+//    wave; the steady-state loop issues unconditionally, so the compiler keeps
+//    the window in flight instead of waiting for every load.
+//  * S waves of a workgroup may split the K range of one 16-row tile (S = 4
+//    for matrices with few tiles, so that enough workgroups exist); their
+//    partial sums are added in a fixed order through LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemv_device.hpp"
+#include "q8gemv.h"
+
+namespace {
+
+using namespace q8g;
+
+constexpr int kBatchMax = Q8G_BATCH_MAX;  // MFMA M dimension
+constexpr int kTileRows = 16;             // weight rows per tile (MFMA N dimension)
+#ifndef Q8G_BATCH_WAVES
+#define Q8G_BATCH_WAVES 4
+#endif
+constexpr int kWavesB = Q8G_BATCH_WAVES;  // waves per workgroup (a multiple of 4)
+constexpr int kThreadsB = kWavesB * kWave;
+constexpr int kTileK = 1024;  // activation columns staged in LDS at a time
+constexpr int kStepK = 64;    // k per MFMA step (two Q8_0 blocks)
+constexpr int64_t kMaxElems = (int64_t)1 << 60;
+constexpr int64_t kMaxK = (int64_t)1 << 27;  // 16 rows x K bytes of a tile addressed with 32-bit offsets
+#ifndef Q8G_BATCH_SPLIT_TILES
+#define Q8G_BATCH_SPLIT_TILES 2048
+#endif
+#ifndef Q8G_BATCH_PIPE_SPLIT
+#define Q8G_BATCH_PIPE_SPLIT 4
+#endif
+#ifndef Q8G_BATCH_PIPE_WHOLE
+#define Q8G_BATCH_PIPE_WHOLE 8
+#endif
+#ifndef Q8G_BATCH_MIN_WAVES
+#define Q8G_BATCH_MIN_WAVES 1
+#endif
+constexpr int64_t kSplitTiles = Q8G_BATCH_SPLIT_TILES;  // up to this many 16-row tiles: K split over 4 waves
+constexpr int kPipeSplit = Q8G_BATCH_PIPE_SPLIT;        // steps in flight per wave, K split
+constexpr int kPipeWhole = Q8G_BATCH_PIPE_WHOLE;        // steps in flight per wave, whole-K tiles
+constexpr int kMinWavesPerSimd = Q8G_BATCH_MIN_WAVES;   // register budget: waves resident per SIMD
+
+// LDS: [16 zero bytes][activation scales: (kTileK/32) blocks x 16 vectors, one
+//      dword each][codes: 16 vectors x kTileK bytes, XOR-swizzled][weight
+//      scales: per wave, 16 rows x its blocks of the tile, one dword each].
+// The zero slot is what a lane reads for an operand group that must be zero
+// (another block's half of a step, a vector past B); it also keeps every
+// direct-load destination away from LDS offset 0.
+constexpr int kDxOff = 16;
+constexpr int kCodesOff = kDxOff + (kTileK / 32) * kBatchMax * 4;
+constexpr int kWscOff = kCodesOff + kBatchMax * kTileK;
+constexpr int kWscWave = kTileRows * (kTileK / 32) * 4;  // bytes per wave
+constexpr int kLdsBytes = kWscOff + kWavesB * kWscWave;
+static_assert(kTileK % kStepK == 0 && (kTileK / 16) % 16 == 0, "tile of whole steps and chunk groups");
+static_assert(kCodesOff % 16 == 0, "16-byte aligned code area");
+static_assert(kWavesB * kWave * 4 * 4 <= kBatchMax * kTileK, "partials fit in the code area");
+
+__device__ __forceinline__ v4i as_v4i(const int4 &v) { return v4i{v.x, v.y, v.z, v.w}; }
+
+// s_waitcnt with vmcnt <= n (n < 64), the other counters left alone
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// S: waves splitting the K range of one tile; P: weight steps in flight per wave.
+template <int S, int P>
+__global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(const int8_t *__restrict__ qw,
+                                                                            const uint16_t *__restrict__ dw,
+                                                                            const int8_t *__restrict__ qx,
+                                                                            const uint16_t *__restrict__ dx,
+                                                                            const float *residual, float *y,
+                                                                            int64_t N, int64_t K, int B)
+{
+    __shared__ __align__(16) uint8_t s_lds[kLdsBytes];
+    uint8_t *const s_codes = s_lds + kCodesOff;
+    const float *const s_dxf = reinterpret_cast<const float *>(s_lds + kDxOff);
+
+    constexpr int kTilesPerGroup = kWavesB / S;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int tile = wave / S, split = wave % S;
+    const int j = lane & 15;  // weight row in the tile / activation vector of the operand
+    const int q = lane >> 4;  // 16-byte k group of a step
+    const int64_t row0 = ((int64_t)blockIdx.x * kTilesPerGroup + tile) * kTileRows;  // wave-uniform
+    const int64_t row = row0 + j;
+    const bool row_ok = row < N;
+    const int64_t nb = K / 32;
+    // a wave-uniform base and a 32-bit lane offset in [0, 16) rows (rows of at
+    // most 2^27 bytes; larger K is refused on the host). Rows past N re-read
+    // row N-1; a tile wholly past N (the last workgroup's) re-reads it too.
+    const int64_t rbase = row0 < N ? row0 : N - 1;
+    const int jr = (int)((row_ok ? row : N - 1) - rbase);
+    const int8_t *wbase = qw + rbase * K;
+    const uint32_t woff = (uint32_t)jr * (uint32_t)K;
+
+    if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(s_lds) = make_uint4(0u, 0u, 0u, 0u);  // the zero slot
+
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t k0 = 0; k0 < K; k0 += kTileK) {
+        const int kt = (int)(K - k0 < kTileK ? K - k0 : kTileK);  // multiple of 32
+        const int nbt = kt / 32;
+        const int cpv = kt / 16;                   // 16-byte chunks per vector
+        const int rowc16 = (cpv + 15) & ~15;       // LDS chunks per vector (whole groups of 16)
+        const int steps = (kt + kStepK - 1) / kStepK;
+        const int s_begin = steps * split / S, s_end = steps * (split + 1) / S;
+
+        // 1. direct copies into LDS, requested first (one wave's loads complete
+        //    in issue order). Codes: LDS chunk position p -> vector p / rowc16,
+        //    chunk (p % rowc16) ^ vector; positions past the real chunks copy
+        //    chunk 0 of their vector and are never read.
+        const int code_pos = B * rowc16;
+        for (int p0 = wave * kWave; p0 < code_pos; p0 += kWavesB * kWave) {
+            const int p = p0 + lane;
+            const int b = p / rowc16, c = (p - b * rowc16) ^ (b & 15);
+            const int bb = b < B ? b : B - 1;
+            const int cc = c < cpv ? c : 0;
+            if (p < code_pos)
+                __builtin_amdgcn_global_load_lds(qx + (int64_t)bb * K + k0 + 16 * cc, s_codes + 16 * p0, 16, 0, 0);
+        }
+        //    Scales: LDS dword t -> block t / 16, vector t % 16 (vectors past B
+        //    copy vector B-1; their outputs are never stored).
+        const int dx_pos = nbt * kBatchMax;
+        for (int p0 = wave * kWave; p0 < dx_pos; p0 += kWavesB * kWave) {
+            const int t = p0 + lane;
+            const int blk = t / kBatchMax, b = t - blk * kBatchMax;
+            const int bb = b < B ? b : B - 1;
+            if (t < dx_pos)
+                __builtin_amdgcn_global_load_lds(dx + (int64_t)bb * nb + k0 / 32 + blk,
+                                                 s_lds + kDxOff + 4 * p0, 2, 0, 0);
+        }
+
+        //    Weight scales of this wave's rows and steps: LDS dword t -> row
+        //    t / nbw of the tile, block t % nbw of the wave's blocks (rows past
+        //    N read row N-1; a missing second block of the last step reads the
+        //    first, and its product is zero).
+        const int nbw = 2 * (s_end - s_begin);
+        const int64_t blk0 = k0 / 32 + 2 * s_begin;
+        uint8_t *const s_wsc = s_lds + kWscOff + wave * kWscWave;
+        for (int p0 = 0; p0 < kTileRows * nbw; p0 += kWave) {
+            const int t = p0 + lane;
+            const int r = t / nbw, bo = t - r * nbw;
+            const int64_t rr = row0 + r < N ? row0 + r : N - 1;
+            const int64_t bk = blk0 + bo < nb ? blk0 + bo : blk0;
+            if (t < kTileRows * nbw) __builtin_amdgcn_global_load_lds(dw + rr * nb + bk, s_wsc + 4 * p0, 2, 0, 0);
+        }
+
+        // 2. the first window of weights (one load per step). Steps past the
+        //    wave's share re-read its last step, so every issue is unconditional.
+        int4 wv[P];
+        auto issue = [&](int p, int st) {
+            const bool hi = st * kStepK + 32 < kt;  // the step's second block exists
+            wv[p] = load16_stream(wbase + (woff + ((q < 2 || hi) ? (uint32_t)(k0 + st * kStepK + 16 * q) : 0u)));
+        };
+        const int last = s_end > s_begin ? s_end - 1 : s_begin;
+#pragma unroll
+        for (int p = 0; p < P; ++p) issue(p, s_begin + p < s_end ? s_begin + p : last);
+
+        // 3. the copies are older than the P weight loads: wait for them only,
+        //    then a bare barrier (LDS needs no memory fence within the
+        //    workgroup; a full __syncthreads would also wait for the weights)
+        wait_vmcnt<P>();
+        __builtin_amdgcn_s_barrier();
+        //    the staged scale bits to f32, in place, once per tile
+        for (int t = threadIdx.x; t < dx_pos; t += kThreadsB) {
+            uint32_t *v = reinterpret_cast<uint32_t *>(s_lds + kDxOff) + t;
+            *v = __builtin_bit_cast(uint32_t, f16_bits_to_f32((uint16_t)*v));
+        }
+        __builtin_amdgcn_s_barrier();
+
+        auto consume = [&](int p, int st) {
+            const bool hi = st * kStepK + 32 < kt;
+            const v4i zero = {0, 0, 0, 0};
+            // operand groups 0-1 feed the first block's MFMA, 2-3 the second's;
+            // a lane whose group belongs to the other block (or to a vector
+            // past B, or to a missing second block) reads the zero slot
+            const int c = 4 * st + q;  // the lane's 16-byte chunk of vector j
+            const uint32_t at = kCodesOff + 16u * (uint32_t)(j * rowc16 + (c ^ j));
+            const bool lo_ok = j < B && q < 2, hi_ok = j < B && q >= 2 && hi;
+            const v4i a_lo = *reinterpret_cast<const v4i *>(s_lds + (lo_ok ? at : 0u));
+            const v4i a_hi = *reinterpret_cast<const v4i *>(s_lds + (hi_ok ? at : 0u));
+            const v4i w = as_v4i(wv[p]);
+            const v4i i0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo, w, zero, 0, 0, 0);
+            const v4i i1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi, w, zero, 0, 0, 0);
+            const int blk = 2 * st;  // within the tile
+            const float4 x0 = *reinterpret_cast<const float4 *>(s_dxf + blk * kBatchMax + 4 * q);
+            const float4 x1 = hi ? *reinterpret_cast<const float4 *>(s_dxf + (blk + 1) * kBatchMax + 4 * q)
+                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            const uint2 ws = *reinterpret_cast<const uint2 *>(s_wsc + 4 * (j * nbw + 2 * (st - s_begin)));
+            const float w0 = f16_bits_to_f32((uint16_t)ws.x), w1 = f16_bits_to_f32((uint16_t)ws.y);
+            acc[0] = __builtin_fmaf((float)i0[0], w0 * x0.x, acc[0]);
+            acc[1] = __builtin_fmaf((float)i0[1], w0 * x0.y, acc[1]);
+            acc[2] = __builtin_fmaf((float)i0[2], w0 * x0.z, acc[2]);
+            acc[3] = __builtin_fmaf((float)i0[3], w0 * x0.w, acc[3]);
+            acc[0] = __builtin_fmaf((float)i1[0], w1 * x1.x, acc[0]);
+            acc[1] = __builtin_fmaf((float)i1[1], w1 * x1.y, acc[1]);
+            acc[2] = __builtin_fmaf((float)i1[2], w1 * x1.z, acc[2]);
+            acc[3] = __builtin_fmaf((float)i1[3], w1 * x1.w, acc[3]);
+            // one step at a time: the empty asm makes this step's sums exist here,
+            // so the compiler cannot sink them to the end of the window and keep
+            // every MFMA result of the window live (registers, and so waves per
+            // SIMD, are what a memory-bound loop needs)
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+        };
+
+        // 4. steady state: a whole window is consumed while the next is requested
+        int s0 = s_begin;
+        for (; s0 + P < s_end; s0 += P) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                consume(p, s0 + p);
+                const int nx = s0 + P + p;
+                issue(p, nx < s_end ? nx : s_end - 1);
+            }
+        }
+        // the last window: consumed, nothing more requested
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (s0 + p < s_end) consume(p, s0 + p);
+        __syncthreads();  // the next tile's copies overwrite the staging area
+    }
+
+    // residuals of the four outputs this lane stores
+    float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (residual && row_ok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * q + r < B) res[r] = residual[(int64_t)(4 * q + r) * N + row];
+    }
+
+    if constexpr (S > 1) {
+        // partial sums of the S waves of a tile, added in split order
+        float *part = reinterpret_cast<float *>(s_codes);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[(wave * kWave + lane) * 4 + r] = acc[r];
+        __syncthreads();
+        if (split != 0) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float t = part[(wave * kWave + lane) * 4 + r];
+#pragma unroll
+            for (int k = 1; k < S; ++k) t += part[((wave + k) * kWave + lane) * 4 + r];
+            acc[r] = t;
+        }
+    }
+    if (!row_ok) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int b = 4 * q + r;
+        if (b < B) y[(int64_t)b * N + row] = residual ? acc[r] + res[r] : acc[r];
+    }
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
+{
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+template <int S, int P>
+hipError_t launch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx, const float *residual,
+                  float *y, int64_t N, int64_t K, int B, hipStream_t s)
+{
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    const int64_t groups = (tiles + kWavesB / S - 1) / (kWavesB / S);
+    void *args[] = {&qw, &dw, &qx, &dx, &residual, &y, &N, &K, &B};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&batch_kernel<S, P>), dim3((unsigned)groups),
+                           dim3(kThreadsB), args, 0, s);
+}
+
+}  // namespace
+
+extern "C" q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                                    const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream)
+{
+    if (N < 0 || K < 0 || B < 0 || B > kBatchMax || N > kMaxElems || K > kMaxElems) return Q8G_ERR_SHAPE;
+    if (K % 32 || K > kMaxK) return Q8G_ERR_SHAPE;
+    if (N > 0 && K > 0 && N > kMaxElems / K) return Q8G_ERR_SHAPE;
+    if ((N + kTileRows - 1) / kTileRows > (int64_t)INT32_MAX) return Q8G_ERR_SHAPE;
+    if (N == 0 || B == 0) return Q8G_OK;
+    if (!y || (K > 0 && (!qw || !dw || !qx || !dx))) return Q8G_ERR_NULL;
+    if (!aligned(qw, 16) || !aligned(qx, 16) || !aligned(dw, 2) || !aligned(dx, 2) || !aligned(y, 4) ||
+        (residual && !aligned(residual, 4)))
+        return Q8G_ERR_ALIGN;
+    const int64_t ybytes = B * N * 4;
+    if (overlap(y, ybytes, qw, N * K) || overlap(y, ybytes, dw, N * (K / 32) * 2) || overlap(y, ybytes, qx, B * K) ||
+        overlap(y, ybytes, dx, B * (K / 32) * 2))
+        return Q8G_ERR_OVERLAP;
+    // the residual may be y itself (each element is read, then written, by one lane)
+    if (residual && residual != y && overlap(y, ybytes, residual, ybytes)) return Q8G_ERR_OVERLAP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    const hipError_t e = tiles <= kSplitTiles ? launch<4, kPipeSplit>(qw, dw, qx, dx, residual, y, N, K, (int)B, s)
+                                              : launch<1, kPipeWhole>(qw, dw, qx, dx, residual, y, N, K, (int)B, s);
+    return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}

@@ -96,6 +96,24 @@ q8g_status bf16_gemv(const uint16_t *w, const uint16_t *x, const float *residual
 q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, float *y,
                     int64_t N, int64_t K, void *stream);
 
+/* Small-batch Q8_0 GEMV: B activation vectors share one pass over the weights.
+ * [P] Fast Decode sets the two ends: decode reads each weight once per token
+ * (memory-bound), prompt processing reuses each weight once per prompt token
+ * and belongs on the matrix units. For 1 <= B <= Q8G_BATCH_MAX, each weight
+ * byte read serves B outputs, and the block sums run on the matrix cores:
+ *   y[b][n] = sum_blk float(isum(n, b, blk)) * (f16(dw[n][blk]) * f16(dx[b][blk]))
+ *             (+ residual[b][n]),   isum(n, b, blk) = sum_{i<32} qw[n][32 blk+i] * qx[b][32 blk+i]
+ * i.e. q8_gemv once per vector b. qw int8 [N][K], dw uint16 [N][K/32] as for
+ * q8_gemv; qx int8 [B][K] and dx uint16 [B][K/32] row-major (B activations
+ * quantized by one q8_quantize_act call over B*K values); residual f32 [B][N]
+ * or NULL (may equal y); y f32 [B][N]. K % 32 == 0 and K <= 2^27; B == 0 or
+ * N == 0 enqueues nothing; B > Q8G_BATCH_MAX gives Q8G_ERR_SHAPE. The f32 accumulation order
+ * differs from q8_gemv's, so results agree with it within the tolerance of the
+ * f32 sum, not bit for bit. */
+#define Q8G_BATCH_MAX 16
+q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                         const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream);
+
 /* One matrix of a stacked projection. */
 typedef struct {
     const void *w;         /* Q8_0: int8 codes [n][K]; bf16 / f16: uint16 [n][K] */

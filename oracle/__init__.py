@@ -5,8 +5,8 @@ CPU-baseline leg may import this package; the product path never does. It
 shares no code with the HIP library. Arrays are numpy; results are f64.
 
 What it computes is stated, with its sources, at the top of oracle.c:
-the Q8_0 activation quantizer, the per-block int32 dot, the Q8_0 GEMV and the
-bf16 and f16 GEMVs of "Filling in the blanks: Inference using Phobos" (section Fast
+the Q8_0 activation quantizer, the per-block int32 dot, the Q8_0 GEMV (single
+vector and small batch) and the bf16 and f16 GEMVs of "Filling in the blanks: Inference using Phobos" (section Fast
 Decode) and "One level down: #002 the same compiler on a GPU" (sections
 Emitting for a GPU and The numerical contract).
 """
@@ -66,6 +66,8 @@ def _bind(lib):
     lib.orc_f16_gemv.restype = None
     lib.orc_f16_gemv_mt.argtypes = [_P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int]
     lib.orc_f16_gemv_mt.restype = ctypes.c_int
+    lib.orc_q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
+    lib.orc_q8_gemv_batch.restype = None
     return lib
 
 
@@ -146,6 +148,30 @@ class Oracle:
             self.lib.orc_q8_gemv(pw, pdw, pq, pdx, pr, n, k, y.ctypes.data, s.ctypes.data)
         return y, s
 
+    def q8_gemv_batch(self, qw, dw, qx, dx, residual=None, nthreads: int = 0):
+        """(y, S) as [B, N] f64 for B activation vectors qx [B, K], dx [B, K/32].
+        nthreads 0: the oracle's batch entry; otherwise the threaded GEMV once per vector."""
+        qw, pw = _c(qw, np.int8)
+        dw, pdw = _c(dw, np.uint16)
+        qx, pq = _c(qx, np.int8)
+        dx, pdx = _c(dx, np.uint16)
+        n, k = qw.shape
+        b = qx.shape[0]
+        assert k % 32 == 0 and dw.shape == (n, k // 32) and qx.shape == (b, k) and dx.shape == (b, k // 32)
+        pr = None
+        if residual is not None:
+            residual, pr = _c(residual, np.float32)
+            assert residual.shape == (b, n)
+        y = np.empty((b, n), np.float64)
+        s = np.empty((b, n), np.float64)
+        if nthreads:
+            for i in range(b):
+                yi, si = self.q8_gemv(qw, dw, qx[i], dx[i], None if residual is None else residual[i], nthreads)
+                y[i], s[i] = yi, si
+        else:
+            self.lib.orc_q8_gemv_batch(pw, pdw, pq, pdx, pr, n, k, b, y.ctypes.data, s.ctypes.data)
+        return y, s
+
     def f16_gemv(self, w, x, residual=None, nthreads: int = 0):
         return self._16bit_gemv("f16", w, x, residual, nthreads)
 
@@ -202,3 +228,7 @@ def bf16_gemv(w, x, residual=None, nthreads: int = 0):
 
 def f16_gemv(w, x, residual=None, nthreads: int = 0):
     return get().f16_gemv(w, x, residual, nthreads)
+
+
+def q8_gemv_batch(qw, dw, qx, dx, residual=None, nthreads: int = 0):
+    return get().q8_gemv_batch(qw, dw, qx, dx, residual, nthreads)

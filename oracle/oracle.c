@@ -229,6 +229,19 @@ void orc_f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual, i
     }
 }
 
+/* ---- small-batch Q8_0 GEMV: B activation vectors against one weight matrix.
+ * By definition this is the Q8_0 GEMV once per vector b ([P] Fast Decode: the
+ * per-token product; a batch only lets one weight pass serve B tokens):
+ * qx int8 [B][K], dx [B][K/32], residual f32 [B][N] or NULL, y and S [B][N]. */
+void orc_q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                       const float *residual, int64_t N, int64_t K, int64_t B, double *y, double *S)
+{
+    int64_t nb = K / ORC_QBLOCK;
+    for (int64_t b = 0; b < B; ++b)
+        orc_q8_gemv(qw, dw, qx + b * K, dx + b * nb, residual ? residual + b * N : NULL, N, K, y + b * N,
+                    S + b * N);
+}
+
 /* ---- row-partitioned threading (same per-row arithmetic, so identical
  * results to the single-threaded calls) ------------------------------------ */
 typedef struct {

@@ -390,6 +390,63 @@ def pin_bf16_residual(o):
     assert np.array_equal(y, r.astype(np.float64))
 
 
+# ----------------------------------------------------------------------------- small-batch Q8_0 GEMV
+
+
+def _q8_batch_case(j, n, k, nb, resid=True):
+    g = rng(j)
+    qw, dw = synth.q8_weights(g, n, k)
+    x = np.stack([synth.activation_f32(g, k) for _ in range(nb)])
+    r = np.stack([synth.residual_f32(g, n) for _ in range(nb)]) if resid else None
+    return qw, dw, x, r
+
+
+def pin_q8_batch_unit_scales_exact(o):
+    """All scales 1.0: y[b] = qx[b] . qw^T in integers, an exact int64 matmul."""
+    g = rng(30)
+    n, k, nb = 23, 160, 6
+    qw = g.integers(-128, 128, (n, k)).astype(np.int8)
+    qx = g.integers(-127, 128, (nb, k)).astype(np.int8)
+    one = np.uint16(0x3C00)
+    dw = np.full((n, k // QB), one, np.uint16)
+    dx = np.full((nb, k // QB), one, np.uint16)
+    y, S = o.q8_gemv_batch(qw, dw, qx, dx)
+    W, X = qw.astype(np.int64), qx.astype(np.int64)
+    assert np.array_equal(y, (X @ W.T).astype(np.float64))
+    assert np.array_equal(S, (np.abs(X) @ np.abs(W).T).astype(np.float64))
+
+
+def pin_q8_batch_vs_dense_dequant(o):
+    for j, (n, k, nb) in enumerate(((40, 1024, 16), (9, 96, 3), (17, 2048, 5))):
+        qw, dw, x, r = _q8_batch_case(31 + j, n, k, nb, resid=(j != 1))
+        q = [np_quantize(v) for v in x]
+        qx = np.stack([a for a, _ in q])
+        dx = np.stack([d for _, d in q])
+        y, S = o.q8_gemv_batch(qw, dw, qx, dx, r)
+        W = dequant_rows(qw, dw)
+        X = np.stack([dequant_rows(qx[i][None, :], dx[i][None, :])[0] for i in range(nb)])
+        R = 0.0 if r is None else r.astype(np.float64)
+        close_to(y, X @ W.T + R, S, (k // QB) * 2.0**-52)
+        close_to(S, np.abs(X) @ np.abs(W).T + np.abs(R), S, (k // QB) * 2.0**-52)
+
+
+def pin_q8_batch_rows_are_single_gemvs(o):
+    """Vector b of a batch gives what the single-vector GEMV gives for qx[b]
+    (both pinned independently above), with vectors kept apart."""
+    qw, dw, x, r = _q8_batch_case(35, 21, 128, 4)
+    q = [np_quantize(v) for v in x]
+    qx = np.stack([a for a, _ in q])
+    dx = np.stack([d for _, d in q])
+    dx[2] = np.uint16(0x4000)  # a distinct scale plane per vector
+    y, S = o.q8_gemv_batch(qw, dw, qx, dx, r)
+    for b in range(4):
+        yb, Sb = o.q8_gemv(qw, dw, qx[b], dx[b], r[b])
+        assert np.array_equal(y[b], yb) and np.array_equal(S[b], Sb)
+    for t in (2, 5):
+        yt, St = o.q8_gemv_batch(qw, dw, qx, dx, r, nthreads=t)
+        assert np.array_equal(yt, y) and np.array_equal(St, S)
+
+
 # ----------------------------------------------------------------------------- f16 GEMV
 
 

@@ -41,6 +41,7 @@ def lib():
     L.q8_gemv.argtypes = [P, P, P, P, P, P, I64, I64, P]
     L.bf16_gemv.argtypes = [P, P, P, P, I64, I64, P]
     L.f16_gemv.argtypes = [P, P, P, P, I64, I64, P]
+    L.q8_gemv_batch.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
     L.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(Part), ctypes.c_int, P, P, I64, P]
     L.q8g_status_str.argtypes = [ctypes.c_int]
     L.q8g_status_str.restype = ctypes.c_char_p
@@ -51,7 +52,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    for expected in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "f16_gemv", "gemv_stacked", "q8g_status_str",
+    for expected in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
+                     "q8g_status_str",
                      "q8g_probe_read", "q8g_flush"):
         assert expected in names
     for n in names:
@@ -103,6 +105,31 @@ def test_q8_gemv_validation(lib):
     assert g(W, DW, QX, DX, None, QX, 8, 64, None) == ERR_OVERLAP
     assert g(W, DW, QX, DX, None, DX, 8, 64, None) == ERR_OVERLAP
     assert g(W, DW, QX, DX, Y + 4, Y, 8, 64, None) == ERR_OVERLAP  # partial residual alias
+
+
+def test_q8_gemv_batch_validation(lib):
+    g = lib.q8_gemv_batch
+    assert g(W, DW, QX, DX, None, Y, 8, 48, 2, None) == ERR_SHAPE  # K % 32
+    assert g(W, DW, QX, DX, None, Y, 8, 64, 17, None) == ERR_SHAPE  # B > 16
+    assert g(W, DW, QX, DX, None, Y, 8, 64, -1, None) == ERR_SHAPE
+    assert g(W, DW, QX, DX, None, Y, -1, 64, 2, None) == ERR_SHAPE
+    assert g(W, DW, QX, DX, None, Y, 1 << 40, 1 << 30, 2, None) == ERR_SHAPE  # N*K overflow guard
+    assert g(None, None, None, None, None, None, 0, 64, 4, None) == OK  # N == 0
+    assert g(None, None, None, None, None, None, 8, 64, 0, None) == OK  # B == 0
+    assert g(None, DW, QX, DX, None, Y, 8, 64, 2, None) == ERR_NULL
+    assert g(W, DW, QX, None, None, Y, 8, 64, 2, None) == ERR_NULL
+    assert g(W, DW, QX, DX, None, None, 8, 64, 2, None) == ERR_NULL
+    assert g(W + 8, DW, QX, DX, None, Y, 8, 64, 2, None) == ERR_ALIGN
+    assert g(W, DW, QX + 8, DX, None, Y, 8, 64, 2, None) == ERR_ALIGN
+    assert g(W, DW + 1, QX, DX, None, Y, 8, 64, 2, None) == ERR_ALIGN
+    assert g(W, DW, QX, DX, R + 2, Y, 8, 64, 2, None) == ERR_ALIGN
+    assert g(W, DW, QX, DX, None, Y + 2, 8, 64, 2, None) == ERR_ALIGN
+    # y [B][N] against every input, and a residual that overlaps y without being y
+    assert g(W, DW, QX, DX, None, W + 64, 8, 64, 2, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, None, QX + 64, 8, 64, 2, None) == ERR_OVERLAP  # inside vector 1's codes
+    assert g(W, DW, QX, DX, None, DX, 8, 64, 2, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, None, DW, 8, 64, 2, None) == ERR_OVERLAP
+    assert g(W, DW, QX, DX, Y + 4, Y, 8, 64, 2, None) == ERR_OVERLAP
 
 
 @pytest.mark.parametrize("name", ["bf16_gemv", "f16_gemv"])

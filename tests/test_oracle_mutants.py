@@ -45,8 +45,11 @@ MUTANTS = [
     ("bf16_reversed_row", "orc_bf16_value(w[n * K + k])", "orc_bf16_value(w[n * K + (K - 1 - k)])"),
     ("bf16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- f16",
      "mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- f16"),
-    ("f16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row",
-     "mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- row"),
+    ("f16_dropped_residual", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- small-batch",
+     "mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- small-batch"),
+    ("batch_shared_dx", "qx + b * K, dx + b * nb,", "qx + b * K, dx,"),
+    ("batch_shared_residual", "residual ? residual + b * N : NULL", "residual"),
+    ("batch_shared_codes", "orc_q8_gemv(qw, dw, qx + b * K,", "orc_q8_gemv(qw, dw, qx,"),
     ("f16_reversed_row", "orc_f16_value(w[n * K + k])", "orc_f16_value(w[n * K + (K - 1 - k)])"),
     ("f16_decoded_as_bf16", "double p = orc_f16_value(w[n * K + k]) * orc_f16_value(x[k]);",
      "double p = orc_bf16_value(w[n * K + k]) * orc_f16_value(x[k]);"),
