@@ -10,12 +10,17 @@ layers of [QKV 1024->4096 (stacked 2048/1024/1024), out 2048->1024, gate+up 1024
 1024->151936. 97 activation quantizes + 97 GEMV launches per token, 609,613,952
 algorithmic bytes per token (weights, scales, activations in and out, residual).
 
+q8-stack-0.8b-b16: the same stack for 16 decode streams at once (small-batch GEMV on the
+matrix cores): per projection one q8_quantize_act over the 16 inputs and one
+q8_gemv_batch launch; a step serves 16 tokens.
+
 Other workloads (per-call figures; a step is one call):
   q8-gateup-7168x1024   Q8_0 7168x1024, rotating over >= 1 GiB of distinct copies
   bf16-gateup-7168x1024 bf16 7168x1024 as two stacked 3584-row halves, rotating copies
   f16-gateup-7168x1024  the same with IEEE binary16 weights and activation
   bf16-gateup-18432x2560-x36  bf16 18432x2560 over 36 independent matrices, round-robin
   q8-head-131072x5120   Q8_0 131072x5120, cold cache (1 GiB flush before every call)
+  q8-head-151936x1024-b16  q8_gemv_batch over 16 vectors on the 0.8B output head, rotating copies
 
 Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
 then K timed steps between two synchronizations, measured with HIP events on the
@@ -36,8 +41,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
-WORKLOADS = ["q8-stack-0.8b", "q8-gateup-7168x1024", "bf16-gateup-7168x1024", "f16-gateup-7168x1024",
-             "bf16-gateup-18432x2560-x36", "q8-head-131072x5120"]
+WORKLOADS = ["q8-stack-0.8b", "q8-stack-0.8b-b16", "q8-gateup-7168x1024", "q8-head-151936x1024-b16",
+             "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120"]
+BATCH = 16  # decode streams of the -b16 workloads
 
 
 def log(*a):
@@ -89,6 +95,53 @@ def probe_gbps(q8, torch, gib=4, reps=10):
     del buf
     times.sort()
     return (gib << 30) / times[len(times) // 2] / 1e9
+
+
+def graph_seconds(torch, fn, reps, warmup):
+    """Capture fn (a sequence of launches) into a HIP graph; mean seconds per replay."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def cold_seconds(torch, q8, fn, flush_buf, reps=10):
+    """A few launches (too few to amortize the events): one graph replay after a
+    1 GiB cache-evicting write, bracketed by HIP events; median of reps."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    ts = []
+    for r in range(reps):
+        q8.flush(flush_buf, r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return sorted(ts)[len(ts) // 2]
 
 
 def cpu_threads():
@@ -151,51 +204,12 @@ def run_stack(args, torch, q8, np):
     log(f"[bench] pure-read probe: {probe:.0f} GB/s")
 
     def time_graph(fn, reps):
-        """Capture fn (a sequence of launches) into a HIP graph; mean seconds per replay."""
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            fn()
-        for _ in range(max(1, args.warmup)):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps
+        return graph_seconds(torch, fn, reps, args.warmup)
 
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
     def time_cold(fn, reps=10):
-        """A few launches (too few to amortize the events): one graph replay after a
-        1 GiB cache-evicting write, bracketed by HIP events; median of reps."""
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            fn()
-        ts = []
-        for r in range(reps):
-            q8.flush(flush_buf, r)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e-3)
-        return sorted(ts)[len(ts) // 2]
+        return cold_seconds(torch, q8, fn, flush_buf, reps)
 
     # (a) per projection q8_quantize_act + gemv_stacked, the step replayed as a HIP graph
     t_graph = time_graph(lambda: stack.step(fused=False), args.steps)
@@ -317,14 +331,18 @@ def run_stack(args, torch, q8, np):
     return out
 
 
-def cpu_baseline_single(dt, first, n, k, per, orc, np, min_seconds=10.0):
+def cpu_baseline_single(dt, first, n, k, per, orc, np, min_seconds=10.0, nb=1):
     """The oracle on the host cores over whole copies of the first matrix (all rows),
     repeated until about min_seconds have been timed; GB/s over the same algorithmic bytes."""
     nth = cpu_threads()
     calls = 0
     t0 = time.perf_counter()
     while True:
-        if dt == "q8":
+        if dt == "q8" and nb > 1:
+            qw, dw, x = first
+            q = [orc.quantize_act(v) for v in x]
+            orc.q8_gemv_batch(qw, dw, np.stack([a for a, _ in q]), np.stack([d for _, d in q]), nthreads=nth)
+        elif dt == "q8":
             qw, dw, x = first
             qx, dx = orc.quantize_act(x)
             orc.q8_gemv(qw, dw, qx, dx, nthreads=nth)
@@ -405,6 +423,110 @@ def cpu_baseline_stack(ops, host, orc, min_seconds=10.0):
             "tok_per_s": round(tokens / dt, 2), "cpu": cpu_model()}
 
 
+# ----------------------------------------------------------------------------- 16 streams
+
+
+def run_batch_stack(args, torch, q8, np):
+    import oracle
+    import synth
+    from block_quantized_weight_q8_amd.stack import Q8BatchStack, Q8DecodeStack
+
+    nb = BATCH
+    ops = synth.q8_stack_08b()
+    t0 = time.time()
+    host = synth.q8_stack_inputs(ops)  # the weights (and each op's single-stream input, unused here)
+    batch = synth.q8_batch_inputs(ops, nb)
+    log(f"[bench] generated {len(ops)} projections and {nb} streams of inputs in {time.time() - t0:.1f}s")
+    stack = Q8DecodeStack(ops, host)
+    bs = Q8BatchStack(stack, batch)
+    torch.cuda.synchronize()
+    bytes_gemv = [synth.q8_batch_gemv_bytes(op.n, op.k, nb, op.residual) for op in ops]
+    bytes_quant = [nb * synth.q8_quantize_bytes(op.k) for op in ops]
+    step_bytes = sum(bytes_gemv) + sum(bytes_quant)
+
+    # parity gate: every stream's codes bit-exact, sampled rows of every projection
+    orc = oracle.get()
+    bs.step()
+    torch.cuda.synchronize()
+    g = np.random.default_rng(12345)
+    worst = 0.0
+    for i, (op, h, hb) in enumerate(zip(ops, host, batch)):
+        b = bs.bufs[i]
+        qx = b["qx"].cpu().numpy().reshape(nb, op.k)
+        dx = b["dx"].cpu().view(torch.int16).numpy().view(np.uint16).reshape(nb, op.k // 32)
+        for v in range(nb):
+            rq, rd = orc.quantize_act(hb["x"][v])
+            if not (np.array_equal(qx[v], rq) and np.array_equal(dx[v], rd)):
+                raise SystemExit(f"parity: quantized input {v} of {op.name} differs from the oracle")
+        rows = np.unique(np.concatenate([[0, op.n - 1], g.integers(0, op.n, 8 if op.n < 100000 else 64)]))
+        yr, S = orc.q8_gemv_batch(h["qw"][rows], h["dw"][rows], qx, dx, hb["r"][:, rows] if op.residual else None)
+        rel = np.abs(b["y"].cpu().numpy()[:, rows].astype(np.float64) - yr) / S
+        worst = max(worst, float(rel.max()))
+        if not np.all(rel <= 1e-5):
+            raise SystemExit(f"parity: {op.name} rows off by {rel.max():.2e} * S")
+    log(f"[bench] parity on sampled rows of all {len(ops)} projections x {nb} streams: worst |err|/S = {worst:.2e}")
+    probe = probe_gbps(q8, torch)
+    log(f"[bench] pure-read probe: {probe:.0f} GB/s")
+
+    t_step = graph_seconds(torch, bs.step, args.steps, args.warmup)
+    log(f"[bench] {nb} streams, quantize + q8_gemv_batch per projection (194 launches), graph replay: "
+        f"{t_step * 1e6:.1f} us/step, {nb / t_step:.0f} tok/s")
+
+    # per launch group (the library's configuration for each shape)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    groups = {}
+    for i, op in enumerate(ops):
+        groups.setdefault(q8.batch_config(op.n), []).append(i)
+    per = {}
+    for (ks, sf), idx in groups.items():
+        name = f"batch_kernel<{ks}, {sf}>"
+        fn = (lambda idx=idx: [bs.launch_gemv(i) for i in idx])
+        t = (graph_seconds(torch, fn, max(5, args.steps // 2), args.warmup) if len(idx) >= 8
+             else cold_seconds(torch, q8, fn, flush_buf)) / len(idx)
+        per[name] = [len(idx), t, sum(bytes_gemv[i] for i in idx) / len(idx)]
+    for name, (c, t, nbytes) in sorted(per.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        log(f"[bench] {name}: {c} launches/step, {t * 1e6:.2f} us each, {nbytes / t / 1e9:.0f} GB/s")
+    dname, (dc, dt_, db) = max(per.items(), key=lambda kv: kv[1][0] * kv[1][1])
+    roofline = {"bound": "hbm", "kernel": dname, "achieved": round(db / dt_ / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(db / dt_ / 1e9 / HBM_PEAK_GBPS, 4),
+                "avg_launch_us": round(dt_ * 1e6, 3), "bytes_per_launch": round(db),
+                "launches_per_step": dc, "traffic": traffic_for(dname)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nth = cpu_threads()
+        nbytes, steps = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            for op, h, hb in zip(ops, host, batch):
+                q = [orc.quantize_act(v) for v in hb["x"]]
+                orc.q8_gemv_batch(h["qw"], h["dw"], np.stack([a for a, _ in q]), np.stack([d for _, d in q]),
+                                  hb["r"], nthreads=nth)
+            nbytes += step_bytes
+            steps += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt = time.perf_counter() - t0
+        log(f"[bench] oracle on {nth} host threads: {nbytes / dt / 1e9:.2f} GB/s, {steps} steps in {dt:.1f}s")
+        cpu = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+               "sample": f"{steps} whole steps of {nb} streams through the 0.8B-shaped stack, {nbytes} "
+                         f"algorithmic bytes in {dt:.1f} s", "tok_per_s": round(steps * nb / dt, 2), "cpu": cpu_model()}
+
+    value = step_bytes / t_step / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "q8-stack-0.8b-b16", "streams": nb, "layers": 24, "hidden": 1024, "vocab": 151936,
+                   "projections_per_step": len(ops), "launches_per_step": 2 * len(ops), "bytes_per_step": step_bytes,
+                   "mode": "hipGraph, q8_quantize_act over 16 inputs + q8_gemv_batch per projection",
+                   "accumulate": "int32 per block (matrix cores), f32"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2), "tok_per_s": round(nb / t_step, 1),
+        "probe_GBps": round(probe, 1), "pct_of_probe": round(100 * value / probe, 2),
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+
+
 # ----------------------------------------------------------------------------- per-call workloads
 
 
@@ -415,7 +537,11 @@ def run_single(args, torch, q8, np):
     orc = oracle.get()
     wl = args.workload
     cold = wl == "q8-head-131072x5120"
-    if wl == "q8-gateup-7168x1024":
+    nb = BATCH if wl.endswith("-b16") else 1
+    if wl == "q8-head-151936x1024-b16":
+        n, k, dt, tag = 151936, 1024, "q8", synth.TAG_Q8_HEAD
+        per = synth.q8_batch_gemv_bytes(n, k, nb)
+    elif wl == "q8-gateup-7168x1024":
         n, k, dt, tag = 7168, 1024, "q8", synth.TAG_Q8_GATEUP
         per = synth.q8_gemv_bytes(n, k)
     elif wl == "bf16-gateup-7168x1024":
@@ -449,7 +575,7 @@ def run_single(args, torch, q8, np):
             continue
         if dt == "q8":
             qw, dw = synth.q8_weights(gr, n, k)
-            x = synth.activation_f32(gr, k)
+            x = synth.activation_f32(gr, k) if nb == 1 else np.stack([synth.activation_f32(gr, k) for _ in range(nb)])
             m = {"w": torch.from_numpy(qw).cuda(),
                  "dw": torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16),
                  "x": torch.from_numpy(x).cuda()}
@@ -469,10 +595,15 @@ def run_single(args, torch, q8, np):
     log(f"[bench] {copies} matrices generated and uploaded in {time.time() - t0:.1f}s")
     if dt == "q8":
         for m in mats:
-            m["qx"], m["dx"] = q8.q8_quantize_act(m["x"])
+            m["qx"], m["dx"] = q8.q8_quantize_act(m["x"].reshape(-1))
+            if nb > 1:
+                m["qx"], m["dx"] = m["qx"].view(nb, k), m["dx"].view(nb, k // 32)
+                m["y"] = torch.empty((nb, n), dtype=torch.float32, device="cuda")
 
     def call(m):
-        if dt == "q8":
+        if dt == "q8" and nb > 1:
+            q8.q8_gemv_batch(m["w"], m["dw"], m["qx"], m["dx"], y=m["y"])
+        elif dt == "q8":
             q8.q8_gemv(m["w"], m["dw"], m["qx"], m["dx"], y=m["y"])
         else:
             h = n // 2
@@ -481,14 +612,19 @@ def run_single(args, torch, q8, np):
     call(mats[0])
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(7).integers(0, n, 512)]))
-    if dt == "q8":
+    if dt == "q8" and nb > 1:
+        qw, dw, x = first
+        q = [orc.quantize_act(v) for v in x]
+        yr, S = orc.q8_gemv_batch(qw[rows], dw[rows], np.stack([a for a, _ in q]), np.stack([d for _, d in q]))
+    elif dt == "q8":
         qw, dw, x = first
         rq, rd = orc.quantize_act(x)
         yr, S = orc.q8_gemv(qw[rows], dw[rows], rq, rd)
     else:
         w, x = first
         yr, S = (orc.f16_gemv if dt == "f16" else orc.bf16_gemv)(w[rows], x)
-    rel = np.abs(mats[0]["y"].cpu().numpy()[rows].astype(np.float64) - yr) / S
+    yg = mats[0]["y"].cpu().numpy()
+    rel = np.abs((yg[:, rows] if nb > 1 else yg[rows]).astype(np.float64) - yr) / S
     if not np.all(rel <= 1e-5):
         raise SystemExit(f"parity: sampled rows off by {rel.max():.2e} * S")
     log(f"[bench] parity on {len(rows)} sampled rows: worst |err|/S = {rel.max():.2e}")
@@ -537,21 +673,27 @@ def run_single(args, torch, q8, np):
         torch.cuda.synchronize()
         calls = reps * copies
         t = a.elapsed_time(b) * 1e-3 / calls
-    cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np, nb=nb)
     gbps = per / t / 1e9
-    r, w_ = q8.gemv_config({"q8": q8.Q8G_Q8_0, "bf16": q8.Q8G_BF16, "f16": q8.Q8G_F16}[dt], n, k)
-    kname = f"{dt if dt != 'q8' else 'q8'}_gemv[rows_per_wave={r},waves={w_}]"
+    if nb > 1:
+        ks, sf = q8.batch_config(n)
+        kname = f"batch_kernel<{ks}, {sf}>"
+    else:
+        r, w_ = q8.gemv_config({"q8": q8.Q8G_Q8_0, "bf16": q8.Q8G_BF16, "f16": q8.Q8G_F16}[dt], n, k)
+        kname = f"{dt}_gemv[rows_per_wave={r},waves={w_}]"
     stack_bytes = 609613952 if dt == "q8" else 1143991808
     return {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": calls,
         "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": {"q8": "int8", "bf16": "bf16", "f16": "f16"}[dt], "data": "synthetic",
-        "config": {"workload": wl, "n": n, "k": k, "copies": copies, "cold_cache": cold, "bytes_per_call": per,
-                   "call": "q8_gemv" if dt == "q8" else "gemv_stacked, two halves",
+        "config": {"workload": wl, "n": n, "k": k, "vectors": nb, "copies": copies, "cold_cache": cold,
+                   "bytes_per_call": per,
+                   "call": ("q8_gemv_batch" if nb > 1 else "q8_gemv") if dt == "q8" else "gemv_stacked, two halves",
                    "timing": "per call after a 1 GiB flush" if cold else "HIP graph over one pass of the copies"},
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
         "pct_of_probe": round(100 * gbps / probe, 2),
-        "equiv_tok_per_s": round(gbps * 1e9 / stack_bytes, 1),
+        "equiv_tok_per_s": round(gbps * 1e9 / stack_bytes, 1) if nb == 1 else None,
+        "vectors_per_s": round(nb / t, 1),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 3),
                      "bytes_per_launch": per, "traffic": traffic_for(kname)},
@@ -612,6 +754,8 @@ def main():
         return
     if args.workload == "q8-stack-0.8b":
         out = run_stack(args, torch, q8, np)
+    elif args.workload == "q8-stack-0.8b-b16":
+        out = run_batch_stack(args, torch, q8, np)
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)

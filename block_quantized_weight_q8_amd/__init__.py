@@ -92,6 +92,7 @@ def load_library(path: str = LIB_PATH):
     lib.bf16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
     lib.f16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
     lib.q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+    lib.q8g_batch_config.argtypes = [_I64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
@@ -100,8 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_decode_stack.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
     lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
                                     ctypes.POINTER(ctypes.c_int)]
-    for fn in ("q8_quantize_act", "q8_gemv", "bf16_gemv", "f16_gemv", "gemv_stacked", "q8g_probe_read", "q8g_flush",
-               "q8g_gemv_config", "q8_decode_stack"):
+    for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
+               "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -189,6 +190,13 @@ def q8_gemv_batch(qw, dw, qx, dx, y=None, residual=None, stream=None):
         _ptr(y, "y", _F32, (b, n)), n, k, b, _stream(stream))
     _check("q8_gemv_batch", st)
     return y
+
+
+def batch_config(n):
+    """(k_split, steps_in_flight) that q8_gemv_batch uses for n rows."""
+    ks, sf = ctypes.c_int(), ctypes.c_int()
+    _check("q8g_batch_config", load_library().q8g_batch_config(n, ctypes.byref(ks), ctypes.byref(sf)))
+    return ks.value, sf.value
 
 
 def q8_gemv_f32(qw, dw, x, y=None, residual=None, stream=None):

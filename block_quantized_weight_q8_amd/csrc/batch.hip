@@ -22,7 +22,7 @@
 //    a lane applies one weight scale and four activation scales per block,
 //    as float(isum) * (dw * dx) accumulated in f32 (the product of two
 //    binary16 values is exact in f32, and so is float(isum)).
-//  * The activation codes and scales of a tile of kTileK columns are copied
+//  * The activation codes and scales of a tile of TK columns are copied
 //    into LDS with direct global-to-LDS loads (gfx950 global_load_lds): no
 //    registers hold them in flight and no wave waits on them before its
 //    weight stream is requested. Each lane picks its own source address, so
@@ -38,9 +38,9 @@
 //  * Weights stream through registers in a rolling window of P steps per
 //    wave; the steady-state loop issues unconditionally, so the compiler keeps
 //    the window in flight instead of waiting for every load.
-//  * S waves of a workgroup may split the K range of one 16-row tile (S = 4
-//    for matrices with few tiles, so that enough workgroups exist); their
-//    partial sums are added in a fixed order through LDS.
+//  * S waves of a workgroup may split the K range of one 16-row tile (16 or 4
+//    for matrices with few tiles, so that enough waves exist); their partial
+//    sums are added in a fixed order through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,46 +53,49 @@ using namespace q8g;
 
 constexpr int kBatchMax = Q8G_BATCH_MAX;  // MFMA M dimension
 constexpr int kTileRows = 16;             // weight rows per tile (MFMA N dimension)
-#ifndef Q8G_BATCH_WAVES
-#define Q8G_BATCH_WAVES 4
-#endif
-constexpr int kWavesB = Q8G_BATCH_WAVES;  // waves per workgroup (a multiple of 4)
-constexpr int kThreadsB = kWavesB * kWave;
-constexpr int kTileK = 1024;  // activation columns staged in LDS at a time
-constexpr int kStepK = 64;    // k per MFMA step (two Q8_0 blocks)
+constexpr int kStepK = 64;                // k per MFMA step (two Q8_0 blocks)
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
 constexpr int64_t kMaxK = (int64_t)1 << 27;  // 16 rows x K bytes of a tile addressed with 32-bit offsets
-#ifndef Q8G_BATCH_SPLIT_TILES
-#define Q8G_BATCH_SPLIT_TILES 2048
-#endif
-#ifndef Q8G_BATCH_PIPE_SPLIT
-#define Q8G_BATCH_PIPE_SPLIT 4
-#endif
-#ifndef Q8G_BATCH_PIPE_WHOLE
-#define Q8G_BATCH_PIPE_WHOLE 8
-#endif
-#ifndef Q8G_BATCH_MIN_WAVES
-#define Q8G_BATCH_MIN_WAVES 1
-#endif
-constexpr int64_t kSplitTiles = Q8G_BATCH_SPLIT_TILES;  // up to this many 16-row tiles: K split over 4 waves
-constexpr int kPipeSplit = Q8G_BATCH_PIPE_SPLIT;        // steps in flight per wave, K split
-constexpr int kPipeWhole = Q8G_BATCH_PIPE_WHOLE;        // steps in flight per wave, whole-K tiles
-constexpr int kMinWavesPerSimd = Q8G_BATCH_MIN_WAVES;   // register budget: waves resident per SIMD
+// 16-row tile counts that select the launch shape (MI355X has 256 compute units)
+constexpr int64_t kWideSplitTiles = 256;  // up to this many: 16 waves per tile, one workgroup per unit
+constexpr int64_t kSplitTiles = 2048;     // up to this many: 4 waves per tile
 
-// LDS: [16 zero bytes][activation scales: (kTileK/32) blocks x 16 vectors, one
-//      dword each][codes: 16 vectors x kTileK bytes, XOR-swizzled][weight
-//      scales: per wave, 16 rows x its blocks of the tile, one dword each].
-// The zero slot is what a lane reads for an operand group that must be zero
-// (another block's half of a step, a vector past B); it also keeps every
-// direct-load destination away from LDS offset 0.
-constexpr int kDxOff = 16;
-constexpr int kCodesOff = kDxOff + (kTileK / 32) * kBatchMax * 4;
-constexpr int kWscOff = kCodesOff + kBatchMax * kTileK;
-constexpr int kWscWave = kTileRows * (kTileK / 32) * 4;  // bytes per wave
-constexpr int kLdsBytes = kWscOff + kWavesB * kWscWave;
-static_assert(kTileK % kStepK == 0 && (kTileK / 16) % 16 == 0, "tile of whole steps and chunk groups");
-static_assert(kCodesOff % 16 == 0, "16-byte aligned code area");
-static_assert(kWavesB * kWave * 4 * 4 <= kBatchMax * kTileK, "partials fit in the code area");
+// Launch shape: W waves per workgroup, S of them splitting the K range of one
+// 16-row tile (W / S tiles per workgroup), P weight steps in flight per wave,
+// TK activation columns staged in LDS at a time.
+//
+// LDS: [16 zero bytes][activation scales: TK/32 blocks x 16 vectors, one dword
+//      each][codes: 16 vectors x TK bytes, XOR-swizzled][weight scales: per
+//      tile, the S split waves' regions of 16 rows x their blocks, one dword
+//      each]. The zero slot is what a lane reads for an operand group that must
+//      be zero (another block's half of a step, a vector past B); it also keeps
+//      every direct-load destination away from LDS offset 0.
+template <int W_, int S_, int P_, int TK_>
+struct Shape {
+    static constexpr int W = W_, S = S_, P = P_, TK = TK_;
+    static constexpr int kThreads = W * kWave;
+    static constexpr int kTiles = W / S;
+    static constexpr int kDxOff = 16;
+    static constexpr int kCodesOff = kDxOff + (TK / 32) * kBatchMax * 4;
+    static constexpr int kWscOff = kCodesOff + kBatchMax * TK;
+    static constexpr int kWscTile = kTileRows * (TK / 32) * 4;
+    static constexpr int kLds = kWscOff + kTiles * kWscTile;
+    static_assert(W % S == 0 && W >= 1 && W <= 16, "whole tiles per workgroup");
+    static_assert(TK % kStepK == 0 && (TK / 16) % 16 == 0, "tile of whole steps and chunk groups");
+    static_assert(kCodesOff % 16 == 0, "16-byte aligned code area");
+    static_assert(kThreads * 4 * 4 <= kBatchMax * TK, "partials fit in the code area");
+    static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+};
+// Matrices with few 16-row tiles (the decode stack's narrow projections): 16
+// waves split each tile's K range, so that the launch spreads over enough
+// compute units, and a 4096-column staging tile covers K <= 4096 in one pass.
+using WideSplitShape = Shape<16, 16, 2, 4096>;
+// A few hundred to a few thousand tiles: 4 waves per tile, small workgroups so
+// that four fit on a compute unit and the launch runs in one round.
+using SplitShape = Shape<4, 4, 4, 1024>;
+// Many tiles (output heads): each wave streams whole rows of K with 8 steps in
+// flight; small staging tiles keep four workgroups per compute unit.
+using WholeShape = Shape<4, 1, 8, 1024>;
 
 __device__ __forceinline__ v4i as_v4i(const int4 &v) { return v4i{v.x, v.y, v.z, v.w}; }
 
@@ -104,32 +107,31 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// S: waves splitting the K range of one tile; P: weight steps in flight per wave.
-template <int S, int P>
-__global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(const int8_t *__restrict__ qw,
-                                                                            const uint16_t *__restrict__ dw,
-                                                                            const int8_t *__restrict__ qx,
-                                                                            const uint16_t *__restrict__ dx,
-                                                                            const float *residual, float *y,
-                                                                            int64_t N, int64_t K, int B)
+template <class SH>
+__global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__restrict__ qw,
+                                                            const uint16_t *__restrict__ dw,
+                                                            const int8_t *__restrict__ qx,
+                                                            const uint16_t *__restrict__ dx,
+                                                            const float *residual, float *y, int64_t N, int64_t K,
+                                                            int B)
 {
-    __shared__ __align__(16) uint8_t s_lds[kLdsBytes];
-    uint8_t *const s_codes = s_lds + kCodesOff;
-    const float *const s_dxf = reinterpret_cast<const float *>(s_lds + kDxOff);
+    constexpr int W = SH::W, S = SH::S, P = SH::P, TK = SH::TK;
+    __shared__ __align__(16) uint8_t s_lds[SH::kLds];
+    uint8_t *const s_codes = s_lds + SH::kCodesOff;
+    const float *const s_dxf = reinterpret_cast<const float *>(s_lds + SH::kDxOff);
 
-    constexpr int kTilesPerGroup = kWavesB / S;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int tile = wave / S, split = wave % S;
     const int j = lane & 15;  // weight row in the tile / activation vector of the operand
     const int q = lane >> 4;  // 16-byte k group of a step
-    const int64_t row0 = ((int64_t)blockIdx.x * kTilesPerGroup + tile) * kTileRows;  // wave-uniform
+    const int64_t row0 = ((int64_t)blockIdx.x * SH::kTiles + tile) * kTileRows;  // wave-uniform
     const int64_t row = row0 + j;
     const bool row_ok = row < N;
     const int64_t nb = K / 32;
     // a wave-uniform base and a 32-bit lane offset in [0, 16) rows (rows of at
     // most 2^27 bytes; larger K is refused on the host). Rows past N re-read
-    // row N-1; a tile wholly past N (the last workgroup's) re-reads it too.
+    // row N-1; a tile wholly past N (in the last workgroup) re-reads it too.
     const int64_t rbase = row0 < N ? row0 : N - 1;
     const int jr = (int)((row_ok ? row : N - 1) - rbase);
     const int8_t *wbase = qw + rbase * K;
@@ -138,11 +140,11 @@ __global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(cons
     if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(s_lds) = make_uint4(0u, 0u, 0u, 0u);  // the zero slot
 
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t k0 = 0; k0 < K; k0 += kTileK) {
-        const int kt = (int)(K - k0 < kTileK ? K - k0 : kTileK);  // multiple of 32
+    for (int64_t k0 = 0; k0 < K; k0 += TK) {
+        const int kt = (int)(K - k0 < TK ? K - k0 : TK);  // multiple of 32
         const int nbt = kt / 32;
-        const int cpv = kt / 16;                   // 16-byte chunks per vector
-        const int rowc16 = (cpv + 15) & ~15;       // LDS chunks per vector (whole groups of 16)
+        const int cpv = kt / 16;              // 16-byte chunks per vector
+        const int rowc16 = (cpv + 15) & ~15;  // LDS chunks per vector (whole groups of 16)
         const int steps = (kt + kStepK - 1) / kStepK;
         const int s_begin = steps * split / S, s_end = steps * (split + 1) / S;
 
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(cons
         //    chunk (p % rowc16) ^ vector; positions past the real chunks copy
         //    chunk 0 of their vector and are never read.
         const int code_pos = B * rowc16;
-        for (int p0 = wave * kWave; p0 < code_pos; p0 += kWavesB * kWave) {
+        for (int p0 = wave * kWave; p0 < code_pos; p0 += W * kWave) {
             const int p = p0 + lane;
             const int b = p / rowc16, c = (p - b * rowc16) ^ (b & 15);
             const int bb = b < B ? b : B - 1;
@@ -159,25 +161,24 @@ __global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(cons
             if (p < code_pos)
                 __builtin_amdgcn_global_load_lds(qx + (int64_t)bb * K + k0 + 16 * cc, s_codes + 16 * p0, 16, 0, 0);
         }
-        //    Scales: LDS dword t -> block t / 16, vector t % 16 (vectors past B
-        //    copy vector B-1; their outputs are never stored).
+        //    Activation scales: LDS dword t -> block t / 16, vector t % 16
+        //    (vectors past B copy vector B-1; their outputs are never stored).
         const int dx_pos = nbt * kBatchMax;
-        for (int p0 = wave * kWave; p0 < dx_pos; p0 += kWavesB * kWave) {
+        for (int p0 = wave * kWave; p0 < dx_pos; p0 += W * kWave) {
             const int t = p0 + lane;
             const int blk = t / kBatchMax, b = t - blk * kBatchMax;
             const int bb = b < B ? b : B - 1;
             if (t < dx_pos)
                 __builtin_amdgcn_global_load_lds(dx + (int64_t)bb * nb + k0 / 32 + blk,
-                                                 s_lds + kDxOff + 4 * p0, 2, 0, 0);
+                                                 s_lds + SH::kDxOff + 4 * p0, 2, 0, 0);
         }
-
-        //    Weight scales of this wave's rows and steps: LDS dword t -> row
-        //    t / nbw of the tile, block t % nbw of the wave's blocks (rows past
-        //    N read row N-1; a missing second block of the last step reads the
-        //    first, and its product is zero).
+        //    Weight scales of this wave's rows and steps, into its region of the
+        //    tile's area: LDS dword t -> row t / nbw, block t % nbw of the
+        //    wave's blocks (rows past N read row N-1; a missing second block of
+        //    the last step reads the first, and its product is zero).
         const int nbw = 2 * (s_end - s_begin);
         const int64_t blk0 = k0 / 32 + 2 * s_begin;
-        uint8_t *const s_wsc = s_lds + kWscOff + wave * kWscWave;
+        uint8_t *const s_wsc = s_lds + SH::kWscOff + tile * SH::kWscTile + kTileRows * 4 * (2 * s_begin);
         for (int p0 = 0; p0 < kTileRows * nbw; p0 += kWave) {
             const int t = p0 + lane;
             const int r = t / nbw, bo = t - r * nbw;
@@ -202,9 +203,9 @@ __global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(cons
         //    workgroup; a full __syncthreads would also wait for the weights)
         wait_vmcnt<P>();
         __builtin_amdgcn_s_barrier();
-        //    the staged scale bits to f32, in place, once per tile
-        for (int t = threadIdx.x; t < dx_pos; t += kThreadsB) {
-            uint32_t *v = reinterpret_cast<uint32_t *>(s_lds + kDxOff) + t;
+        //    the staged activation scale bits to f32, in place, once per tile
+        for (int t = threadIdx.x; t < dx_pos; t += SH::kThreads) {
+            uint32_t *v = reinterpret_cast<uint32_t *>(s_lds + SH::kDxOff) + t;
             *v = __builtin_bit_cast(uint32_t, f16_bits_to_f32((uint16_t)*v));
         }
         __builtin_amdgcn_s_barrier();
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kThreadsB, kMinWavesPerSimd) void batch_kernel(cons
             // a lane whose group belongs to the other block (or to a vector
             // past B, or to a missing second block) reads the zero slot
             const int c = 4 * st + q;  // the lane's 16-byte chunk of vector j
-            const uint32_t at = kCodesOff + 16u * (uint32_t)(j * rowc16 + (c ^ j));
+            const uint32_t at = SH::kCodesOff + 16u * (uint32_t)(j * rowc16 + (c ^ j));
             const bool lo_ok = j < B && q < 2, hi_ok = j < B && q >= 2 && hi;
             const v4i a_lo = *reinterpret_cast<const v4i *>(s_lds + (lo_ok ? at : 0u));
             const v4i a_hi = *reinterpret_cast<const v4i *>(s_lds + (hi_ok ? at : 0u));
@@ -301,15 +302,15 @@ bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-template <int S, int P>
+template <class SH>
 hipError_t launch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx, const float *residual,
                   float *y, int64_t N, int64_t K, int B, hipStream_t s)
 {
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
-    const int64_t groups = (tiles + kWavesB / S - 1) / (kWavesB / S);
+    const int64_t groups = (tiles + SH::kTiles - 1) / SH::kTiles;
     void *args[] = {&qw, &dw, &qx, &dx, &residual, &y, &N, &K, &B};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&batch_kernel<S, P>), dim3((unsigned)groups),
-                           dim3(kThreadsB), args, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&batch_kernel<SH>), dim3((unsigned)groups),
+                           dim3(SH::kThreads), args, 0, s);
 }
 
 }  // namespace
@@ -334,7 +335,19 @@ extern "C" q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const 
     if (residual && residual != y && overlap(y, ybytes, residual, ybytes)) return Q8G_ERR_OVERLAP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
-    const hipError_t e = tiles <= kSplitTiles ? launch<4, kPipeSplit>(qw, dw, qx, dx, residual, y, N, K, (int)B, s)
-                                              : launch<1, kPipeWhole>(qw, dw, qx, dx, residual, y, N, K, (int)B, s);
+    const hipError_t e = tiles <= kWideSplitTiles ? launch<WideSplitShape>(qw, dw, qx, dx, residual, y, N, K, (int)B, s)
+                         : tiles <= kSplitTiles   ? launch<SplitShape>(qw, dw, qx, dx, residual, y, N, K, (int)B, s)
+                                                  : launch<WholeShape>(qw, dw, qx, dx, residual, y, N, K, (int)B, s);
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
+extern "C" q8g_status q8g_batch_config(int64_t N, int *k_split, int *steps_in_flight)
+{
+    if (N < 0) return Q8G_ERR_SHAPE;
+    if (!k_split || !steps_in_flight) return Q8G_ERR_NULL;
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    *k_split = tiles <= kWideSplitTiles ? WideSplitShape::S : tiles <= kSplitTiles ? SplitShape::S : WholeShape::S;
+    *steps_in_flight = tiles <= kWideSplitTiles ? WideSplitShape::P : tiles <= kSplitTiles ? SplitShape::P
+                                                                                          : WholeShape::P;
+    return Q8G_OK;
 }

@@ -10,7 +10,10 @@ This module lays one step out two ways over the same buffers, allocated up front
   * per projection one gemv_stacked launch that quantizes the f32 input itself;
   * the whole step as one q8_decode_stack launch (persistent workgroups, a device-wide
     barrier between projections, the next projection's weights fetched during it).
-All three produce bit-identical outputs.
+All three produce bit-identical outputs. Q8BatchStack runs nb decode streams at once
+over the same weights: per projection one q8_quantize_act over all nb inputs and one
+q8_gemv_batch launch (stacked parts are row ranges of one matrix, so one launch
+covers them).
 
 Each projection's input is its own buffer: the layers in between (norms, attention,
 activations) are not part of this path, so the inputs are seeded synthetic vectors.
@@ -20,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import DecodeStackPlan, gemv_stacked, q8_gemv, q8_quantize_act
+from . import DecodeStackPlan, gemv_stacked, q8_gemv, q8_gemv_batch, q8_quantize_act
 
 
 def _dev(a, device):
@@ -127,3 +130,39 @@ class Q8DecodeStack:
     def replay(self):
         self.graph.replay()
 
+
+class Q8BatchStack:
+    """nb activation vectors per projection over the weights of a Q8DecodeStack (shared,
+    not copied). batch: per op a dict with "x" f32 [nb, k] and "r" f32 [nb, n] or None."""
+
+    def __init__(self, stack: Q8DecodeStack, batch):
+        self.stack = stack
+        self.nb = batch[0]["x"].shape[0]
+        dev = stack.device
+        self.bufs = []
+        for b, h in zip(stack.bufs, batch):
+            nb, k = h["x"].shape
+            n = b["qw"].shape[0]
+            self.bufs.append({
+                "x": _dev(h["x"].reshape(-1), dev),
+                "qx": torch.empty(nb * k, dtype=torch.int8, device=dev),
+                "dx": torch.empty(nb * k // 32, dtype=torch.float16, device=dev),
+                "y": torch.empty((nb, n), dtype=torch.float32, device=dev),
+                "r": _dev(h["r"], dev) if h["r"] is not None else None,
+                "k": k,
+            })
+
+    def launch_quantize(self, i, stream=None):
+        b = self.bufs[i]
+        q8_quantize_act(b["x"], b["qx"], b["dx"], stream=stream)
+
+    def launch_gemv(self, i, stream=None):
+        s, b = self.stack.bufs[i], self.bufs[i]
+        k = b["k"]
+        q8_gemv_batch(s["qw"], s["dw"], b["qx"].view(self.nb, k), b["dx"].view(self.nb, k // 32), y=b["y"],
+                      residual=b["r"], stream=stream)
+
+    def step(self, stream=None):
+        for i in range(len(self.bufs)):
+            self.launch_quantize(i, stream)
+            self.launch_gemv(i, stream)

@@ -114,6 +114,11 @@ q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual,
 q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
                          const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream);
 
+/* Launch configuration q8_gemv_batch picks for N rows: how many waves split the K
+ * range of one 16-row tile, and how many 64-column weight steps each wave keeps
+ * in flight. Pure host query; nothing is enqueued. */
+q8g_status q8g_batch_config(int64_t N, int *k_split, int *steps_in_flight);
+
 /* One matrix of a stacked projection. */
 typedef struct {
     const void *w;         /* Q8_0: int8 codes [n][K]; bf16 / f16: uint16 [n][K] */

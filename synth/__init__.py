@@ -38,6 +38,7 @@ TAG_Q8_STACK = 2
 TAG_BF16_4B_GATEUP = 3
 TAG_Q8_HEAD = 4
 TAG_F16_GATEUP = 5
+TAG_Q8_BATCH = 6
 TAG_TEST = 100
 
 
@@ -144,6 +145,13 @@ def q8_gemv_f32x_bytes(n: int, k: int, residual: bool = False) -> int:
     return b + (n * 4 if residual else 0)
 
 
+def q8_batch_gemv_bytes(n: int, k: int, nb: int, residual: bool = False) -> int:
+    """Algorithmic HBM bytes of one small-batch Q8_0 GEMV over nb vectors: the weights
+    once, each vector's quantized activation, f32 outputs (and residuals)."""
+    b = n * k + n * (k // QBLOCK) * 2 + nb * (k + (k // QBLOCK) * 2) + nb * n * 4
+    return b + (nb * n * 4 if residual else 0)
+
+
 def q8_quantize_bytes(k: int) -> int:
     """Algorithmic bytes of one activation quantize: f32 in, int8 codes + binary16 scales out."""
     return 4 * k + k + (k // QBLOCK) * 2
@@ -166,3 +174,15 @@ def q8_stack_inputs(ops, tag: int = TAG_Q8_STACK):
         r = residual_f32(g, op.n) if op.residual else None
         host.append({"qw": qw, "dw": dw, "x": x, "r": r})
     return host
+
+
+def q8_batch_inputs(ops, nb: int, tag: int = TAG_Q8_BATCH):
+    """Seeded activation vectors [nb, k] (and residuals [nb, n] where the projection folds
+    one in) for each projection j of a stack, for nb decode streams at once."""
+    out = []
+    for j, op in enumerate(ops):
+        g = rng_for(tag, j)
+        x = np.stack([activation_f32(g, op.k) for _ in range(nb)])
+        r = np.stack([residual_f32(g, op.n) for _ in range(nb)]) if op.residual else None
+        out.append({"x": x, "r": r})
+    return out
