@@ -50,26 +50,41 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+# the sources that define each kernel family (a counter summary is valid while they are unchanged)
+KERNEL_SOURCES = {
+    "gemv_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
+    "quantize_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
+    "batch_kernel": ("batch.hip", "gemv_device.hpp", "q8gemv.h"),
+    "stack_kernel": ("stack.hip", "gemv_device.hpp", "q8gemv.h"),
+}
+
+
+def source_digest(files) -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "block_quantized_weight_q8_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
+    for fn in files:
+        d = os.path.join(ROOT, "include") if fn.endswith(".h") else os.path.join(ROOT, "block_quantized_weight_q8_amd", "csrc")
+        with open(os.path.join(d, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
 
 
+def kernel_source_digest(kernel: str = "gemv_kernel") -> str:
+    fam = next((k for k in KERNEL_SOURCES if kernel.startswith(k)), "gemv_kernel")
+    return source_digest(KERNEL_SOURCES[fam])
+
+
 def traffic_for(kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
-    taken on the current kernel source; otherwise None."""
+    taken on the current source of that kernel; otherwise None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_digest") != kernel_source_digest():
+    e = t.get("kernels", {}).get(kernel)
+    if not e or e.get("source_digest") != kernel_source_digest(kernel):
         return None
-    return t.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
+    return e.get("bytes_per_launch")
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -223,8 +238,9 @@ def run_stack(args, torch, q8, np):
     for i, b in enumerate(stack.bufs):
         if not torch.equal(b["y"], ref[i]):
             raise SystemExit(f"parity: fused output of {ops[i].name} differs from quantize + gemv")
-    log(f"[bench] fused quantize+GEMV per projection (97 launches), graph replay: {t_fused * 1e6:.1f} us/token; "
-        f"outputs bit-identical")
+    n_launch_fused = sum(1 if op.n <= stack.FUSED_MAX_ROWS else 2 for op in ops)
+    log(f"[bench] fused quantize+GEMV per projection ({n_launch_fused} launches), graph replay: "
+        f"{t_fused * 1e6:.1f} us/token; outputs bit-identical")
 
     # (c) the whole token as one q8_decode_stack launch
     for b in stack.bufs:
@@ -265,16 +281,14 @@ def run_stack(args, torch, q8, np):
                     "avg_launch_us": round(t_persist * 1e6, 2), "bytes_per_launch": step_bytes,
                     "launches_per_step": 1, "traffic": traffic_for(kname)}
     else:
-        fused = mode == "fused"
-        dt = q8.Q8G_Q8_0_F32 if fused else q8.Q8G_Q8_0
         groups = {}
         for i, op in enumerate(ops):
-            r, w = q8.gemv_config(dt, op.n, op.k)
-            groups.setdefault((r, w), []).append(i)
-        kind = "Q8F32" if fused else "Q8"
+            fused = mode == "fused" and op.n <= stack.FUSED_MAX_ROWS
+            r, w = q8.gemv_config(q8.Q8G_Q8_0_F32 if fused else q8.Q8G_Q8_0, op.n, op.k)
+            groups.setdefault((fused, r, w), []).append(i)
         per = {}
-        for (r, w), idx in groups.items():
-            name = f"gemv_kernel<{kind}, rows_per_wave={r}, waves={w}>"
+        for (fused, r, w), idx in groups.items():
+            name = f"gemv_kernel<{'Q8F32' if fused else 'Q8'}, rows_per_wave={r}, waves={w}>"
             if fused:
                 nbytes = [synth.q8_gemv_f32x_bytes(ops[i].n, ops[i].k, ops[i].residual) for i in idx]
                 fn = (lambda idx=idx: [stack.launch_op_fused(i) for i in idx])
@@ -293,7 +307,9 @@ def run_stack(args, torch, q8, np):
                     "unit": "GB/s", "frac": round(db / dt_ / 1e9 / HBM_PEAK_GBPS, 4),
                     "avg_launch_us": round(dt_ * 1e6, 3), "bytes_per_launch": round(db),
                     "launches_per_step": dc, "traffic": traffic_for(dname)}
-    mode = {"fused": "hipGraph, one fused quantize+GEMV launch per projection (97 per token)",
+    launches = {"fused": n_launch_fused, "graph": 2 * len(ops), "decode_stack": 1}[mode]
+    mode = {"fused": "hipGraph, one fused quantize+GEMV launch per projection (quantize + GEMV for the head; "
+                     "98 launches per token)",
             "graph": "hipGraph, q8_quantize_act + GEMV per projection (194 launches per token)",
             "decode_stack": "one q8_decode_stack launch per token"}[mode]
 
@@ -316,7 +332,8 @@ def run_stack(args, torch, q8, np):
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "q8-stack-0.8b", "layers": 24, "hidden": 1024, "vocab": 151936,
-                   "projections_per_token": len(ops), "launches_per_token": 2 * len(ops),
+                   "projections_per_token": len(ops),
+                   "launches_per_token": launches,
                    "bytes_per_step": step_bytes, "mode": mode, "accumulate": "int32 per block, f32"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tok_per_s": round(1.0 / t_step, 1),
@@ -704,7 +721,7 @@ def run_single(args, torch, q8, np):
 def pmc_workload(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
-    decode steps of the fused per-projection path."""
+    decode steps of the fused per-projection path and two steps of the 16-stream stack."""
     import synth
     from block_quantized_weight_q8_amd.stack import Q8DecodeStack
 
@@ -719,7 +736,15 @@ def pmc_workload(args, torch, q8, np):
     for _ in range(2):
         stack.step(fused=True)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_workload": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps"}), flush=True)
+    # the same stack for 16 streams (small-batch GEMV)
+    from block_quantized_weight_q8_amd.stack import Q8BatchStack
+
+    bs = Q8BatchStack(stack, synth.q8_batch_inputs(ops, BATCH))
+    for _ in range(2):
+        bs.step()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_workload": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps, "
+                                      "2 steps of 16 streams"}), flush=True)
 
 
 def main():
@@ -747,8 +772,8 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     q8.load_library()
-    log(f"[bench] device: {torch.cuda.get_device_name(0)}; workload {args.workload}; "
-        f"kernel source {kernel_source_digest()}")
+    log(f"[bench] device: {torch.cuda.get_device_name(0)}; workload {args.workload}; kernel sources "
+        + ", ".join(f"{k} {kernel_source_digest(k)}" for k in KERNEL_SOURCES))
     if args.pmc_workload:
         pmc_workload(args, torch, q8, np)
         return

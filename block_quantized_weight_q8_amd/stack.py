@@ -7,7 +7,8 @@ stack projections that read the same input, fold the residual add into the matmu
 This module lays one step out two ways over the same buffers, allocated up front:
   * per projection one q8_quantize_act and one gemv_stacked (or q8_gemv) launch on
     one stream, in dependency order; the step can be captured into a HIP graph;
-  * per projection one gemv_stacked launch that quantizes the f32 input itself;
+  * per projection one gemv_stacked launch that quantizes the f32 input itself
+    (except matrices with very many rows, where quantize + GEMV is faster);
   * the whole step as one q8_decode_stack launch (persistent workgroups, a device-wide
     barrier between projections, the next projection's weights fetched during it).
 All three produce bit-identical outputs. Q8BatchStack runs nb decode streams at once
@@ -105,9 +106,14 @@ class Q8DecodeStack:
         b = self.bufs[i]
         gemv_stacked(b["parts"], b["x"], stream=stream)
 
+    # Above this many rows the fused launch loses: each of its workgroups quantizes
+    # the whole input again for only 16 rows of output, and on MI355X the 151936-row
+    # output head took 38.9 us fused against 26.9 + 1.6 us as quantize + GEMV.
+    FUSED_MAX_ROWS = 65536
+
     def step(self, stream=None, fused=False):
-        for i in range(len(self.ops)):
-            if fused:
+        for i, op in enumerate(self.ops):
+            if fused and op.n <= self.FUSED_MAX_ROWS:
                 self.launch_op_fused(i, stream)
             else:
                 self.launch_op(i, stream)
