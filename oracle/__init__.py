@@ -6,7 +6,8 @@ shares no code with the HIP library. Arrays are numpy; results are f64.
 
 What it computes is stated, with its sources, at the top of oracle.c:
 the Q8_0 activation quantizer, the per-block int32 dot, the Q8_0 GEMV (single
-vector and small batch) and the bf16 and f16 GEMVs of "Filling in the blanks: Inference using Phobos" (section Fast
+vector and small batch), the bf16 and f16 GEMVs, and the RMS-normalization and
+gated-activation steps folded into a projection's prologue, of "Filling in the blanks: Inference using Phobos" (section Fast
 Decode) and "One level down: #002 the same compiler on a GPU" (sections
 Emitting for a GPU and The numerical contract).
 """
@@ -68,6 +69,10 @@ def _bind(lib):
     lib.orc_f16_gemv_mt.restype = ctypes.c_int
     lib.orc_q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
     lib.orc_q8_gemv_batch.restype = None
+    lib.orc_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _I64, _P]
+    lib.orc_rmsnorm.restype = None
+    lib.orc_silu_mul.argtypes = [_P, _I64, _P]
+    lib.orc_silu_mul.restype = None
     return lib
 
 
@@ -105,6 +110,25 @@ class Oracle:
     def f32_to_f16(self, values) -> np.ndarray:
         values = np.asarray(values, dtype=np.float32).ravel()
         return np.array([self.lib.orc_f32_to_f16(float(v)) for v in values], dtype=np.uint16)
+
+    # neighbour steps folded into a projection's prologue
+    def rmsnorm(self, x, gamma, eps):
+        """f32 h = (x * r) * gamma with r = f32(1 / sqrt(mean(x^2) + eps)) from f64."""
+        x, px = _c(x, np.float32)
+        gamma, pg = _c(gamma, np.float32)
+        assert x.ndim == 1 and gamma.shape == x.shape
+        h = np.empty_like(x)
+        self.lib.orc_rmsnorm(px, pg, float(eps), x.shape[0], h.ctypes.data)
+        return h
+
+    def silu_mul(self, gu):
+        """f32 a = silu(gate) * up from gu = [gate (K) | up (K)], in f64 rounded once."""
+        gu, pgu = _c(gu, np.float32)
+        assert gu.ndim == 1 and gu.shape[0] % 2 == 0
+        k = gu.shape[0] // 2
+        a = np.empty(k, np.float32)
+        self.lib.orc_silu_mul(pgu, k, a.ctypes.data)
+        return a
 
     # the method
     def quantize_act(self, x):
@@ -232,3 +256,11 @@ def f16_gemv(w, x, residual=None, nthreads: int = 0):
 
 def q8_gemv_batch(qw, dw, qx, dx, residual=None, nthreads: int = 0):
     return get().q8_gemv_batch(qw, dw, qx, dx, residual, nthreads)
+
+
+def rmsnorm(x, gamma, eps):
+    return get().rmsnorm(x, gamma, eps)
+
+
+def silu_mul(gu):
+    return get().silu_mul(gu)

@@ -145,6 +145,38 @@ void orc_quantize_act(const float *x, int64_t K, int8_t *qx, uint16_t *dx)
     }
 }
 
+/* ---- neighbour steps folded into a projection's prologue ([H] Emitting for a
+ * GPU: at decode the normalization is fused with the projection after it, and
+ * the activation with the projection after it; [P] Q4_K_M: a norm used inside
+ * the fused kernels). The pages name these steps without formulas; the
+ * readings here are the standard ones of the models the pages run.
+ *
+ * RMS normalization: h_i = (x_i * r) * gamma_i in f32, r = f32(1 / sqrt(ss/K
+ * + eps)) with ss = sum x_i^2 and r's expression in f64 (each f32 square is
+ * exact in f64). The f32 vector h is then quantized by orc_quantize_act. */
+void orc_rmsnorm(const float *x, const float *gamma, float eps, int64_t K, float *h)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < K; ++i)
+        ss += (double)x[i] * (double)x[i];
+    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    for (int64_t i = 0; i < K; ++i) {
+        const float t = x[i] * r;
+        h[i] = t * gamma[i];
+    }
+}
+
+/* Gated activation of the MLP: gu holds gate (first K values) then up (next
+ * K); a_i = silu(gate_i) * up_i = gate_i * up_i / (1 + exp(-gate_i)), in f64,
+ * rounded once to f32. */
+void orc_silu_mul(const float *gu, int64_t K, float *a)
+{
+    for (int64_t i = 0; i < K; ++i) {
+        const double g = (double)gu[i], u = (double)gu[K + i];
+        a[i] = (float)((g * u) / (1.0 + exp(-g)));
+    }
+}
+
 /* ---- block integer dot ([P] Fast Decode: the block math end to end in int8) */
 void orc_block_isums(const int8_t *qw, const int8_t *qx, int64_t N, int64_t K, int32_t *isum)
 {

@@ -447,6 +447,88 @@ def pin_q8_batch_rows_are_single_gemvs(o):
         assert np.array_equal(yt, y) and np.array_equal(St, S)
 
 
+# ----------------------------------------------------------------------------- neighbour steps
+
+
+def np_rmsnorm(x, gamma, eps):
+    """Independent RMS normalization: math.fsum of the squares (correctly rounded), numpy
+    f32 multiplies in the same order (x * r, then * gamma)."""
+    import math
+
+    x = np.asarray(x, np.float32)
+    ss = math.fsum(float(v) * float(v) for v in x)
+    r = np.float32(1.0 / math.sqrt(ss / x.shape[0] + float(eps)))
+    return (x * r).astype(np.float32) * np.asarray(gamma, np.float32)
+
+
+def pin_rmsnorm_vs_independent(o):
+    for j, k in enumerate((32, 1024, 3584, 5120)):
+        g = rng(40 + j)
+        x = g.standard_normal(k, dtype=np.float32) * np.float32(3.0)
+        gamma = (1.0 + 0.1 * g.standard_normal(k)).astype(np.float32)
+        for eps in (1e-6, 1e-2):
+            h = o.rmsnorm(x, gamma, eps)
+            ref = np_rmsnorm(x, gamma, eps)
+            assert np.array_equal(h.view(np.uint32), ref.view(np.uint32)), (k, eps, np.count_nonzero(h != ref))
+
+
+def pin_rmsnorm_closed_forms(o):
+    k = 64
+    ones = np.ones(k, np.float32)
+    # a constant vector c = +-2^e with eps = 0 normalizes to exactly +-1
+    for c in (1.0, -4.0, 2.0**-20, 2.0**30):
+        h = o.rmsnorm(np.full(k, c, np.float32), ones, 0.0)
+        assert np.all(h == np.float32(np.sign(c))), (c, h[:3])
+    # with eps = 0, scaling x by 2^e changes nothing, bit for bit
+    g = rng(45)
+    x = g.standard_normal(k, dtype=np.float32)
+    gamma = g.standard_normal(k, dtype=np.float32)
+    h = o.rmsnorm(x, gamma, 0.0)
+    for e in (-40, -3, 5, 60):
+        assert np.array_equal(o.rmsnorm(x * np.float32(2.0**e), gamma, 0.0), h)
+    # gamma enters linearly: doubling it doubles h exactly
+    assert np.array_equal(o.rmsnorm(x, gamma * np.float32(2), 0.0), h * np.float32(2))
+    # eps dominating a tiny input: r rounds to 1 in f32, h = x * gamma exactly
+    tiny = (x * np.float32(1e-20)).astype(np.float32)
+    assert np.array_equal(o.rmsnorm(tiny, gamma, 1.0), tiny * gamma)
+
+
+def np_silu_mul(gu):
+    gu = np.asarray(gu, np.float32)
+    k = gu.shape[0] // 2
+    gt, up = gu[:k].astype(np.float64), gu[k:].astype(np.float64)
+    with np.errstate(over="ignore"):
+        return ((gt * up) / (1.0 + np.exp(-gt))).astype(np.float32)
+
+
+def pin_silu_mul_vs_independent(o):
+    g = rng(46)
+    for k in (32, 3584):
+        gu = (g.standard_normal(2 * k) * 3.0).astype(np.float32)
+        a = o.silu_mul(gu)
+        ref = np_silu_mul(gu)
+        assert np.array_equal(a.view(np.uint32), ref.view(np.uint32)), np.count_nonzero(a != ref)
+
+
+def pin_silu_mul_closed_forms(o):
+    k = 8
+    up = np.float32([1.5, -2.0, 3.0, 0.25, 7.0, -1.0, 100.0, 0.5])
+    # gate 0 gives 0; up 0 gives 0
+    assert np.all(o.silu_mul(np.concatenate([np.zeros(k, np.float32), up])) == 0)
+    gate = np.float32([0.5, -3.0, 2.0, 9.0, -0.1, 4.0, 1.0, -7.0])
+    assert np.all(o.silu_mul(np.concatenate([gate, np.zeros(k, np.float32)])) == 0)
+    # large gate: exp(-g) vanishes against 1 in f64, so a = f32(g * u) exactly
+    big = np.float32([100.0, 250.0, 90.0, 1000.0, 120.0, 800.0, 64.0, 3e4])
+    assert np.array_equal(o.silu_mul(np.concatenate([big, up])),
+                          (big.astype(np.float64) * up.astype(np.float64)).astype(np.float32))
+    # very negative gate: exp(-g) overflows, a is a signed zero
+    assert np.all(o.silu_mul(np.concatenate([-big * np.float32(10), up])) == 0)
+    # silu(g) - silu(-g) = g, so a(g, u) - a(-g, u) = g * u up to rounding
+    d = o.silu_mul(np.concatenate([gate, up])).astype(np.float64) - \
+        o.silu_mul(np.concatenate([-gate, up])).astype(np.float64)
+    assert np.allclose(d, gate.astype(np.float64) * up, rtol=1e-6, atol=1e-6)
+
+
 # ----------------------------------------------------------------------------- f16 GEMV
 
 

@@ -50,6 +50,11 @@ MUTANTS = [
     ("batch_shared_dx", "qx + b * K, dx + b * nb,", "qx + b * K, dx,"),
     ("batch_shared_residual", "residual ? residual + b * N : NULL", "residual"),
     ("batch_shared_codes", "orc_q8_gemv(qw, dw, qx + b * K,", "orc_q8_gemv(qw, dw, qx,"),
+    ("rmsnorm_no_mean", "sqrt(ss / (double)K + (double)eps)", "sqrt(ss + (double)eps)"),
+    ("rmsnorm_no_gamma", "h[i] = t * gamma[i];", "h[i] = t;"),
+    ("rmsnorm_eps_outside", "sqrt(ss / (double)K + (double)eps)", "sqrt(ss / (double)K) + (double)eps"),
+    ("silu_sign", "exp(-g)", "exp(g)"),
+    ("silu_swapped_halves", "g = (double)gu[i], u = (double)gu[K + i]", "g = (double)gu[K + i], u = (double)gu[i]"),
     ("f16_reversed_row", "orc_f16_value(w[n * K + k])", "orc_f16_value(w[n * K + (K - 1 - k)])"),
     ("f16_decoded_as_bf16", "double p = orc_f16_value(w[n * K + k]) * orc_f16_value(x[k]);",
      "double p = orc_bf16_value(w[n * K + k]) * orc_f16_value(x[k]);"),
