@@ -21,6 +21,11 @@ Other workloads (per-call figures; a step is one call):
   bf16-gateup-18432x2560-x36  bf16 18432x2560 over 36 independent matrices, round-robin
   q8-head-131072x5120   Q8_0 131072x5120, cold cache (1 GiB flush before every call)
   q8-head-151936x1024-b16  q8_gemv_batch over 16 vectors on the 0.8B output head, rotating copies
+  q8-rmsnorm-qkv-4096x1024  the 0.8B QKV projection (stacked 2048/1024/1024) with the RMS
+                        normalization of its input folded into the launch, rotating copies;
+                        also times the two-launch path (normalize+quantize, then GEMV)
+  q8-silumul-down-1024x3584  the 0.8B down projection (residual folded in) with
+                        silu(gate) * up formed in the launch, rotating copies; also the two-launch path
 
 Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
 then K timed steps between two synchronizations, measured with HIP events on the
@@ -42,7 +47,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
 WORKLOADS = ["q8-stack-0.8b", "q8-stack-0.8b-b16", "q8-gateup-7168x1024", "q8-head-151936x1024-b16",
-             "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120"]
+             "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120",
+             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584"]
+NORM_EPS = 1e-6  # RMS-normalization epsilon of the neighbour-step workloads
 BATCH = 16  # decode streams of the -b16 workloads
 
 
@@ -718,6 +725,118 @@ def run_single(args, torch, q8, np):
     }
 
 
+def run_neighbour(args, torch, q8, np):
+    """A projection with its neighbour step folded into the launch (RMS normalization before
+    the stacked QKV, or silu(gate) * up before the down projection), rotating over >= 1 GiB
+    of copies in one HIP graph; the two-launch path (neighbour step + quantize, then the
+    GEMV) is timed the same way for comparison."""
+    import oracle
+    import synth
+
+    orc = oracle.get()
+    wl = args.workload
+    norm = wl == "q8-rmsnorm-qkv-4096x1024"
+    sizes, k = ((2048, 1024, 1024), 1024) if norm else ((1024,), 3584)
+    n = int(sum(sizes))
+    resid = not norm
+    per = synth.q8_rmsnorm_gemv_bytes(n, k) if norm else synth.q8_silu_gemv_bytes(n, k, residual=True)
+    copies = max(2, -(-(1 << 30) // (n * k)))
+    t0 = time.time()
+    mats, first = [], None
+    for j in range(copies):
+        g = synth.rng_for(synth.TAG_NEIGHBOUR, 10000 + j)
+        qw, dw = synth.q8_weights(g, n, k)
+        x = synth.activation_f32(g, k) if norm else synth.gate_up_f32(g, k)
+        gamma = synth.norm_gamma(g, k) if norm else None
+        r = synth.residual_f32(g, n) if resid else None
+        if j == 0:
+            first = (qw, dw, x, gamma, r)
+        m = {"w": torch.from_numpy(qw).cuda(), "dw": torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16),
+             "x": torch.from_numpy(x).cuda(), "y": torch.empty(n, dtype=torch.float32, device="cuda"),
+             "y2": torch.empty(n, dtype=torch.float32, device="cuda"),
+             "qx": torch.empty(k, dtype=torch.int8, device="cuda"),
+             "dx": torch.empty(k // 32, dtype=torch.float16, device="cuda")}
+        m["gamma"] = torch.from_numpy(gamma).cuda() if norm else None
+        m["r"] = torch.from_numpy(r).cuda() if resid else None
+        offs = np.cumsum((0,) + sizes)
+        m["parts"] = [{"w": m["w"][a:b], "dw": m["dw"][a:b], "y": m["y"][a:b]} for a, b in zip(offs[:-1], offs[1:])]
+        m["parts2"] = [{"w": m["w"][a:b], "dw": m["dw"][a:b], "y": m["y2"][a:b]} for a, b in zip(offs[:-1], offs[1:])]
+        mats.append(m)
+    log(f"[bench] {copies} matrices generated and uploaded in {time.time() - t0:.1f}s")
+
+    def fused(m):
+        if norm:
+            q8.gemv_stacked_rmsnorm(m["parts"], m["x"], m["gamma"], NORM_EPS)
+        else:
+            q8.q8_gemv_silu_mul(m["w"], m["dw"], m["x"], y=m["y"], residual=m["r"])
+
+    def two_launch(m):
+        if norm:
+            q8.q8_rmsnorm_quantize_act(m["x"], m["gamma"], NORM_EPS, qx=m["qx"], dx=m["dx"])
+            q8.gemv_stacked(m["parts2"], m["qx"], m["dx"])
+        else:
+            q8.q8_silu_mul_quantize_act(m["x"], qx=m["qx"], dx=m["dx"])
+            q8.q8_gemv(m["w"], m["dw"], m["qx"], m["dx"], y=m["y2"], residual=m["r"])
+
+    fused(mats[0])
+    two_launch(mats[0])
+    torch.cuda.synchronize()
+    y, y2 = mats[0]["y"].cpu().numpy(), mats[0]["y2"].cpu().numpy()
+    if not np.array_equal(y, y2):
+        raise SystemExit("parity: fused and two-launch results differ")
+    qw, dw, x, gamma, r = first
+    h = orc.rmsnorm(x, gamma, NORM_EPS) if norm else orc.silu_mul(x)
+    rq, rd = orc.quantize_act(h)
+    if not (np.array_equal(mats[0]["qx"].cpu().numpy(), rq)
+            and np.array_equal(mats[0]["dx"].cpu().view(torch.int16).numpy().view(np.uint16), rd)):
+        raise SystemExit("parity: quantized activation differs from the oracle")
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(7).integers(0, n, 512)]))
+    yr, S = orc.q8_gemv(qw[rows], dw[rows], rq, rd, r[rows] if resid else None)
+    rel = np.abs(y[rows].astype(np.float64) - yr) / S
+    if not np.all(rel <= 1e-5):
+        raise SystemExit(f"parity: sampled rows off by {rel.max():.2e} * S")
+    log(f"[bench] parity: fused == two-launch bit for bit; codes == oracle; {len(rows)} sampled rows "
+        f"worst |err|/S = {rel.max():.2e}")
+    probe = probe_gbps(q8, torch)
+    reps = max(1, -(-args.steps // copies))
+    warm = max(1, -(-args.warmup // copies))
+    t = graph_seconds(torch, lambda: [fused(m) for m in mats], reps, warm) / copies
+    t2 = graph_seconds(torch, lambda: [two_launch(m) for m in mats], reps, warm) / copies
+    cpu = None
+    if not args.no_cpu_baseline:
+        nth = cpu_threads()
+        calls, c0 = 0, time.perf_counter()
+        while True:
+            hh = orc.rmsnorm(x, gamma, NORM_EPS) if norm else orc.silu_mul(x)
+            orc.q8_gemv(qw, dw, *orc.quantize_act(hh), r, nthreads=nth)
+            calls += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
+        dt_ = time.perf_counter() - c0
+        cpu = {"value": round(calls * per / dt_ / 1e9, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+               "sample": f"{calls} whole {n}x{k} calls, {calls * per} algorithmic bytes in {dt_:.1f} s",
+               "cpu": cpu_model()}
+        log(f"[bench] oracle on {nth} host threads: {cpu['value']} GB/s")
+    gbps = per / t / 1e9
+    rw, ww = q8.gemv_config(q8.Q8G_Q8_0_F32, n, k)
+    kname = f"{'q8_rmsnorm_gemv' if norm else 'q8_silu_gemv'}[rows_per_wave={rw},waves={ww}]"
+    return {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps * copies,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": wl, "parts": list(sizes), "n": n, "k": k, "copies": copies, "bytes_per_call": per,
+                   "call": "gemv_stacked_rmsnorm" if norm else "q8_gemv_silu_mul (residual folded in)",
+                   "timing": "HIP graph over one pass of the copies"},
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
+        "two_launch_us": round(t2 * 1e6, 3), "fused_us": round(t * 1e6, 3),
+        "fused_speedup": round(t2 / t, 3),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t * 1e6, 3),
+                     "bytes_per_launch": per, "traffic": traffic_for(kname)},
+        "cpu_baseline": cpu,
+    }
+
+
 def pmc_workload(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
@@ -781,6 +900,8 @@ def main():
         out = run_stack(args, torch, q8, np)
     elif args.workload == "q8-stack-0.8b-b16":
         out = run_batch_stack(args, torch, q8, np)
+    elif args.workload in ("q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584"):
+        out = run_neighbour(args, torch, q8, np)
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)

@@ -94,6 +94,10 @@ def load_library(path: str = LIB_PATH):
     lib.q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
     lib.q8g_batch_config.argtypes = [_I64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
+    lib.q8_rmsnorm_quantize_act.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I64, _P]
+    lib.q8_silu_mul_quantize_act.argtypes = [_P, _P, _P, _I64, _P]
+    lib.gemv_stacked_rmsnorm.argtypes = [ctypes.POINTER(_Part), ctypes.c_int, _P, _P, ctypes.c_float, _I64, _P]
+    lib.q8_gemv_silu_mul.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
     lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
@@ -102,7 +106,9 @@ def load_library(path: str = LIB_PATH):
     lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
                                     ctypes.POINTER(ctypes.c_int)]
     for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
-               "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack"):
+               "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
+               "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
+               "q8_gemv_silu_mul"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -157,6 +163,39 @@ def q8_quantize_act(x, qx=None, dx=None, stream=None):
     st = load_library().q8_quantize_act(_ptr(x, "x", _F32), _ptr(qx, "qx", _I8, (k,)),
                                         _ptr(dx, "dx", _H16, (k // 32,)), k, _stream(stream))
     _check("q8_quantize_act", st)
+    return qx, dx
+
+
+def q8_rmsnorm_quantize_act(x, gamma, eps, qx=None, dx=None, stream=None):
+    """Quantize (x * r) * gamma, r = 1/sqrt(mean(x^2) + eps), into Q8_0 codes qx int8 [K] and
+    binary16 scales dx [K/32]. x, gamma f32 [K], K <= 16384."""
+    k = x.shape[0] if x.dim() == 1 else -1
+    if k < 0 or k % 32:
+        raise ValueError("x must be 1-D with a length that is a multiple of 32")
+    if qx is None:
+        qx = torch.empty(k, dtype=torch.int8, device=x.device)
+    if dx is None:
+        dx = torch.empty(k // 32, dtype=torch.float16, device=x.device)
+    st = load_library().q8_rmsnorm_quantize_act(
+        _ptr(x, "x", _F32), _ptr(gamma, "gamma", _F32, (k,)), float(eps), _ptr(qx, "qx", _I8, (k,)),
+        _ptr(dx, "dx", _H16, (k // 32,)), k, _stream(stream))
+    _check("q8_rmsnorm_quantize_act", st)
+    return qx, dx
+
+
+def q8_silu_mul_quantize_act(gu, qx=None, dx=None, stream=None):
+    """Quantize silu(gate) * up, gu = [gate | up] f32 [2K], into qx int8 [K] and dx [K/32]."""
+    k2 = gu.shape[0] if gu.dim() == 1 else -1
+    if k2 < 0 or k2 % 64:
+        raise ValueError("gu must be 1-D with a length that is a multiple of 64")
+    k = k2 // 2
+    if qx is None:
+        qx = torch.empty(k, dtype=torch.int8, device=gu.device)
+    if dx is None:
+        dx = torch.empty(k // 32, dtype=torch.float16, device=gu.device)
+    st = load_library().q8_silu_mul_quantize_act(
+        _ptr(gu, "gu", _F32), _ptr(qx, "qx", _I8, (k,)), _ptr(dx, "dx", _H16, (k // 32,)), k, _stream(stream))
+    _check("q8_silu_mul_quantize_act", st)
     return qx, dx
 
 
@@ -275,6 +314,54 @@ def gemv_stacked(parts, x, dx=None, stream=None):
     st = load_library().gemv_stacked(dt, arr, len(parts), px, pdx, k, _stream(stream))
     _check("gemv_stacked", st)
     return outs
+
+
+def gemv_stacked_rmsnorm(parts, x, gamma, eps, stream=None):
+    """One launch over 1..4 Q8_0 matrices (parts as for gemv_stacked) of RMSnorm(x) * gamma:
+    x, gamma f32 [K], K <= 16384, normalized and quantized inside the launch."""
+    if not 1 <= len(parts) <= MAX_PARTS:
+        raise ValueError("1 to 4 parts")
+    k = x.shape[0]
+    arr, outs = _q8_parts(parts, k)
+    st = load_library().gemv_stacked_rmsnorm(arr, len(parts), _ptr(x, "x", _F32, (k,)),
+                                             _ptr(gamma, "gamma", _F32, (k,)), float(eps), k, _stream(stream))
+    _check("gemv_stacked_rmsnorm", st)
+    return outs
+
+
+def q8_gemv_silu_mul(qw, dw, gu, y=None, residual=None, stream=None):
+    """y = Q8_0(qw, dw) · quantize(silu(gate) * up) (+ residual), gu = [gate | up] f32 [2K],
+    the activation formed and quantized inside the launch. Returns y (f32 [N])."""
+    if qw.dim() != 2:
+        raise ValueError("qw must be [N, K]")
+    n, k = qw.shape
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=qw.device)
+    st = load_library().q8_gemv_silu_mul(
+        _ptr(qw, "qw", _I8), _ptr(dw, "dw", _H16, (n, k // 32)), _ptr(gu, "gu", _F32, (2 * k,)),
+        _ptr(residual, "residual", _F32, (n,), optional=True), _ptr(y, "y", _F32, (n,)), n, k, _stream(stream))
+    _check("q8_gemv_silu_mul", st)
+    return y
+
+
+def _q8_parts(parts, k):
+    arr = (_Part * len(parts))()
+    outs = []
+    for i, p in enumerate(parts):
+        w = p["w"]
+        if w.dim() != 2 or w.shape[1] != k:
+            raise ValueError(f"part {i}: w must be [n, {k}]")
+        n = w.shape[0]
+        y = p.get("y")
+        if y is None:
+            y = torch.empty(n, dtype=torch.float32, device=w.device)
+        outs.append(y)
+        arr[i].w = _ptr(w, f"parts[{i}].w", _I8)
+        arr[i].dw = _ptr(p.get("dw"), f"parts[{i}].dw", _H16, (n, k // 32))
+        arr[i].n = n
+        arr[i].y = _ptr(y, f"parts[{i}].y", _F32, (n,))
+        arr[i].residual = _ptr(p.get("residual"), f"parts[{i}].residual", _F32, (n,), optional=True)
+    return arr, outs
 
 
 def probe_read(buf, sink, stream=None):

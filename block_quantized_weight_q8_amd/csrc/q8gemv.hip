@@ -48,13 +48,78 @@ constexpr int kMaxParts = 4;
 
 // Q8: x = int8 codes + binary16 scales; BF16: x = bf16; Q8F32: x = f32, quantized
 // by every workgroup into LDS before use (one launch instead of two); F16:
-// binary16 weights and activation.
-enum class Dt { Q8, BF16, Q8F32, F16 };
+// binary16 weights and activation. Q8NORM and Q8SILU are Q8F32 with a neighbour
+// step folded into the prologue ("One level down: #002 the same compiler on a
+// GPU", section Emitting for a GPU: at decode the normalization is fused with
+// the projection after it, and the activation with the projection after it):
+// Q8NORM quantizes (x * r) * gamma, r = 1/sqrt(mean(x^2) + eps); Q8SILU takes
+// x = [gate | up] (2K values) and quantizes silu(gate) * up.
+enum class Dt { Q8, BF16, Q8F32, F16, Q8NORM, Q8SILU };
+
+// f32 activation quantized inside the launch
+constexpr bool is_fused(Dt dt) { return dt == Dt::Q8F32 || dt == Dt::Q8NORM || dt == Dt::Q8SILU; }
 
 // 16-bit float weights (no block scales), two bytes per element
 constexpr bool is_16bit(Dt dt) { return dt == Dt::BF16 || dt == Dt::F16; }
 
 constexpr int kMaxFusedK = 16384;  // LDS bytes for the codes of a fused launch
+
+// ---- neighbour-step prologues ------------------------------------------------
+// The quantization decision is taken on f32 values, so the oracle and every
+// launch shape must form the same f32 values. The gated activation is one f64
+// expression rounded once. The normalization's sum of squares is formed in f64
+// (every f32 square is exact there) in an order that depends on K only: each
+// 32-value block by its 8 lanes (4 values each, then exchanges at distance 1, 2
+// and 4), then the block sums by every wave alike (lane l takes blocks l, l+64,
+// ..., then exchanges at distance 1..32). Every lane of a group, and every
+// wave, ends with the same bits, because IEEE addition is commutative.
+__device__ __forceinline__ double sq4(const float4 &v)
+{
+    return (((double)v.x * v.x + (double)v.y * v.y) + (double)v.z * v.z) + (double)v.w * v.w;
+}
+
+__device__ __forceinline__ double block_sum8(double p)
+{
+    p += __shfl_xor(p, 1);
+    p += __shfl_xor(p, 2);
+    p += __shfl_xor(p, 4);
+    return p;
+}
+
+// sum of nb block partials in LDS, the same bits in every lane of every wave
+__device__ __forceinline__ double blocks_total(const double *s_bss, int64_t nb, int lane)
+{
+    double t = 0.0;
+    for (int64_t b = lane; b < nb; b += kWave) t += s_bss[b];
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) t += __shfl_xor(t, m);
+    return t;
+}
+
+__device__ __forceinline__ float rms_scale(double ss, int64_t K, float eps)
+{
+    return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    const double gd = g, ud = u;
+    return (float)((gd * ud) / (1.0 + exp(-gd)));
+}
+
+// the f32 values that get quantized: Q8F32 x; Q8NORM (x * r) * gamma; Q8SILU
+// silu(gate) * up (v = gate, v2 = up)
+template <Dt DT>
+__device__ __forceinline__ float4 prologue_value(const float4 &v, const float4 &v2, float r)
+{
+    if constexpr (DT == Dt::Q8NORM) {
+        return make_float4((v.x * r) * v2.x, (v.y * r) * v2.y, (v.z * r) * v2.z, (v.w * r) * v2.w);
+    } else if constexpr (DT == Dt::Q8SILU) {
+        return make_float4(silu_mul(v.x, v2.x), silu_mul(v.y, v2.y), silu_mul(v.z, v2.z), silu_mul(v.w, v2.w));
+    } else {
+        return v;
+    }
+}
 
 
 // Stacked parts. The kernel receives them as separate scalar arguments (see
@@ -226,13 +291,16 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 template <Dt DT, int R, int WAVES>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
                                                             const uint16_t *__restrict__ dx,
+                                                            const float *__restrict__ aux, float eps,
                                                             int64_t K, int64_t n_total)
 {
-    constexpr bool FUSED = DT == Dt::Q8F32;
+    constexpr bool FUSED = is_fused(DT);
+    constexpr bool TWO = DT == Dt::Q8NORM || DT == Dt::Q8SILU;  // a second f32 input per value
     constexpr int kThreadsPerGroup = WAVES * kWave;
     constexpr int kXPasses = 4;  // f32 activation passes requested before the weights
     __shared__ __align__(16) int8_t s_qx[FUSED ? kMaxFusedK : 16];
     __shared__ float s_dx[FUSED ? kMaxFusedK / 32 : 4];
+    __shared__ double s_bss[DT == Dt::Q8NORM ? kMaxFusedK / 32 : 1];
 
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform by construction; readfirstlane lets the compiler keep the
@@ -249,13 +317,20 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     const char *x = static_cast<const char *>(xv);
     const int64_t lane_off = (int64_t)lane * 16;
 
-    float4 xin[kXPasses];
+    // the second input of a value: gamma (Q8NORM) or up (Q8SILU, the upper half of x)
+    const float *x2 = DT == Dt::Q8NORM ? aux : static_cast<const float *>(xv) + K;
+    float4 xin[kXPasses], xin2[kXPasses];
     if constexpr (FUSED) {
+        // Every lane loads, past-the-end lanes from the last 4 values (K >= 32 here:
+        // the host runs K == 0 as the Q8 kind). A load under a lane condition would
+        // be waited for at the branch join, before any weight load is issued.
         const float *xf = static_cast<const float *>(xv);
 #pragma unroll
         for (int p = 0; p < kXPasses; ++p) {
             const int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)p * 4 * kThreadsPerGroup;
-            xin[p] = e < K ? *reinterpret_cast<const float4 *>(xf + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int64_t ec = e < K ? e : K - 4;
+            xin[p] = *reinterpret_cast<const float4 *>(xf + ec);
+            if constexpr (TWO) xin2[p] = *reinterpret_cast<const float4 *>(x2 + ec);
         }
     }
 
@@ -272,12 +347,31 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
 
     if constexpr (FUSED) {
         const float *xf = static_cast<const float *>(xv);
+        // Q8NORM: block sums of squares for every block, then their total
+        float r = 1.0f;
+        if constexpr (DT == Dt::Q8NORM) {
+#pragma unroll
+            for (int p = 0; p < kXPasses; ++p) {
+                const int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)p * 4 * kThreadsPerGroup;
+                if (e - (int64_t)(threadIdx.x & 7) * 4 < K) {  // the 8-lane group of this block is in range
+                    const double b = block_sum8(sq4(xin[p]));
+                    if ((lane & 7) == 0) s_bss[e >> 5] = b;
+                }
+            }
+            for (int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)kXPasses * 4 * kThreadsPerGroup; e < K;
+                 e += 4 * kThreadsPerGroup) {
+                const double b = block_sum8(sq4(*reinterpret_cast<const float4 *>(xf + e)));
+                if ((lane & 7) == 0) s_bss[e >> 5] = b;
+            }
+            __syncthreads();
+            r = rms_scale(blocks_total(s_bss, nb, lane), K, eps);
+        }
 #pragma unroll
         for (int p = 0; p < kXPasses; ++p) {
             const int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)p * 4 * kThreadsPerGroup;
             if (e - (int64_t)(threadIdx.x & 7) * 4 < K) {  // the 8-lane group of this block is in range
                 float d;
-                const uint32_t packed = quantize4(xin[p], &d);
+                const uint32_t packed = quantize4(prologue_value<DT>(xin[p], xin2[p], r), &d);
                 if (e < K) {
                     *reinterpret_cast<uint32_t *>(s_qx + e) = packed;
                     if ((lane & 7) == 0) s_dx[e >> 5] = f16_bits_to_f32(scale_bits(d));
@@ -287,8 +381,9 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
         for (int64_t e = (int64_t)threadIdx.x * 4 + (int64_t)kXPasses * 4 * kThreadsPerGroup; e < K;
              e += 4 * kThreadsPerGroup) {
             const float4 v = *reinterpret_cast<const float4 *>(xf + e);
+            const float4 v2 = TWO ? *reinterpret_cast<const float4 *>(x2 + e) : v;
             float d;
-            const uint32_t packed = quantize4(v, &d);
+            const uint32_t packed = quantize4(prologue_value<DT>(v, v2, r), &d);
             *reinterpret_cast<uint32_t *>(s_qx + e) = packed;
             if ((lane & 7) == 0) s_dx[e >> 5] = f16_bits_to_f32(scale_bits(d));
         }
@@ -324,6 +419,50 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     if ((lane & 7) == 0) dx[e >> 5] = scale_bits(d);
 }
 
+// Quantize silu(gate) * up (gu = [gate | up], K values each): the Q8SILU
+// prologue as its own launch.
+__global__ __launch_bounds__(256) void silu_quantize_kernel(const float *__restrict__ gu, int8_t *__restrict__ qx,
+                                                            uint16_t *__restrict__ dx, int64_t K)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const bool active = e < K;
+    const float4 g = active ? *reinterpret_cast<const float4 *>(gu + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 u = active ? *reinterpret_cast<const float4 *>(gu + K + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float d;
+    const uint32_t packed = quantize4(prologue_value<Dt::Q8SILU>(g, u, 1.0f), &d);
+    if (!active) return;
+    *reinterpret_cast<uint32_t *>(qx + e) = packed;
+    if ((lane & 7) == 0) dx[e >> 5] = scale_bits(d);
+}
+
+// Quantize (x * r) * gamma with the Q8NORM prologue's arithmetic and order, as
+// one workgroup of kNormThreads (K <= kMaxFusedK): block sums of squares, their
+// total, then the values.
+constexpr int kNormThreads = 1024;
+__global__ __launch_bounds__(kNormThreads) void norm_quantize_kernel(const float *__restrict__ x,
+                                                                     const float *__restrict__ gamma, float eps,
+                                                                     int8_t *__restrict__ qx,
+                                                                     uint16_t *__restrict__ dx, int64_t K)
+{
+    __shared__ double s_bss[kMaxFusedK / 32];
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t e = (int64_t)threadIdx.x * 4; e < K; e += 4 * kNormThreads) {
+        const double b = block_sum8(sq4(*reinterpret_cast<const float4 *>(x + e)));
+        if ((lane & 7) == 0) s_bss[e >> 5] = b;
+    }
+    __syncthreads();
+    const float r = rms_scale(blocks_total(s_bss, K / 32, lane), K, eps);
+    for (int64_t e = (int64_t)threadIdx.x * 4; e < K; e += 4 * kNormThreads) {
+        const float4 v = *reinterpret_cast<const float4 *>(x + e);
+        const float4 g = *reinterpret_cast<const float4 *>(gamma + e);
+        float d;
+        const uint32_t packed = quantize4(prologue_value<Dt::Q8NORM>(v, g, r), &d);
+        *reinterpret_cast<uint32_t *>(qx + e) = packed;
+        if ((lane & 7) == 0) dx[e >> 5] = scale_bits(d);
+    }
+}
+
 // ---- host side ---------------------------------------------------------------
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -343,8 +482,8 @@ struct Input {
 };
 
 template <Dt DT, int R, int WAVES>
-hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, int64_t K, int64_t n_total,
-                       hipStream_t s)
+hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const float *aux, float eps, int64_t K,
+                       int64_t n_total, hipStream_t s)
 {
     const int64_t rows_per_block = (int64_t)R * WAVES;
     const int64_t blocks = (n_total + rows_per_block - 1) / rows_per_block;
@@ -352,11 +491,13 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, int64_
     Parts pc = p;
     const void *xc = x;
     const uint16_t *dxc = dx;
+    const float *auxc = aux;
+    float epsc = eps;
     int64_t kc = K, nc = n_total;
     void *args[] = {&pc.w[0],   &pc.w[1],   &pc.w[2],   &pc.w[3],   &pc.dw[0],  &pc.dw[1], &pc.dw[2],
                     &pc.dw[3],  &pc.y[0],   &pc.y[1],   &pc.y[2],   &pc.y[3],   &pc.res[0], &pc.res[1],
                     &pc.res[2], &pc.res[3], &pc.end[0], &pc.end[1], &pc.end[2], &xc,       &dxc,
-                    &kc,        &nc};
+                    &auxc,      &epsc,      &kc,        &nc};
     const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(WAVES * kWave), args, 0, s);
 }
@@ -408,37 +549,50 @@ Config pick_config(q8g_dtype dt, int64_t n_total)
     return c;
 }
 
+// the f32 input and its neighbour step of a fused launch
+struct Prologue {
+    const float *aux;  // Q8NORM: gamma [K]
+    float eps;         // Q8NORM: added to the mean square
+};
+
 template <Dt DT, int W>
-hipError_t dispatch_rows(int rows, const Parts &p, const void *x, const uint16_t *dx, int64_t K, int64_t n_total,
-                         hipStream_t s)
+hipError_t dispatch_rows(int rows, const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K,
+                         int64_t n_total, hipStream_t s)
 {
     switch (rows) {
-    case 4: return launch_gemv<DT, 4, W>(p, x, dx, K, n_total, s);
-    case 2: return launch_gemv<DT, 2, W>(p, x, dx, K, n_total, s);
-    default: return launch_gemv<DT, 1, W>(p, x, dx, K, n_total, s);
+    case 4: return launch_gemv<DT, 4, W>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+    case 2: return launch_gemv<DT, 2, W>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+    default: return launch_gemv<DT, 1, W>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
     }
 }
 
 template <Dt DT>
-hipError_t dispatch_gemv(Config c, const Parts &p, const void *x, const uint16_t *dx, int64_t K, int64_t n_total,
-                         hipStream_t s)
+hipError_t dispatch_gemv(Config c, const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K,
+                         int64_t n_total, hipStream_t s)
 {
-    if constexpr (DT == Dt::Q8F32) {
-        if (c.waves == 8) return dispatch_rows<DT, 8>(c.rows, p, x, dx, K, n_total, s);
+    if constexpr (is_fused(DT)) {
+        if (c.waves == 8) return dispatch_rows<DT, 8>(c.rows, p, x, dx, pr, K, n_total, s);
     }
-    return dispatch_rows<DT, kWavesPerGroup>(c.rows, p, x, dx, K, n_total, s);
+    return dispatch_rows<DT, kWavesPerGroup>(c.rows, p, x, dx, pr, K, n_total, s);
 }
 
+// Launch kinds: the public dtypes, and the two neighbour-step prologues (f32
+// input, Q8_0 weights) reached through their own entry points.
+constexpr int kKindNorm = 100;  // x f32 [K] and gamma f32 [K]
+constexpr int kKindSilu = 101;  // x = [gate | up] f32 [2K]
+
 // Validate parts and the shared input, build the kernel's part table.
-q8g_status prepare(q8g_dtype dt, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx, int64_t K,
-                   Parts &out, int64_t &n_total)
+q8g_status prepare(int dt, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx, int64_t K,
+                   Parts &out, int64_t &n_total, const float *aux = nullptr)
 {
-    if (dt != Q8G_Q8_0 && dt != Q8G_BF16 && dt != Q8G_Q8_0_F32 && dt != Q8G_F16) return Q8G_ERR_ARG;
+    if (dt != Q8G_Q8_0 && dt != Q8G_BF16 && dt != Q8G_Q8_0_F32 && dt != Q8G_F16 && dt != kKindNorm &&
+        dt != kKindSilu)
+        return Q8G_ERR_ARG;
     if (!parts) return Q8G_ERR_NULL;
     if (nparts < 1 || nparts > kMaxParts) return Q8G_ERR_ARG;
     if (K < 0 || K > kMaxElems) return Q8G_ERR_SHAPE;
-    const bool q8 = dt == Q8G_Q8_0 || dt == Q8G_Q8_0_F32;  // Q8_0 weights (codes + scales)
-    const bool fused = dt == Q8G_Q8_0_F32;   // x is f32, quantized in the launch
+    const bool fused = dt == Q8G_Q8_0_F32 || dt == kKindNorm || dt == kKindSilu;  // x is f32, quantized in the launch
+    const bool q8 = dt == Q8G_Q8_0 || fused;  // Q8_0 weights (codes + scales)
     if (q8 ? (K % 32) : (K % 8)) return Q8G_ERR_SHAPE;
     if (fused && K > kMaxFusedK) return Q8G_ERR_SHAPE;
     n_total = 0;
@@ -457,11 +611,13 @@ q8g_status prepare(q8g_dtype dt, const q8g_part *parts, int nparts, const void *
     }
     if (n_total == 0) return Q8G_OK;
     // with K == 0 no weight or activation byte is read, so those may be NULL
-    if (K > 0 && (!x || (q8 && !fused && !dx))) return Q8G_ERR_NULL;
-    if (!aligned(x, 16) || (q8 && !fused && !aligned(dx, 2))) return Q8G_ERR_ALIGN;
+    if (K > 0 && (!x || (q8 && !fused && !dx) || (dt == kKindNorm && !aux))) return Q8G_ERR_NULL;
+    if (!aligned(x, 16) || (q8 && !fused && !aligned(dx, 2)) || (dt == kKindNorm && !aligned(aux, 16)))
+        return Q8G_ERR_ALIGN;
     if (fused) dx = nullptr;  // not read
 
-    const int64_t xbytes = fused ? 4 * K : (q8 ? K : 2 * K);
+    const int64_t xbytes = dt == kKindSilu ? 8 * K : fused ? 4 * K : (q8 ? K : 2 * K);
+    const int64_t auxbytes = dt == kKindNorm ? 4 * K : 0;
     const int64_t dxbytes = (q8 && !fused) ? (K / 32) * 2 : 0;
     int64_t begin = 0;
     int slot = 0;
@@ -485,7 +641,9 @@ q8g_status prepare(q8g_dtype dt, const q8g_part *parts, int nparts, const void *
         const q8g_part &a = parts[i];
         if (a.n == 0) continue;
         const int64_t ybytes = a.n * 4;
-        if (overlap(a.y, ybytes, x, xbytes) || overlap(a.y, ybytes, dx, dxbytes)) return Q8G_ERR_OVERLAP;
+        if (overlap(a.y, ybytes, x, xbytes) || overlap(a.y, ybytes, dx, dxbytes) ||
+            overlap(a.y, ybytes, aux, auxbytes))
+            return Q8G_ERR_OVERLAP;
         for (int j = 0; j < nparts; ++j) {
             const q8g_part &b = parts[j];
             if (b.n == 0) continue;
@@ -502,21 +660,29 @@ q8g_status prepare(q8g_dtype dt, const q8g_part *parts, int nparts, const void *
     return Q8G_OK;
 }
 
-q8g_status run(q8g_dtype dt, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx, int64_t K,
-               void *stream)
+q8g_status run(int dt, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx, int64_t K,
+               void *stream, Prologue pr = Prologue{nullptr, 0.0f})
 {
     Parts p;
     int64_t n_total = 0;
-    const q8g_status st = prepare(dt, parts, nparts, x, dx, K, p, n_total);
+    const q8g_status st = prepare(dt, parts, nparts, x, dx, K, p, n_total, pr.aux);
     if (st != Q8G_OK || n_total == 0) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Config c = pick_config(dt, n_total);
-    const hipError_t e = dt == Q8G_Q8_0       ? dispatch_gemv<Dt::Q8>(c, p, x, dx, K, n_total, s)
-                         : dt == Q8G_Q8_0_F32 ? dispatch_gemv<Dt::Q8F32>(c, p, x, nullptr, K, n_total, s)
-                         : dt == Q8G_F16      ? dispatch_gemv<Dt::F16>(c, p, x, nullptr, K, n_total, s)
-                                              : dispatch_gemv<Dt::BF16>(c, p, x, dx, K, n_total, s);
+    // with K == 0 no activation is read: the f32-input kinds run as the Q8 kind
+    // (their kernels assume K >= 32)
+    if (K == 0 && (dt == Q8G_Q8_0_F32 || dt == kKindNorm || dt == kKindSilu)) dt = Q8G_Q8_0;
+    // the neighbour-step kinds launch like the fused f32-input kind
+    const Config c = pick_config(dt == kKindNorm || dt == kKindSilu ? Q8G_Q8_0_F32 : (q8g_dtype)dt, n_total);
+    const hipError_t e = dt == Q8G_Q8_0       ? dispatch_gemv<Dt::Q8>(c, p, x, dx, pr, K, n_total, s)
+                         : dt == Q8G_Q8_0_F32 ? dispatch_gemv<Dt::Q8F32>(c, p, x, nullptr, pr, K, n_total, s)
+                         : dt == kKindNorm    ? dispatch_gemv<Dt::Q8NORM>(c, p, x, nullptr, pr, K, n_total, s)
+                         : dt == kKindSilu    ? dispatch_gemv<Dt::Q8SILU>(c, p, x, nullptr, pr, K, n_total, s)
+                         : dt == Q8G_F16      ? dispatch_gemv<Dt::F16>(c, p, x, nullptr, pr, K, n_total, s)
+                                              : dispatch_gemv<Dt::BF16>(c, p, x, dx, pr, K, n_total, s);
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
+
+bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }  // finite, not negative (NaN fails)
 
 }  // namespace
 
@@ -570,7 +736,65 @@ q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual,
 q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx,
                         int64_t K, void *stream)
 {
+    if (dtype != Q8G_Q8_0 && dtype != Q8G_BF16 && dtype != Q8G_Q8_0_F32 && dtype != Q8G_F16) return Q8G_ERR_ARG;
     return run(dtype, parts, nparts, x, dx, K, stream);
+}
+
+q8g_status q8_rmsnorm_quantize_act(const float *x, const float *gamma, float eps, int8_t *qx, uint16_t *dx, int64_t K,
+                                   void *stream)
+{
+    if (K < 0 || K > kMaxFusedK || K % 32) return Q8G_ERR_SHAPE;
+    if (!eps_ok(eps)) return Q8G_ERR_ARG;
+    if (K == 0) return Q8G_OK;
+    if (!x || !gamma || !qx || !dx) return Q8G_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(qx, 16) || !aligned(dx, 2)) return Q8G_ERR_ALIGN;
+    if (overlap(qx, K, x, 4 * K) || overlap(qx, K, gamma, 4 * K) || overlap(dx, K / 16, x, 4 * K) ||
+        overlap(dx, K / 16, gamma, 4 * K) || overlap(qx, K, dx, K / 16))
+        return Q8G_ERR_OVERLAP;
+    const float *xc = x, *gc = gamma;
+    float ec = eps;
+    int8_t *qc = qx;
+    uint16_t *dc = dx;
+    int64_t kc = K;
+    void *args[] = {&xc, &gc, &ec, &qc, &dc, &kc};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&norm_quantize_kernel), dim3(1),
+                                         dim3(kNormThreads), args, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
+q8g_status q8_silu_mul_quantize_act(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, void *stream)
+{
+    if (K < 0 || K > kMaxElems / 2 || K % 32) return Q8G_ERR_SHAPE;
+    if (K == 0) return Q8G_OK;
+    if (!gu || !qx || !dx) return Q8G_ERR_NULL;
+    if (!aligned(gu, 16) || !aligned(qx, 16) || !aligned(dx, 2)) return Q8G_ERR_ALIGN;
+    if (overlap(qx, K, gu, 8 * K) || overlap(dx, K / 16, gu, 8 * K) || overlap(qx, K, dx, K / 16))
+        return Q8G_ERR_OVERLAP;
+    const int64_t blocks = (K / 4 + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return Q8G_ERR_SHAPE;
+    const float *gc = gu;
+    int8_t *qc = qx;
+    uint16_t *dc = dx;
+    int64_t kc = K;
+    void *args[] = {&gc, &qc, &dc, &kc};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&silu_quantize_kernel), dim3((unsigned)blocks),
+                                         dim3(256), args, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
+q8g_status gemv_stacked_rmsnorm(const q8g_part *parts, int nparts, const float *x, const float *gamma, float eps,
+                                int64_t K, void *stream)
+{
+    if (!eps_ok(eps)) return Q8G_ERR_ARG;
+    return run(kKindNorm, parts, nparts, x, nullptr, K, stream, Prologue{gamma, eps});
+}
+
+q8g_status q8_gemv_silu_mul(const int8_t *qw, const uint16_t *dw, const float *gu, const float *residual, float *y,
+                            int64_t N, int64_t K, void *stream)
+{
+    if (N < 0) return Q8G_ERR_SHAPE;
+    const q8g_part part = {qw, dw, N, y, residual};
+    return run(kKindSilu, &part, 1, gu, nullptr, K, stream);
 }
 
 q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows, int *waves)

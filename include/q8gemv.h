@@ -142,6 +142,44 @@ typedef struct {
 q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, const void *x,
                         const uint16_t *dx, int64_t K, void *stream);
 
+/* ---- neighbour steps folded into the projection --------------------------
+ * [H] Emitting for a GPU: at decode the normalization runs fused with the
+ * projection that follows it, and the activation with the projection that
+ * follows it. [P] Q4_K_M names the operations of a block's forward pass: RMS
+ * normalization before the attention and MLP projections, and the gated MLP.
+ * The values that get quantized are formed in f32 exactly as follows:
+ *   RMS normalization (x, gamma f32 [K], eps >= 0 finite):
+ *     ss = sum_i x_i^2 in f64 (every square exact), summed in an order that
+ *          depends on K only;
+ *     r  = fl32(1 / sqrt(ss / K + eps)) in f64, rounded once;
+ *     h_i = fl32(fl32(x_i * r) * gamma_i).
+ *   Gated activation (gu f32 [2K] = gate [K] then up [K]):
+ *     a_i = fl32(gate_i * up_i / (1 + exp(-gate_i))) in f64, rounded once.
+ * h or a is then quantized exactly as q8_quantize_act quantizes x. */
+
+/* Quantize RMSnorm(x) * gamma. K % 32 == 0, K <= 16384 (one workgroup holds
+ * the row). x, gamma f32 [K] 16-byte aligned; qx int8 [K] 16-byte aligned;
+ * dx uint16 [K/32]. Outputs may not overlap the inputs or each other. */
+q8g_status q8_rmsnorm_quantize_act(const float *x, const float *gamma, float eps, int8_t *qx, uint16_t *dx,
+                                   int64_t K, void *stream);
+
+/* Quantize silu(gate) * up. gu f32 [2K] 16-byte aligned; qx, dx as above;
+ * K % 32 == 0. */
+q8g_status q8_silu_mul_quantize_act(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, void *stream);
+
+/* Stacked Q8_0 projection of RMSnorm(x) * gamma: one launch normalizes and
+ * quantizes x in every workgroup, then runs the dot products. K <= 16384.
+ * Part p's result is identical, bit for bit, to q8_rmsnorm_quantize_act then
+ * q8_gemv on that part; no output may overlap x or gamma. */
+q8g_status gemv_stacked_rmsnorm(const q8g_part *parts, int nparts, const float *x, const float *gamma,
+                                float eps, int64_t K, void *stream);
+
+/* Q8_0 GEMV of silu(gate) * up: y = W · a (+ residual), a formed and
+ * quantized inside the launch from gu f32 [2K]. K <= 16384. Identical, bit for
+ * bit, to q8_silu_mul_quantize_act then q8_gemv; y may not overlap gu. */
+q8g_status q8_gemv_silu_mul(const int8_t *qw, const uint16_t *dw, const float *gu, const float *residual,
+                            float *y, int64_t N, int64_t K, void *stream);
+
 /* ---- a whole decode step in one launch ------------------------------------
  * "Filling in the blanks: Inference using Phobos", section Fast Decode, lists
  * the launch-level steps of a fast decode pass: replay the pass as one unit,

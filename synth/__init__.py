@@ -18,6 +18,8 @@ on a GPU" (§Emitting for a GPU: the bf16 gate+up projection, 1024->7168 on the
 * bf16 activation: N(0, 1) in f32, rounded to bf16.
 * f16 weights / activation: as bf16, rounded to IEEE binary16 instead.
 * residual: N(0, 1) in f32.
+* normalization input: N(0, 1) in f32; its weights gamma: 1 + 0.1 N(0, 1).
+* gated activation input [gate | up]: gate 2 N(0, 1), up N(0, 1), in f32.
 
 Every matrix j of workload `tag` draws from
 ``np.random.default_rng(np.random.SeedSequence([tag, j]))`` in the order
@@ -39,6 +41,7 @@ TAG_BF16_4B_GATEUP = 3
 TAG_Q8_HEAD = 4
 TAG_F16_GATEUP = 5
 TAG_Q8_BATCH = 6
+TAG_NEIGHBOUR = 7
 TAG_TEST = 100
 
 
@@ -100,6 +103,21 @@ def residual_f32(rng: np.random.Generator, n: int) -> np.ndarray:
     return rng.standard_normal(n, dtype=np.float32)
 
 
+def norm_gamma(rng: np.random.Generator, k: int) -> np.ndarray:
+    """Per-channel RMS-normalization weights: 1 + 0.1 N(0, 1)."""
+    g = rng.standard_normal(k, dtype=np.float32)
+    g *= np.float32(0.1)
+    g += np.float32(1.0)
+    return g
+
+
+def gate_up_f32(rng: np.random.Generator, k: int) -> np.ndarray:
+    """[gate | up] f32 [2k]: gate 2 N(0, 1) (both arms of silu), up N(0, 1)."""
+    gate = rng.standard_normal(k, dtype=np.float32)
+    gate *= np.float32(2.0)
+    return np.concatenate([gate, rng.standard_normal(k, dtype=np.float32)])
+
+
 # ---------------------------------------------------------------------------
 # Workload shapes
 
@@ -150,6 +168,18 @@ def q8_batch_gemv_bytes(n: int, k: int, nb: int, residual: bool = False) -> int:
     once, each vector's quantized activation, f32 outputs (and residuals)."""
     b = n * k + n * (k // QBLOCK) * 2 + nb * (k + (k // QBLOCK) * 2) + nb * n * 4
     return b + (nb * n * 4 if residual else 0)
+
+
+def q8_rmsnorm_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
+    """Algorithmic bytes of a Q8_0 GEMV that normalizes its f32 input in the same
+    launch: q8_gemv_f32x_bytes plus the f32 normalization weights."""
+    return q8_gemv_f32x_bytes(n, k, residual) + 4 * k
+
+
+def q8_silu_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
+    """Algorithmic bytes of a Q8_0 GEMV that forms silu(gate) * up from f32 [2k] in the
+    same launch: q8_gemv_f32x_bytes plus the second f32 half."""
+    return q8_gemv_f32x_bytes(n, k, residual) + 4 * k
 
 
 def q8_quantize_bytes(k: int) -> int:

@@ -43,6 +43,10 @@ def lib():
     L.f16_gemv.argtypes = [P, P, P, P, I64, I64, P]
     L.q8_gemv_batch.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
     L.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(Part), ctypes.c_int, P, P, I64, P]
+    L.q8_rmsnorm_quantize_act.argtypes = [P, P, ctypes.c_float, P, P, I64, P]
+    L.q8_silu_mul_quantize_act.argtypes = [P, P, P, I64, P]
+    L.gemv_stacked_rmsnorm.argtypes = [ctypes.POINTER(Part), ctypes.c_int, P, P, ctypes.c_float, I64, P]
+    L.q8_gemv_silu_mul.argtypes = [P, P, P, P, P, I64, I64, P]
     L.q8g_status_str.argtypes = [ctypes.c_int]
     L.q8g_status_str.restype = ctypes.c_char_p
     L.q8g_probe_read.argtypes = [P, I64, P, P]
@@ -53,8 +57,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     for expected in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
-                     "q8g_status_str",
-                     "q8g_probe_read", "q8g_flush"):
+                     "q8g_status_str", "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act",
+                     "gemv_stacked_rmsnorm", "q8_gemv_silu_mul", "q8g_probe_read", "q8g_flush"):
         assert expected in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -180,6 +184,63 @@ def test_stacked_validation(lib):
     assert s(0, two, 2, QX, DX, 64, None) == ERR_OVERLAP
     # all parts empty: nothing to do
     assert s(1, parts((None, None, 0, None, None), (None, None, 0, None, None)), 2, None, None, 16, None) == OK
+
+
+def test_rmsnorm_quantize_validation(lib):
+    q = lib.q8_rmsnorm_quantize_act
+    G = R  # gamma
+    assert q(X, G, 1e-6, QX, DX, 48, None) == ERR_SHAPE  # K % 32
+    assert q(X, G, 1e-6, QX, DX, 16384 + 32, None) == ERR_SHAPE  # one workgroup holds the row
+    assert q(X, G, 1e-6, QX, DX, -32, None) == ERR_SHAPE
+    assert q(X, G, -1e-6, QX, DX, 64, None) == ERR_ARG  # eps < 0
+    assert q(X, G, float("nan"), QX, DX, 64, None) == ERR_ARG
+    assert q(X, G, float("inf"), QX, DX, 64, None) == ERR_ARG
+    assert q(None, None, 0.0, None, None, 0, None) == OK  # empty
+    assert q(X, None, 1e-6, QX, DX, 64, None) == ERR_NULL
+    assert q(None, G, 1e-6, QX, DX, 64, None) == ERR_NULL
+    assert q(X, G, 1e-6, QX, None, 64, None) == ERR_NULL
+    assert q(X, G + 4, 1e-6, QX, DX, 64, None) == ERR_ALIGN
+    assert q(X + 4, G, 1e-6, QX, DX, 64, None) == ERR_ALIGN
+    assert q(X, G, 1e-6, QX + 1, DX, 64, None) == ERR_ALIGN
+    assert q(X, G, 1e-6, QX, DX + 1, 64, None) == ERR_ALIGN
+    assert q(X, G, 1e-6, G + 16, DX, 64, None) == ERR_OVERLAP  # codes inside gamma
+    assert q(X, G, 1e-6, QX, X + 64, 64, None) == ERR_OVERLAP  # scales inside x
+    assert q(X, G, 1e-6, QX, QX + 32, 64, None) == ERR_OVERLAP
+
+
+def test_silu_mul_quantize_validation(lib):
+    q = lib.q8_silu_mul_quantize_act
+    assert q(X, QX, DX, 48, None) == ERR_SHAPE
+    assert q(X, QX, DX, -32, None) == ERR_SHAPE
+    assert q(None, None, None, 0, None) == OK
+    assert q(None, QX, DX, 64, None) == ERR_NULL
+    assert q(X + 4, QX, DX, 64, None) == ERR_ALIGN
+    assert q(X, QX, DX + 1, 64, None) == ERR_ALIGN
+    assert q(X, X + 4 * 64, DX, 64, None) == ERR_OVERLAP  # codes inside the up half
+    assert q(X, QX, QX + 32, 64, None) == ERR_OVERLAP
+
+
+def test_fused_neighbour_gemv_validation(lib):
+    Part = lib.Part
+    s = lib.gemv_stacked_rmsnorm
+    G = R
+    one = (Part * 1)(Part(W, DW, 8, Y, None))
+    assert s(one, 1, X, G, -1.0, 64, None) == ERR_ARG
+    assert s(one, 0, X, G, 1e-6, 64, None) == ERR_ARG
+    assert s(one, 1, X, G, 1e-6, 16384 + 32, None) == ERR_SHAPE
+    assert s(one, 1, X, G, 1e-6, 48, None) == ERR_SHAPE
+    assert s(one, 1, X, None, 1e-6, 64, None) == ERR_NULL  # gamma
+    assert s(one, 1, X, G + 8, 1e-6, 64, None) == ERR_ALIGN
+    assert s((Part * 1)(Part(W, DW, 8, G + 128, None)), 1, X, G, 1e-6, 64, None) == ERR_OVERLAP  # y in gamma
+    assert s((Part * 1)(Part(W, None, 8, Y, None)), 1, X, G, 1e-6, 64, None) == ERR_NULL  # dw
+    g = lib.q8_gemv_silu_mul
+    assert g(W, DW, X, None, Y, 8, 48, None) == ERR_SHAPE
+    assert g(W, DW, X, None, Y, -1, 64, None) == ERR_SHAPE
+    assert g(W, DW, X, None, Y, 8, 16384 + 32, None) == ERR_SHAPE
+    assert g(None, None, None, None, None, 0, 64, None) == OK
+    assert g(W, DW, None, None, Y, 8, 64, None) == ERR_NULL
+    assert g(W, DW, X + 4, None, Y, 8, 64, None) == ERR_ALIGN
+    assert g(W, DW, X, None, X + 4 * 64, 8, 64, None) == ERR_OVERLAP  # y in the up half
 
 
 def test_probe_validation(lib):
