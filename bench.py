@@ -840,7 +840,8 @@ def run_neighbour(args, torch, q8, np):
 def pmc_workload(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
-    decode steps of the fused per-projection path and two steps of the 16-stream stack."""
+    decode steps of the fused per-projection path, two steps of the 16-stream stack, and
+    four launches of each neighbour-step GEMV (distinct weights each time)."""
     import synth
     from block_quantized_weight_q8_amd.stack import Q8DecodeStack
 
@@ -862,8 +863,23 @@ def pmc_workload(args, torch, q8, np):
     for _ in range(2):
         bs.step()
     torch.cuda.synchronize()
+    # the two neighbour-step launches, each over 4 distinct copies of its weights
+    for j in range(4):
+        g = synth.rng_for(synth.TAG_NEIGHBOUR, 20000 + j)
+        qw, dw = synth.q8_weights(g, 4096, 1024)
+        x, gamma = synth.activation_f32(g, 1024), synth.norm_gamma(g, 1024)
+        w = torch.from_numpy(qw).cuda()
+        dwt = torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16)
+        q8.gemv_stacked_rmsnorm([{"w": w[:2048], "dw": dwt[:2048]}, {"w": w[2048:3072], "dw": dwt[2048:3072]},
+                                 {"w": w[3072:], "dw": dwt[3072:]}], torch.from_numpy(x).cuda(),
+                                torch.from_numpy(gamma).cuda(), NORM_EPS)
+        qw, dw = synth.q8_weights(g, 1024, 3584)
+        q8.q8_gemv_silu_mul(torch.from_numpy(qw).cuda(), torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16),
+                            torch.from_numpy(synth.gate_up_f32(g, 3584)).cuda(),
+                            residual=torch.from_numpy(synth.residual_f32(g, 1024)).cuda())
+    torch.cuda.synchronize()
     print(json.dumps({"pmc_workload": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps, "
-                                      "2 steps of 16 streams"}), flush=True)
+                                      "2 steps of 16 streams, 4 + 4 neighbour-step launches"}), flush=True)
 
 
 def main():
