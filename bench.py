@@ -26,6 +26,10 @@ Other workloads (per-call figures; a step is one call):
                         also times the two-launch path (normalize+quantize, then GEMV)
   q8-silumul-down-1024x3584  the 0.8B down projection (residual folded in) with
                         silu(gate) * up formed in the launch, rotating copies; also the two-launch path
+  q8-mlp-0.8b           the 0.8B MLP block (RMSnorm, gate+up 2x3584x1024, silu*up, down 1024x3584 with
+                        the residual) as two launches: gate+up with the normalization in its prologue
+                        and silu*up quantized in its epilogue, then the Q8_0 down projection; also the
+                        prologue-fused and the four-launch chains (all three bit-identical)
 
 Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
 then K timed steps between two synchronizations, measured with HIP events on the
@@ -48,7 +52,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
 WORKLOADS = ["q8-stack-0.8b", "q8-stack-0.8b-b16", "q8-gateup-7168x1024", "q8-head-151936x1024-b16",
              "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120",
-             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584"]
+             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584", "q8-mlp-0.8b"]
 NORM_EPS = 1e-6  # RMS-normalization epsilon of the neighbour-step workloads
 BATCH = 16  # decode streams of the -b16 workloads
 
@@ -837,6 +841,134 @@ def run_neighbour(args, torch, q8, np):
     }
 
 
+def run_mlp(args, torch, q8, np):
+    """The 0.8B MLP block, rotating over >= 1 GiB of copies in one HIP graph per chain."""
+    import oracle
+    import synth
+
+    orc = oracle.get()
+    f, k = 3584, 1024
+    b1 = 2 * f * k + 2 * (2 * f * (k // 32)) + 8 * k + f + 2 * (f // 32)  # gate+up launch
+    b2 = synth.q8_gemv_bytes(k, f, residual=True)  # down launch (reads qa/da)
+    per = b1 + b2
+    copies = max(2, -(-(1 << 30) // (3 * f * k)))
+    t0 = time.time()
+    mats, first = [], None
+    for j in range(copies):
+        g = synth.rng_for(synth.TAG_NEIGHBOUR, 30000 + j)
+        qgu, dgu = synth.q8_weights(g, 2 * f, k)
+        qd, dd = synth.q8_weights(g, k, f)
+        x, gamma, r = synth.activation_f32(g, k), synth.norm_gamma(g, k), synth.residual_f32(g, k)
+        if j == 0:
+            first = (qgu, dgu, qd, dd, x, gamma, r)
+        h16 = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+        m = {"wgu": torch.from_numpy(qgu).cuda(), "dgu": h16(dgu), "wd": torch.from_numpy(qd).cuda(), "dd": h16(dd),
+             "x": torch.from_numpy(x).cuda(), "gamma": torch.from_numpy(gamma).cuda(),
+             "r": torch.from_numpy(r).cuda(), "qa": torch.empty(f, dtype=torch.int8, device="cuda"),
+             "da": torch.empty(f // 32, dtype=torch.float16, device="cuda"),
+             "qx": torch.empty(k, dtype=torch.int8, device="cuda"),
+             "dx": torch.empty(k // 32, dtype=torch.float16, device="cuda"),
+             "gu": torch.empty(2 * f, dtype=torch.float32, device="cuda"),
+             "y": torch.empty(k, dtype=torch.float32, device="cuda"),
+             "y2": torch.empty(k, dtype=torch.float32, device="cuda"),
+             "y3": torch.empty(k, dtype=torch.float32, device="cuda")}
+        mats.append(m)
+    log(f"[bench] {copies} MLP weight sets generated and uploaded in {time.time() - t0:.1f}s")
+
+    def gate_up(m):
+        return (m["wgu"][:f], m["dgu"][:f], m["wgu"][f:], m["dgu"][f:])
+
+    def epi_front(m):
+        q8.q8_gateup_silu_quantize(*gate_up(m), m["x"], gamma=m["gamma"], eps=NORM_EPS, qa=m["qa"], da=m["da"])
+
+    def epi(m):
+        epi_front(m)
+        q8.q8_gemv(m["wd"], m["dd"], m["qa"], m["da"], y=m["y"], residual=m["r"])
+
+    def pro(m):
+        wg, dg, wu, du = gate_up(m)
+        q8.gemv_stacked_rmsnorm([{"w": wg, "dw": dg, "y": m["gu"][:f]}, {"w": wu, "dw": du, "y": m["gu"][f:]}],
+                                m["x"], m["gamma"], NORM_EPS)
+        q8.q8_gemv_silu_mul(m["wd"], m["dd"], m["gu"], y=m["y2"], residual=m["r"])
+
+    def four(m):
+        wg, dg, wu, du = gate_up(m)
+        q8.q8_rmsnorm_quantize_act(m["x"], m["gamma"], NORM_EPS, qx=m["qx"], dx=m["dx"])
+        q8.gemv_stacked([{"w": wg, "dw": dg, "y": m["gu"][:f]}, {"w": wu, "dw": du, "y": m["gu"][f:]}], m["qx"], m["dx"])
+        q8.q8_silu_mul_quantize_act(m["gu"], qx=m["qa"], dx=m["da"])
+        q8.q8_gemv(m["wd"], m["dd"], m["qa"], m["da"], y=m["y3"], residual=m["r"])
+
+    m0 = mats[0]
+    four(m0)
+    pro(m0)
+    epi(m0)
+    torch.cuda.synchronize()
+    y, y2, y3 = m0["y"].cpu().numpy(), m0["y2"].cpu().numpy(), m0["y3"].cpu().numpy()
+    if not (np.array_equal(y, y2) and np.array_equal(y, y3)):
+        raise SystemExit("parity: the three MLP chains differ")
+    qgu, dgu, qd, dd, x, gamma, r = first
+    # the oracle on the GPU's f32 gate/up results: its silu*up + quantizer must give the same codes
+    gu = m0["gu"].cpu().numpy()
+    rq, rd = orc.quantize_act(orc.silu_mul(gu))
+    if not (np.array_equal(m0["qa"].cpu().numpy(), rq)
+            and np.array_equal(m0["da"].cpu().view(torch.int16).numpy().view(np.uint16), rd)):
+        raise SystemExit("parity: the MLP activation codes differ from the oracle's")
+    hq, hd = orc.quantize_act(orc.rmsnorm(x, gamma, NORM_EPS))
+    rows = np.unique(np.concatenate([[0, 2 * f - 1], np.random.default_rng(7).integers(0, 2 * f, 256)]))
+    yr, S = orc.q8_gemv(qgu[rows], dgu[rows], hq, hd)
+    rel_gu = np.max(np.abs(gu[rows].astype(np.float64) - yr) / S)
+    yr, S = orc.q8_gemv(qd, dd, rq, rd, r)
+    rel = np.max(np.abs(y.astype(np.float64) - yr) / S)
+    if not (rel_gu <= 1e-5 and rel <= 1e-5):
+        raise SystemExit(f"parity: gate/up off by {rel_gu:.2e} * S, down by {rel:.2e} * S")
+    log(f"[bench] parity: three chains bit-identical; codes == oracle; worst |err|/S gate/up {rel_gu:.2e}, "
+        f"down {rel:.2e}")
+    probe = probe_gbps(q8, torch)
+    reps = max(1, -(-args.steps // copies))
+    warm = max(1, -(-args.warmup // copies))
+    t = graph_seconds(torch, lambda: [epi(m) for m in mats], reps, warm) / copies
+    t_pro = graph_seconds(torch, lambda: [pro(m) for m in mats], reps, warm) / copies
+    t_four = graph_seconds(torch, lambda: [four(m) for m in mats], reps, warm) / copies
+    t_front = graph_seconds(torch, lambda: [epi_front(m) for m in mats], reps, warm) / copies
+    log(f"[bench] MLP block: epilogue chain {t * 1e6:.2f} us, prologue chain {t_pro * 1e6:.2f} us, "
+        f"four launches {t_four * 1e6:.2f} us; gate+up with epilogue alone {t_front * 1e6:.2f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        nth = cpu_threads()
+        calls, c0 = 0, time.perf_counter()
+        while True:
+            hq, hd = orc.quantize_act(orc.rmsnorm(x, gamma, NORM_EPS))
+            yy, _ = orc.q8_gemv(qgu, dgu, hq, hd, nthreads=nth)
+            aq, ad = orc.quantize_act(orc.silu_mul(yy.astype(np.float32)))
+            orc.q8_gemv(qd, dd, aq, ad, r, nthreads=nth)
+            calls += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
+        dt_ = time.perf_counter() - c0
+        cpu = {"value": round(calls * per / dt_ / 1e9, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+               "sample": f"{calls} whole MLP blocks (RMSnorm, 7168x1024, silu*up, 1024x3584), "
+                         f"{calls * per} algorithmic bytes in {dt_:.1f} s", "cpu": cpu_model()}
+        log(f"[bench] oracle on {nth} host threads: {cpu['value']} GB/s")
+    gbps = per / t / 1e9
+    front_gbps = b1 / t_front / 1e9
+    return {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps * copies,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "q8-mlp-0.8b", "hidden": k, "ffn": f, "copies": copies, "bytes_per_step": per,
+                   "chain": "q8_gateup_rmsnorm_silu_quantize, then q8_gemv (down, residual)",
+                   "timing": "HIP graph over one pass of the copies"},
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
+        "chains_us": {"epilogue_2_launches": round(t * 1e6, 3), "prologue_2_launches": round(t_pro * 1e6, 3),
+                      "four_launches": round(t_four * 1e6, 3)},
+        "roofline": {"bound": "hbm", "kernel": "q8_gateup_rmsnorm_silu[rows_per_wave=4,waves=16]",
+                     "achieved": round(front_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(front_gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(t_front * 1e6, 3),
+                     "bytes_per_launch": b1, "traffic": traffic_for("q8_gateup_rmsnorm_silu[rows_per_wave=4,waves=16]")},
+        "cpu_baseline": cpu,
+    }
+
+
 def pmc_workload(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
@@ -877,9 +1009,14 @@ def pmc_workload(args, torch, q8, np):
         q8.q8_gemv_silu_mul(torch.from_numpy(qw).cuda(), torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16),
                             torch.from_numpy(synth.gate_up_f32(g, 3584)).cuda(),
                             residual=torch.from_numpy(synth.residual_f32(g, 1024)).cuda())
+        qw, dw = synth.q8_weights(g, 2 * 3584, 1024)
+        w = torch.from_numpy(qw).cuda()
+        dwt = torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16)
+        q8.q8_gateup_silu_quantize(w[:3584], dwt[:3584], w[3584:], dwt[3584:], torch.from_numpy(x).cuda(),
+                                   gamma=torch.from_numpy(gamma).cuda(), eps=NORM_EPS)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_workload": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps, "
-                                      "2 steps of 16 streams, 4 + 4 neighbour-step launches"}), flush=True)
+                                      "2 steps of 16 streams, 4 + 4 + 4 neighbour-step launches"}), flush=True)
 
 
 def main():
@@ -918,6 +1055,8 @@ def main():
         out = run_batch_stack(args, torch, q8, np)
     elif args.workload in ("q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584"):
         out = run_neighbour(args, torch, q8, np)
+    elif args.workload == "q8-mlp-0.8b":
+        out = run_mlp(args, torch, q8, np)
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)

@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_silu_mul_quantize_act.argtypes = [_P, _P, _P, _I64, _P]
     lib.gemv_stacked_rmsnorm.argtypes = [ctypes.POINTER(_Part), ctypes.c_int, _P, _P, ctypes.c_float, _I64, _P]
     lib.q8_gemv_silu_mul.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
+    lib.q8_gateup_silu_quantize.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P]
+    lib.q8_gateup_rmsnorm_silu_quantize.argtypes = [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_float, _I64, _P, _P, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
     lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
@@ -108,7 +110,7 @@ def load_library(path: str = LIB_PATH):
     for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
                "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
-               "q8_gemv_silu_mul"):
+               "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -342,6 +344,37 @@ def q8_gemv_silu_mul(qw, dw, gu, y=None, residual=None, stream=None):
         _ptr(residual, "residual", _F32, (n,), optional=True), _ptr(y, "y", _F32, (n,)), n, k, _stream(stream))
     _check("q8_gemv_silu_mul", st)
     return y
+
+
+def q8_gateup_silu_quantize(w_gate, dw_gate, w_up, dw_up, x, dx=None, gamma=None, eps=None, qa=None, da=None,
+                            stream=None):
+    """Gate+up projection (Q8_0, F rows each) with a = silu(gate) * up quantized in the epilogue:
+    returns (qa int8 [F], da binary16 [F/32]), the down projection's quantized input. x is either
+    int8 codes [K] with dx binary16 scales [K/32], or f32 [K] with gamma f32 [K] and eps (RMS
+    normalization in the prologue)."""
+    if w_gate.dim() != 2 or w_up.shape != w_gate.shape:
+        raise ValueError("w_gate and w_up must both be [F, K]")
+    f, k = w_gate.shape
+    if qa is None:
+        qa = torch.empty(f, dtype=torch.int8, device=w_gate.device)
+    if da is None:
+        da = torch.empty(f // 32, dtype=torch.float16, device=w_gate.device)
+    lib = load_library()
+    common = (_ptr(w_gate, "w_gate", _I8), _ptr(dw_gate, "dw_gate", _H16, (f, k // 32)), _ptr(w_up, "w_up", _I8),
+              _ptr(dw_up, "dw_up", _H16, (f, k // 32)), f)
+    outs = (_ptr(qa, "qa", _I8, (f,)), _ptr(da, "da", _H16, (f // 32,)))
+    if gamma is None:
+        st = lib.q8_gateup_silu_quantize(*common, _ptr(x, "x", _I8, (k,)), _ptr(dx, "dx", _H16, (k // 32,)), k,
+                                         *outs, _stream(stream))
+        fn = "q8_gateup_silu_quantize"
+    else:
+        if eps is None:
+            raise ValueError("eps is required with gamma")
+        st = lib.q8_gateup_rmsnorm_silu_quantize(*common, _ptr(x, "x", _F32, (k,)), _ptr(gamma, "gamma", _F32, (k,)),
+                                                 float(eps), k, *outs, _stream(stream))
+        fn = "q8_gateup_rmsnorm_silu_quantize"
+    _check(fn, st)
+    return qa, da
 
 
 def _q8_parts(parts, k):

@@ -78,11 +78,24 @@ __device__ __forceinline__ double sq4(const float4 &v)
     return (((double)v.x * v.x + (double)v.y * v.y) + (double)v.z * v.z) + (double)v.w * v.w;
 }
 
+// the f64 value of the lane at xor distance M: both halves through the f32
+// exchange (DPP for 1 and 2, swizzle for 4..16, permute for 32), which keeps
+// the LDS crossbar out of distances 1 and 2 and the address VGPRs out of 4..16
+template <int M>
+__device__ __forceinline__ double xchg64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const float lo = xchg<M>(__builtin_bit_cast(float, (uint32_t)u));
+    const float hi = xchg<M>(__builtin_bit_cast(float, (uint32_t)(u >> 32)));
+    return __builtin_bit_cast(double, ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32) |
+                                          __builtin_bit_cast(uint32_t, lo));
+}
+
 __device__ __forceinline__ double block_sum8(double p)
 {
-    p += __shfl_xor(p, 1);
-    p += __shfl_xor(p, 2);
-    p += __shfl_xor(p, 4);
+    p += xchg64<1>(p);
+    p += xchg64<2>(p);
+    p += xchg64<4>(p);
     return p;
 }
 
@@ -91,8 +104,12 @@ __device__ __forceinline__ double blocks_total(const double *s_bss, int64_t nb, 
 {
     double t = 0.0;
     for (int64_t b = lane; b < nb; b += kWave) t += s_bss[b];
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) t += __shfl_xor(t, m);
+    t += xchg64<1>(t);
+    t += xchg64<2>(t);
+    t += xchg64<4>(t);
+    t += xchg64<8>(t);
+    t += xchg64<16>(t);
+    t += xchg64<32>(t);
     return t;
 }
 
@@ -288,12 +305,21 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 // q8_quantize_act) while the weights are in flight. Per row, the arithmetic and
 // its order are the same for all three kinds, so a Q8F32 launch is
 // bit-identical to q8_quantize_act followed by a Q8 launch.
-template <Dt DT, int R, int WAVES>
+//
+// EPI: the gate+up projection with the gated activation and its quantization in
+// the epilogue (parts 0 and 1 are gate and up, F = n_total / 2 rows each).
+// Workgroup b owns gate rows 32b..32b+31 (waves 0..7) and the same up rows
+// (waves 8..15); it writes no f32 output but the 32 codes qa[32b..] and the
+// scale da[b] of a = silu(gate) * up, formed and quantized exactly as
+// q8_silu_mul_quantize_act forms them from the two rows' f32 results.
+template <Dt DT, int R, int WAVES, bool EPI = false>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
                                                             const uint16_t *__restrict__ dx,
                                                             const float *__restrict__ aux, float eps,
-                                                            int64_t K, int64_t n_total)
+                                                            int64_t K, int64_t n_total, int8_t *__restrict__ qa,
+                                                            uint16_t *__restrict__ da)
 {
+    static_assert(!EPI || (R == 4 && WAVES == 16), "the epilogue needs 32 gate and 32 up rows per workgroup");
     constexpr bool FUSED = is_fused(DT);
     constexpr bool TWO = DT == Dt::Q8NORM || DT == Dt::Q8SILU;  // a second f32 input per value
     constexpr int kThreadsPerGroup = WAVES * kWave;
@@ -306,7 +332,9 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     // wave-uniform by construction; readfirstlane lets the compiler keep the
     // row bookkeeping and the part table in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R;
+    const int64_t row0 = !EPI       ? ((int64_t)blockIdx.x * WAVES + wave) * R
+                         : wave < 8 ? 32 * (int64_t)blockIdx.x + R * wave
+                                    : n_total / 2 + 32 * (int64_t)blockIdx.x + R * (wave - 8);
     const bool has_rows = row0 < n_total;  // wave-uniform
     if (!FUSED && !has_rows) return;
 
@@ -401,7 +429,30 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
         compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
         cur = nxt;
     }
-    reduce_and_store<R>(acc, rows, valid, lane);
+    if constexpr (EPI) {
+        // s_gu[0..31]: gate rows 32b.., s_gu[32..63]: up rows 32b..
+        __shared__ __align__(16) float s_gu[64];
+        const float total = wave_reduce_rows<R>(acc, lane);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if (lane == lane_of<R>(i)) s_gu[(wave < 8 ? 0 : 32) + R * (wave & 7) + i] = total;
+        __syncthreads();
+        if (wave == 0) {
+            // every 8-lane group forms the block (quantize4 reduces over the group);
+            // lanes 0..7 write it
+            const int l = lane & 7;
+            const float4 g = *reinterpret_cast<const float4 *>(s_gu + 4 * l);
+            const float4 u = *reinterpret_cast<const float4 *>(s_gu + 32 + 4 * l);
+            float d;
+            const uint32_t packed = quantize4(prologue_value<Dt::Q8SILU>(g, u, 1.0f), &d);
+            if (lane < 8) {
+                *reinterpret_cast<uint32_t *>(qa + 32 * (int64_t)blockIdx.x + 4 * l) = packed;
+                if (lane == 0) da[blockIdx.x] = scale_bits(d);
+            }
+        }
+    } else {
+        reduce_and_store<R>(acc, rows, valid, lane);
+    }
 }
 
 // One 8-lane group per 32-value block; each lane quantizes 4 values.
@@ -481,12 +532,13 @@ struct Input {
     int64_t bytes;
 };
 
-template <Dt DT, int R, int WAVES>
+template <Dt DT, int R, int WAVES, bool EPI = false>
 hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const float *aux, float eps, int64_t K,
-                       int64_t n_total, hipStream_t s)
+                       int64_t n_total, hipStream_t s, int8_t *qa = nullptr, uint16_t *da = nullptr)
 {
     const int64_t rows_per_block = (int64_t)R * WAVES;
-    const int64_t blocks = (n_total + rows_per_block - 1) / rows_per_block;
+    // EPI: one workgroup per 32 gate rows and the matching 32 up rows
+    const int64_t blocks = EPI ? n_total / 64 : (n_total + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     Parts pc = p;
     const void *xc = x;
@@ -494,11 +546,13 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const 
     const float *auxc = aux;
     float epsc = eps;
     int64_t kc = K, nc = n_total;
+    int8_t *qac = qa;
+    uint16_t *dac = da;
     void *args[] = {&pc.w[0],   &pc.w[1],   &pc.w[2],   &pc.w[3],   &pc.dw[0],  &pc.dw[1], &pc.dw[2],
                     &pc.dw[3],  &pc.y[0],   &pc.y[1],   &pc.y[2],   &pc.y[3],   &pc.res[0], &pc.res[1],
                     &pc.res[2], &pc.res[3], &pc.end[0], &pc.end[1], &pc.end[2], &xc,       &dxc,
-                    &auxc,      &epsc,      &kc,        &nc};
-    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES>);
+                    &auxc,      &epsc,      &kc,        &nc,        &qac,       &dac};
+    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES, EPI>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(WAVES * kWave), args, 0, s);
 }
 
@@ -684,6 +738,60 @@ q8g_status run(int dt, const q8g_part *parts, int nparts, const void *x, const u
 
 bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }  // finite, not negative (NaN fails)
 
+// Gate+up projection (F rows each, Q8_0) with silu(gate) * up quantized in the
+// epilogue. kind: Q8G_Q8_0 (x = codes + dx) or kKindNorm (x f32, normalized with
+// gamma and eps in the prologue).
+q8g_status gateup_silu(int kind, const int8_t *qg, const uint16_t *dg, const int8_t *qu, const uint16_t *du, int64_t F,
+                       const void *x, const uint16_t *dx, const float *gamma, float eps, int8_t *qa, uint16_t *da,
+                       int64_t K, void *stream)
+{
+    if (F < 0 || F % 32 || F > kMaxElems / 2 || K < 0 || K % 32 || K > kMaxElems) return Q8G_ERR_SHAPE;
+    if (K > 0 && F > kMaxElems / K) return Q8G_ERR_SHAPE;
+    if (kind == kKindNorm && (K > kMaxFusedK)) return Q8G_ERR_SHAPE;
+    if (kind == kKindNorm && !eps_ok(eps)) return Q8G_ERR_ARG;
+    if (F == 0) return Q8G_OK;
+    if (!qa || !da) return Q8G_ERR_NULL;
+    if (K > 0 && (!qg || !dg || !qu || !du || !x || (kind == Q8G_Q8_0 && !dx) || (kind == kKindNorm && !gamma)))
+        return Q8G_ERR_NULL;
+    if (!aligned(qg, 16) || !aligned(qu, 16) || !aligned(dg, 2) || !aligned(du, 2) || !aligned(x, 16) ||
+        !aligned(qa, 16) || !aligned(da, 2) || (kind == Q8G_Q8_0 && !aligned(dx, 2)) ||
+        (kind == kKindNorm && !aligned(gamma, 16)))
+        return Q8G_ERR_ALIGN;
+    const int64_t wbytes = F * K, dwbytes = F * (K / 32) * 2;
+    const int64_t xbytes = kind == kKindNorm ? 4 * K : K;
+    const int64_t dxbytes = kind == Q8G_Q8_0 ? (K / 32) * 2 : 0;
+    const int64_t gbytes = kind == kKindNorm ? 4 * K : 0;
+    const int64_t qabytes = F, dabytes = (F / 32) * 2;
+    const void *ins[6] = {qg, dg, qu, du, x, kind == Q8G_Q8_0 ? static_cast<const void *>(dx) : gamma};
+    const int64_t inbytes[6] = {wbytes, dwbytes, wbytes, dwbytes, xbytes, kind == Q8G_Q8_0 ? dxbytes : gbytes};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(qa, qabytes, ins[i], inbytes[i]) || overlap(da, dabytes, ins[i], inbytes[i])) return Q8G_ERR_OVERLAP;
+    if (overlap(qa, qabytes, da, dabytes)) return Q8G_ERR_OVERLAP;
+
+    Parts p;
+    for (int i = 0; i < kMaxParts; ++i) {
+        p.w[i] = nullptr;
+        p.dw[i] = nullptr;
+        p.y[i] = nullptr;
+        p.res[i] = nullptr;
+        p.end[i] = INT64_MAX;
+    }
+    p.w[0] = qg;
+    p.dw[0] = dg;
+    p.end[0] = F;
+    p.w[1] = qu;
+    p.dw[1] = du;
+    p.end[1] = 2 * F;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // with K == 0 no activation is read: gate = up = 0, a = 0
+    const hipError_t e =
+        (kind == kKindNorm && K > 0)
+            ? launch_gemv<Dt::Q8NORM, 4, 16, true>(p, x, nullptr, gamma, eps, K, 2 * F, s, qa, da)
+            : launch_gemv<Dt::Q8, 4, 16, true>(p, kind == Q8G_Q8_0 ? x : nullptr, kind == Q8G_Q8_0 ? dx : nullptr,
+                                               nullptr, 0.0f, K, 2 * F, s, qa, da);
+    return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -795,6 +903,20 @@ q8g_status q8_gemv_silu_mul(const int8_t *qw, const uint16_t *dw, const float *g
     if (N < 0) return Q8G_ERR_SHAPE;
     const q8g_part part = {qw, dw, N, y, residual};
     return run(kKindSilu, &part, 1, gu, nullptr, K, stream);
+}
+
+q8g_status q8_gateup_silu_quantize(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
+                                   const uint16_t *dw_up, int64_t F, const int8_t *qx, const uint16_t *dx, int64_t K,
+                                   int8_t *qa, uint16_t *da, void *stream)
+{
+    return gateup_silu(Q8G_Q8_0, qw_gate, dw_gate, qw_up, dw_up, F, qx, dx, nullptr, 0.0f, qa, da, K, stream);
+}
+
+q8g_status q8_gateup_rmsnorm_silu_quantize(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
+                                           const uint16_t *dw_up, int64_t F, const float *x, const float *gamma,
+                                           float eps, int64_t K, int8_t *qa, uint16_t *da, void *stream)
+{
+    return gateup_silu(kKindNorm, qw_gate, dw_gate, qw_up, dw_up, F, x, nullptr, gamma, eps, qa, da, K, stream);
 }
 
 q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows, int *waves)

@@ -180,6 +180,32 @@ q8g_status gemv_stacked_rmsnorm(const q8g_part *parts, int nparts, const float *
 q8g_status q8_gemv_silu_mul(const int8_t *qw, const uint16_t *dw, const float *gu, const float *residual,
                             float *y, int64_t N, int64_t K, void *stream);
 
+/* Gate+up projection with the gated activation and its quantization in the
+ * epilogue ([H] Emitting for a GPU: gate and up computed in one go; [P] Fast
+ * Decode: quantize the activation once, here where it is produced). For F
+ * gate rows and the F matching up rows (Q8_0, K columns each):
+ *   g = W_gate · x, u = W_up · x     (each row exactly as gemv_stacked computes it)
+ *   a = silu(g) * u, quantized       (exactly as q8_silu_mul_quantize_act)
+ * qa int8 [F] and da uint16 [F/32] are the quantized input of the down
+ * projection: bit-identical to gemv_stacked over (gate, up) followed by
+ * q8_silu_mul_quantize_act on [g | u]. No f32 g or u is written.
+ * F % 32 == 0 (one workgroup owns 32 gate and 32 up rows); K % 32 == 0.
+ * qw_* int8 [F][K] and dw_* uint16 [F][K/32] as for q8_gemv (the two may be the
+ * halves of one stacked [2F][K] matrix); qa 16-byte aligned; outputs may not
+ * overlap any input or each other. */
+q8g_status q8_gateup_silu_quantize(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
+                                   const uint16_t *dw_up, int64_t F, const int8_t *qx, const uint16_t *dx,
+                                   int64_t K, int8_t *qa, uint16_t *da, void *stream);
+
+/* The same with RMSnorm(x) * gamma as the input (x, gamma f32 [K], K <= 16384),
+ * normalized and quantized in the prologue exactly as q8_rmsnorm_quantize_act:
+ * the whole MLP front of a decode step (normalize, gate and up, activate,
+ * quantize) in one launch, bit-identical to q8_rmsnorm_quantize_act, then
+ * gemv_stacked, then q8_silu_mul_quantize_act. */
+q8g_status q8_gateup_rmsnorm_silu_quantize(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
+                                           const uint16_t *dw_up, int64_t F, const float *x, const float *gamma,
+                                           float eps, int64_t K, int8_t *qa, uint16_t *da, void *stream);
+
 /* ---- a whole decode step in one launch ------------------------------------
  * "Filling in the blanks: Inference using Phobos", section Fast Decode, lists
  * the launch-level steps of a fast decode pass: replay the pass as one unit,

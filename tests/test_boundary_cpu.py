@@ -47,6 +47,8 @@ def lib():
     L.q8_silu_mul_quantize_act.argtypes = [P, P, P, I64, P]
     L.gemv_stacked_rmsnorm.argtypes = [ctypes.POINTER(Part), ctypes.c_int, P, P, ctypes.c_float, I64, P]
     L.q8_gemv_silu_mul.argtypes = [P, P, P, P, P, I64, I64, P]
+    L.q8_gateup_silu_quantize.argtypes = [P, P, P, P, I64, P, P, I64, P, P, P]
+    L.q8_gateup_rmsnorm_silu_quantize.argtypes = [P, P, P, P, I64, P, P, ctypes.c_float, I64, P, P, P]
     L.q8g_status_str.argtypes = [ctypes.c_int]
     L.q8g_status_str.restype = ctypes.c_char_p
     L.q8g_probe_read.argtypes = [P, I64, P, P]
@@ -58,7 +60,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     for expected in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
                      "q8g_status_str", "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act",
-                     "gemv_stacked_rmsnorm", "q8_gemv_silu_mul", "q8g_probe_read", "q8g_flush"):
+                     "gemv_stacked_rmsnorm", "q8_gemv_silu_mul", "q8_gateup_silu_quantize",
+                     "q8_gateup_rmsnorm_silu_quantize", "q8g_probe_read", "q8g_flush"):
         assert expected in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -241,6 +244,32 @@ def test_fused_neighbour_gemv_validation(lib):
     assert g(W, DW, None, None, Y, 8, 64, None) == ERR_NULL
     assert g(W, DW, X + 4, None, Y, 8, 64, None) == ERR_ALIGN
     assert g(W, DW, X, None, X + 4 * 64, 8, 64, None) == ERR_OVERLAP  # y in the up half
+
+
+def test_gateup_epilogue_validation(lib):
+    g = lib.q8_gateup_silu_quantize
+    WU, DU = W + 0x1000000, DW + 0x1000000
+    QA, DA = Y, Y + 0x100000
+    assert g(W, DW, WU, DU, 48, QX, DX, 64, QA, DA, None) == ERR_SHAPE  # F % 32
+    assert g(W, DW, WU, DU, 64, QX, DX, 48, QA, DA, None) == ERR_SHAPE  # K % 32
+    assert g(W, DW, WU, DU, -32, QX, DX, 64, QA, DA, None) == ERR_SHAPE
+    assert g(None, None, None, None, 0, None, None, 64, None, None, None) == OK  # F == 0
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, None, DA, None) == ERR_NULL
+    assert g(W, DW, None, DU, 64, QX, DX, 64, QA, DA, None) == ERR_NULL
+    assert g(W, DW, WU, DU, 64, QX, None, 64, QA, DA, None) == ERR_NULL
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, QA + 4, DA, None) == ERR_ALIGN
+    assert g(W, DW, WU + 8, DU, 64, QX, DX, 64, QA, DA, None) == ERR_ALIGN
+    assert g(W, DW, WU, DU + 1, 64, QX, DX, 64, QA, DA, None) == ERR_ALIGN
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, WU + 64, DA, None) == ERR_OVERLAP  # codes in the up weights
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, QA, DX, None) == ERR_OVERLAP
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, QA, QA + 32, None) == ERR_OVERLAP
+    n = lib.q8_gateup_rmsnorm_silu_quantize
+    G = R
+    assert n(W, DW, WU, DU, 64, X, G, 1e-6, 16384 + 32, QA, DA, None) == ERR_SHAPE
+    assert n(W, DW, WU, DU, 64, X, G, -1.0, 64, QA, DA, None) == ERR_ARG
+    assert n(W, DW, WU, DU, 64, X, None, 1e-6, 64, QA, DA, None) == ERR_NULL
+    assert n(W, DW, WU, DU, 64, X, G + 4, 1e-6, 64, QA, DA, None) == ERR_ALIGN
+    assert n(W, DW, WU, DU, 64, X, G, 1e-6, 64, G + 64, DA, None) == ERR_OVERLAP  # codes in gamma
 
 
 def test_probe_validation(lib):

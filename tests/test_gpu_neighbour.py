@@ -218,3 +218,114 @@ def test_rejections(q8):
     with pytest.raises(q8.Q8GemvError) as e:
         q8.q8_rmsnorm_quantize_act(xs, xs.clone(), -1.0)
     assert e.value.status == 4
+
+
+# --------------------------------------------------------------------------- gate+up with the activation in its epilogue
+
+
+EPI_SHAPES = [(32, 32), (64, 96), (3584, 1024), (9216, 2560), (4096 + 32, 1024 + 32), (96, 16384), (32, 40960)]
+
+
+def gateup_case(f, k, j):
+    g = synth.rng_for(synth.TAG_NEIGHBOUR, 4000 + j)
+    qw, dw = synth.q8_weights(g, 2 * f, k)  # one stacked [2F][K] matrix: gate rows, then up rows
+    return g, qw, dw
+
+
+def check_epilogue(q8, orc, qa, da, W, DW, qw, dw, rq, rd, f, what):
+    """qa/da == the two-launch path (gemv_stacked over gate and up, then silu*up quantize), and
+    == the oracle's silu*up + quantizer applied to those f32 gate/up results; gate/up within
+    1e-5 * S of the oracle."""
+    yg, yu = q8.gemv_stacked([{"w": W[:f], "dw": DW[:f]}, {"w": W[f:], "dw": DW[f:]}], dev(rq), h16(rd))
+    gu = np.concatenate([host(yg), host(yu)])
+    q2, d2 = q8.q8_silu_mul_quantize_act(dev(gu))
+    gq, gd = host(qa), bits(da)
+    assert np.array_equal(gq, host(q2)), f"{what}: {np.count_nonzero(gq != host(q2))} codes differ from two launches"
+    assert np.array_equal(gd, bits(d2)), f"{what}: scales differ from two launches"
+    oq, od = orc.quantize_act(orc.silu_mul(gu))
+    assert np.array_equal(gq, oq) and np.array_equal(gd, od), f"{what}: differs from the oracle's silu*up + quantize"
+    yr, S = orc.q8_gemv(qw, dw, rq, rd)
+    within(gu, yr, S, f"{what} gate/up")
+
+
+@pytest.mark.parametrize("f,k", EPI_SHAPES)
+def test_gateup_epilogue_codes_input(q8, orc, f, k):
+    print_case("gate+up silu epilogue, codes in", f, k)
+    g, qw, dw = gateup_case(f, k, f + k)
+    x = synth.activation_f32(g, k)
+    W, DW = dev(qw), h16(dw)
+    qx, dx = q8.q8_quantize_act(dev(x))
+    rq, rd = orc.quantize_act(x)
+    assert np.array_equal(host(qx), rq)
+    qa, da = q8.q8_gateup_silu_quantize(W[:f], DW[:f], W[f:], DW[f:], qx, dx)
+    check_epilogue(q8, orc, qa, da, W, DW, qw, dw, rq, rd, f, f"codes {f}x{k}")
+
+
+@pytest.mark.parametrize("f,k", [s for s in EPI_SHAPES if s[1] <= 16384])
+def test_gateup_epilogue_rmsnorm_input(q8, orc, f, k):
+    """The whole MLP front in one launch: normalize, gate and up, silu*up, quantize."""
+    print_case("gate+up silu epilogue, rmsnorm in", f, k)
+    g, qw, dw = gateup_case(f, k, 7 * f + k)
+    x, gamma = synth.activation_f32(g, k), synth.norm_gamma(g, k)
+    W, DW = dev(qw), h16(dw)
+    qa, da = q8.q8_gateup_silu_quantize(W[:f], DW[:f], W[f:], DW[f:], dev(x), gamma=dev(gamma), eps=EPS)
+    qx, dx = q8.q8_rmsnorm_quantize_act(dev(x), dev(gamma), EPS)
+    rq, rd = orc.quantize_act(orc.rmsnorm(x, gamma, EPS))
+    assert np.array_equal(host(qx), rq) and np.array_equal(bits(dx), rd)
+    check_epilogue(q8, orc, qa, da, W, DW, qw, dw, rq, rd, f, f"rmsnorm {f}x{k}")
+
+
+def test_gateup_epilogue_separate_matrices_and_mlp_chain(q8, orc):
+    """Gate and up as two allocations; the chain epilogue -> down projection with the residual
+    equals the prologue-fused chain and the four-launch chain bit for bit."""
+    print_case("mlp chains")
+    f, k = 3584, 1024
+    g = synth.rng_for(synth.TAG_NEIGHBOUR, 4999)
+    qg, dg = synth.q8_weights(g, f, k)
+    qu, du = synth.q8_weights(g, f, k)
+    qd, dd = synth.q8_weights(g, k, f)
+    x, gamma, r = synth.activation_f32(g, k), synth.norm_gamma(g, k), synth.residual_f32(g, k)
+    Wg, Dg, Wu, Du, Wd, Dd = dev(qg), h16(dg), dev(qu), h16(du), dev(qd), h16(dd)
+    X, G, Rr = dev(x), dev(gamma), dev(r)
+    qa, da = q8.q8_gateup_silu_quantize(Wg, Dg, Wu, Du, X, gamma=G, eps=EPS)
+    y_epi = host(q8.q8_gemv(Wd, Dd, qa, da, residual=Rr))
+    yg, yu = q8.gemv_stacked_rmsnorm([{"w": Wg, "dw": Dg}, {"w": Wu, "dw": Du}], X, G, EPS)
+    import torch
+
+    gu = torch.cat([yg, yu])
+    y_pro = host(q8.q8_gemv_silu_mul(Wd, Dd, gu, residual=Rr))
+    qx, dx = q8.q8_rmsnorm_quantize_act(X, G, EPS)
+    yg2, yu2 = q8.gemv_stacked([{"w": Wg, "dw": Dg}, {"w": Wu, "dw": Du}], qx, dx)
+    qa2, da2 = q8.q8_silu_mul_quantize_act(torch.cat([yg2, yu2]))
+    y_four = host(q8.q8_gemv(Wd, Dd, qa2, da2, residual=Rr))
+    assert np.array_equal(y_epi, y_pro) and np.array_equal(y_epi, y_four)
+    rq, rd = orc.quantize_act(orc.silu_mul(host(gu)))
+    yr, S = orc.q8_gemv(qd, dd, rq, rd, r)
+    within(y_epi, yr, S, "mlp chain")
+
+
+def test_gateup_epilogue_k0_and_guards(q8):
+    import torch
+
+    print_case("gate+up epilogue K=0 and guards")
+    f = 64
+    w = torch.empty((f, 0), dtype=torch.int8, device="cuda")
+    dw = torch.empty((f, 0), dtype=torch.float16, device="cuda")
+    qa = torch.full((f + 64,), 5, dtype=torch.int8, device="cuda")
+    da = torch.full((f // 32 + 8,), 1.0, dtype=torch.float16, device="cuda")
+    q8.q8_gateup_silu_quantize(w, dw, w, dw, torch.empty(0, dtype=torch.int8, device="cuda"),
+                               torch.empty(0, dtype=torch.float16, device="cuda"), qa=qa[:f], da=da[:f // 32])
+    assert (host(qa[:f]) == 0).all() and (bits(da[:f // 32]) == 0).all()
+    assert (host(qa[f:]) == 5).all() and (host(da[f // 32:]) == 1.0).all()
+    k = 1024
+    g, qw, dwn = gateup_case(f, k, 77)
+    W, DW = dev(qw), h16(dwn)
+    x = dev(synth.activation_f32(g, k))
+    qa = torch.full((f + 64,), 5, dtype=torch.int8, device="cuda")
+    da = torch.full((f // 32 + 8,), 1.0, dtype=torch.float16, device="cuda")
+    q8.q8_gateup_silu_quantize(W[:f], DW[:f], W[f:], DW[f:], x, gamma=dev(synth.norm_gamma(g, k)), eps=EPS,
+                               qa=qa[:f], da=da[:f // 32])
+    assert (host(qa[f:]) == 5).all() and (host(da[f // 32:]) == 1.0).all()
+    with pytest.raises(q8.Q8GemvError) as e:
+        q8.q8_gateup_silu_quantize(W[:48], DW[:48], W[f:f + 48], DW[f:f + 48], x, gamma=x.clone(), eps=EPS)
+    assert e.value.status == 2
