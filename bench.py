@@ -30,6 +30,11 @@ Other workloads (per-call figures; a step is one call):
                         the residual) as two launches: gate+up with the normalization in its prologue
                         and silu*up quantized in its epilogue, then the Q8_0 down projection; also the
                         prologue-fused and the four-launch chains (all three bit-identical)
+  q8-layers-0.8b        the 24 decode layers of the 0.8B shape with their neighbour steps and the real
+                        data flow through the residual stream (attention output a seeded stand-in):
+                        per layer QKV with its normalization, out (+residual), gate+up with silu*up
+                        quantized in its epilogue, down (+residual); then final norm and head. 98
+                        launches per token fused, 194 unfused (timed too; both bit-identical)
 
 Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
 then K timed steps between two synchronizations, measured with HIP events on the
@@ -52,7 +57,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
 WORKLOADS = ["q8-stack-0.8b", "q8-stack-0.8b-b16", "q8-gateup-7168x1024", "q8-head-151936x1024-b16",
              "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120",
-             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584", "q8-mlp-0.8b"]
+             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584", "q8-mlp-0.8b", "q8-layers-0.8b"]
 NORM_EPS = 1e-6  # RMS-normalization epsilon of the neighbour-step workloads
 BATCH = 16  # decode streams of the -b16 workloads
 
@@ -969,6 +974,134 @@ def run_mlp(args, torch, q8, np):
     }
 
 
+def run_layers(args, torch, q8, np):
+    """The 0.8B decode layers with their neighbour steps (Q8LayerChain), fused and unfused."""
+    import oracle
+    import synth
+    from block_quantized_weight_q8_amd.layers import Q8LayerChain
+    from block_quantized_weight_q8_amd.stack import Q8DecodeStack
+
+    orc = oracle.get()
+    t0 = time.time()
+    ops = synth.q8_stack_08b()
+    host = synth.q8_stack_inputs(ops)
+    inputs = synth.layer_chain_inputs()
+    chain = Q8LayerChain(Q8DecodeStack(ops, host), inputs, eps=NORM_EPS)
+    log(f"[bench] generated {len(ops)} projections and the layer inputs in {time.time() - t0:.1f}s")
+    step_bytes = synth.q8_layers_08b_bytes()
+    # parity: fused == unfused bit for bit; every step of sampled layers against the oracle
+    tf, tu = [], []
+    chain.step(fused=True, trace=tf)
+    chain.step(fused=False, trace=tu)
+    tf = {(n, l): t.numpy() for n, l, t in tf}
+    tu = {(n, l): t.numpy() for n, l, t in tu}
+    for key in tf:
+        if not np.array_equal(tf[key], tu[key]):
+            raise SystemExit(f"parity: fused and unfused layer chains differ at {key}")
+    k, f = chain.hidden, chain.ffn
+    worst = 0.0
+
+    def rel(y, yr, S):
+        return float(np.max(np.abs(np.asarray(y, np.float64) - yr) / S))
+
+    for l in (0, chain.layers // 2, chain.layers - 1):
+        qkv, out, gu, down = (host[4 * l + j] for j in range(4))
+        h_in, h_mid, g = tu[("h_in", l)], tu[("h_mid", l)], tu[("gu", l)]
+        rq, rd = orc.quantize_act(orc.rmsnorm(h_in, inputs["gamma_attn"][l], NORM_EPS))
+        cb = tu[("qkv_codes", l)]
+        if not (np.array_equal(cb[:k].view(np.int8), rq) and np.array_equal(cb[k:].view(np.uint16), rd)):
+            raise SystemExit(f"parity: layer {l} normalized codes differ from the oracle")
+        worst = max(worst, rel(tu[("qkv", l)], *orc.q8_gemv(qkv["qw"], qkv["dw"], rq, rd)))
+        worst = max(worst, rel(h_mid, *orc.q8_gemv(out["qw"], out["dw"], *orc.quantize_act(inputs["attn"][l]), h_in)))
+        mq, md = orc.quantize_act(orc.rmsnorm(h_mid, inputs["gamma_mlp"][l], NORM_EPS))
+        worst = max(worst, rel(g, *orc.q8_gemv(gu["qw"], gu["dw"], mq, md)))
+        aq, ad = orc.quantize_act(orc.silu_mul(g))
+        cb = tu[("a_codes", l)]
+        if not (np.array_equal(cb[:f].view(np.int8), aq) and np.array_equal(cb[f:].view(np.uint16), ad)):
+            raise SystemExit(f"parity: layer {l} activation codes differ from the oracle")
+        h_next = tu[("h_in", l + 1)] if l + 1 < chain.layers else tu[("h_out", l)]
+        worst = max(worst, rel(h_next, *orc.q8_gemv(down["qw"], down["dw"], aq, ad, h_mid)))
+    fq, fd = orc.quantize_act(orc.rmsnorm(tu[("h_out", chain.layers - 1)], inputs["gamma_final"], NORM_EPS))
+    rows = np.unique(np.concatenate([[0, ops[-1].n - 1], np.random.default_rng(7).integers(0, ops[-1].n, 512)]))
+    worst = max(worst, rel(tu[("logits", chain.layers)][rows], *orc.q8_gemv(host[-1]["qw"][rows], host[-1]["dw"][rows], fq, fd)))
+    if worst > 1e-5:
+        raise SystemExit(f"parity: layer chain off by {worst:.2e} * S")
+    log(f"[bench] parity: fused == unfused bit for bit; layers 0, {chain.layers // 2}, {chain.layers - 1} and the "
+        f"head against the oracle step by step: codes exact, worst |err|/S = {worst:.2e}")
+    probe = probe_gbps(q8, torch)
+    t_fused = graph_seconds(torch, lambda: chain.step(fused=True), args.steps, args.warmup)
+    t_unfused = graph_seconds(torch, lambda: chain.step(fused=False), args.steps, args.warmup)
+    log(f"[bench] layer chain: fused {t_fused * 1e6:.1f} us/token ({chain.launches_per_token(True)} launches), "
+        f"unfused {t_unfused * 1e6:.1f} us/token ({chain.launches_per_token(False)} launches)")
+    # per-kernel groups of the fused step, each replayed alone over its launches of one token
+    L = chain.layers
+    groups = {
+        "q8_rmsnorm_gemv[rows_per_wave=2,waves=8] (QKV)": (
+            lambda: [q8.gemv_stacked_rmsnorm(chain.qkv_parts(l), chain.h, chain.gamma_attn[l], NORM_EPS)
+                     for l in range(L)], synth.q8_rmsnorm_gemv_bytes(4096, k)),
+        "gemv_kernel<Q8F32, rows_per_wave=1, waves=8> (out)": (
+            lambda: [q8.gemv_stacked(chain.out_parts(l, chain.h), chain.attn[l]) for l in range(L)],
+            synth.q8_gemv_f32x_bytes(k, 2048, residual=True)),
+        "q8_gateup_rmsnorm_silu[rows_per_wave=4,waves=16] (gate+up)": (
+            lambda: [q8.q8_gateup_silu_quantize(*chain.gate_up(l), chain.h, gamma=chain.gamma_mlp[l], eps=NORM_EPS,
+                                                qa=chain.qa, da=chain.da) for l in range(L)],
+            synth.q8_gateup_epilogue_bytes(f, k)),
+        "gemv_kernel<Q8, rows_per_wave=1, waves=4> (down)": (
+            lambda: [q8.q8_gemv(chain._b(l, 3)["qw"], chain._b(l, 3)["dw"], chain.qa, chain.da, y=chain.h,
+                                residual=chain.h) for l in range(L)], synth.q8_gemv_bytes(k, f, residual=True)),
+    }
+    per = {}
+    for name, (fn, b) in groups.items():
+        tg = graph_seconds(torch, fn, max(5, args.steps // 2), 2) / L
+        per[name] = (tg, b)
+        log(f"[bench] {name}: {L} launches/token, {tg * 1e6:.2f} us each, {b / tg / 1e9:.0f} GB/s")
+    dom = max(per, key=lambda n: per[n][0])
+    tg, b = per[dom]
+    kname = dom.split(" (")[0]
+    cpu = None
+    if not args.no_cpu_baseline:
+        nth = cpu_threads()
+        toks, c0 = 0, time.perf_counter()
+        while True:
+            h = inputs["h"].astype(np.float32)
+            for l in range(chain.layers):
+                qkv, out, gu, down = (host[4 * l + j] for j in range(4))
+                orc.q8_gemv(qkv["qw"], qkv["dw"], *orc.quantize_act(orc.rmsnorm(h, inputs["gamma_attn"][l], NORM_EPS)),
+                            nthreads=nth)
+                h = orc.q8_gemv(out["qw"], out["dw"], *orc.quantize_act(inputs["attn"][l]), h, nthreads=nth)[0]
+                h = h.astype(np.float32)
+                g = orc.q8_gemv(gu["qw"], gu["dw"], *orc.quantize_act(orc.rmsnorm(h, inputs["gamma_mlp"][l], NORM_EPS)),
+                                nthreads=nth)[0].astype(np.float32)
+                h = orc.q8_gemv(down["qw"], down["dw"], *orc.quantize_act(orc.silu_mul(g)), h,
+                                nthreads=nth)[0].astype(np.float32)
+            orc.q8_gemv(host[-1]["qw"], host[-1]["dw"], *orc.quantize_act(orc.rmsnorm(h, inputs["gamma_final"], NORM_EPS)),
+                        nthreads=nth)
+            toks += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
+        dt_ = time.perf_counter() - c0
+        cpu = {"value": round(toks * step_bytes / dt_ / 1e9, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+               "sample": f"{toks} whole tokens of the 24-layer chain and head, {toks * step_bytes} algorithmic bytes "
+                         f"in {dt_:.1f} s", "tok_per_s": round(toks / dt_, 2), "cpu": cpu_model()}
+        log(f"[bench] oracle on {nth} host threads: {cpu['value']} GB/s, {cpu['tok_per_s']} tok/s")
+    value = step_bytes / t_fused / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_fused * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "q8-layers-0.8b", "layers": chain.layers, "hidden": k, "ffn": f, "vocab": ops[-1].n,
+                   "launches_per_token": chain.launches_per_token(True), "bytes_per_step": step_bytes,
+                   "attention": "not part of this path: a seeded f32 stand-in per layer feeds the out projection"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2), "tok_per_s": round(1 / t_fused, 1),
+        "probe_GBps": round(probe, 1),
+        "modes_ms_per_step": {"fused_graph": round(t_fused * 1e3, 4), "unfused_graph": round(t_unfused * 1e3, 4)},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(b / tg / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(b / tg / 1e9 / HBM_PEAK_GBPS, 4), "avg_launch_us": round(tg * 1e6, 3),
+                     "bytes_per_launch": b, "launches_per_step": L, "traffic": traffic_for(kname)},
+        "cpu_baseline": cpu,
+    }
+
+
 def pmc_workload(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
@@ -1057,6 +1190,8 @@ def main():
         out = run_neighbour(args, torch, q8, np)
     elif args.workload == "q8-mlp-0.8b":
         out = run_mlp(args, torch, q8, np)
+    elif args.workload == "q8-layers-0.8b":
+        out = run_layers(args, torch, q8, np)
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)

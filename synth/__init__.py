@@ -42,6 +42,7 @@ TAG_Q8_HEAD = 4
 TAG_F16_GATEUP = 5
 TAG_Q8_BATCH = 6
 TAG_NEIGHBOUR = 7
+TAG_LAYERS = 8
 TAG_TEST = 100
 
 
@@ -150,6 +151,20 @@ def q8_stack_08b(layers: int = 24, hidden: int = 1024, vocab: int = 151936):
     return ops
 
 
+def layer_chain_inputs(layers: int = 24, hidden: int = 1024, attn_width: int = 2048, tag: int = TAG_LAYERS):
+    """Seeded inputs of the decode-layer chain: the residual stream entering layer 0, per layer
+    the two normalization weight vectors and the attention output (a stand-in: attention is not
+    part of this path), and the final normalization's weights."""
+    g = rng_for(tag, 0)
+    out = {"h": activation_f32(g, hidden), "gamma_attn": [], "gamma_mlp": [], "attn": []}
+    for _ in range(layers):
+        out["gamma_attn"].append(norm_gamma(g, hidden))
+        out["gamma_mlp"].append(norm_gamma(g, hidden))
+        out["attn"].append(activation_f32(g, attn_width))
+    out["gamma_final"] = norm_gamma(g, hidden)
+    return out
+
+
 def q8_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
     """Algorithmic HBM bytes of one Q8_0 GEMV: codes + scales + quantized activation + f32 out (+ residual)."""
     b = n * k + n * (k // QBLOCK) * 2 + k + (k // QBLOCK) * 2 + n * 4
@@ -180,6 +195,24 @@ def q8_silu_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
     """Algorithmic bytes of a Q8_0 GEMV that forms silu(gate) * up from f32 [2k] in the
     same launch: q8_gemv_f32x_bytes plus the second f32 half."""
     return q8_gemv_f32x_bytes(n, k, residual) + 4 * k
+
+
+def q8_gateup_epilogue_bytes(f: int, k: int) -> int:
+    """Algorithmic bytes of the gate+up launch with the normalization in its prologue and
+    silu(gate) * up quantized in its epilogue: both weight planes of 2f rows, x and gamma
+    f32 [k], codes [f] and binary16 scales [f/32] out."""
+    return 2 * f * k + 2 * (2 * f) * (k // QBLOCK) + 8 * k + f + 2 * (f // QBLOCK)
+
+
+def q8_layers_08b_bytes(layers: int = 24, hidden: int = 1024, ffn: int = 3584, vocab: int = 151936) -> int:
+    """Algorithmic bytes of one token of the fused decode-layer chain: per layer the QKV launch
+    with its normalization, the out projection (f32 input, residual), the gate+up launch with
+    its epilogue and the down projection (codes input, residual); then the final normalization
+    with quantize and the head."""
+    per_layer = (q8_rmsnorm_gemv_bytes(4096, hidden) + q8_gemv_f32x_bytes(hidden, 2048, residual=True)
+                 + q8_gateup_epilogue_bytes(ffn, hidden) + q8_gemv_bytes(hidden, ffn, residual=True))
+    head = 8 * hidden + hidden + 2 * (hidden // QBLOCK) + q8_gemv_bytes(vocab, hidden)
+    return layers * per_layer + head
 
 
 def q8_quantize_bytes(k: int) -> int:
