@@ -438,15 +438,22 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
             if (lane == lane_of<R>(i)) s_gu[(wave < 8 ? 0 : 32) + R * (wave & 7) + i] = total;
         __syncthreads();
         if (wave == 0) {
-            // every 8-lane group forms the block (quantize4 reduces over the group);
-            // lanes 0..7 write it
-            const int l = lane & 7;
-            const float4 g = *reinterpret_cast<const float4 *>(s_gu + 4 * l);
-            const float4 u = *reinterpret_cast<const float4 *>(s_gu + 32 + 4 * l);
-            float d;
-            const uint32_t packed = quantize4(prologue_value<Dt::Q8SILU>(g, u, 1.0f), &d);
-            if (lane < 8) {
-                *reinterpret_cast<uint32_t *>(qa + 32 * (int64_t)blockIdx.x + 4 * l) = packed;
+            // one value per lane (lanes 32..63 repeat 0..31): a = silu(gate) * up, then
+            // the block's quantization with quantize4's arithmetic (max |a| over the
+            // 32 lanes, d = fl32(max / 127), q = rint(fl32(a / d)))
+            const int j = lane & 31;
+            const float a = silu_mul(s_gu[j], s_gu[32 + j]);
+            float m = fabsf(a);
+            m = fmaxf(m, xchg<1>(m));
+            m = fmaxf(m, xchg<2>(m));
+            m = fmaxf(m, xchg<4>(m));
+            m = fmaxf(m, xchg<8>(m));
+            m = fmaxf(m, xchg<16>(m));
+            const float d = m / 127.0f;
+            float q = 0.0f;
+            if (d != 0.0f) q = fminf(fmaxf(__builtin_rintf(a / d), -127.0f), 127.0f);
+            if (lane < 32) {
+                qa[32 * (int64_t)blockIdx.x + j] = (int8_t)(int)q;
                 if (lane == 0) da[blockIdx.x] = scale_bits(d);
             }
         }
