@@ -1,0 +1,215 @@
+"""CPU models of the kernels' address arithmetic (no GPU).
+
+Each model repeats, in Python, the index expressions a kernel uses for its global
+loads, its stores and its LDS slots, for every workgroup, wave and lane of a launch,
+and checks that every access stays inside its buffer and that every LDS slot a lane
+reads was written with the data it expects. The launch-shape constants are read from
+the HIP sources, so a change there is checked here. A model that disagrees with its
+kernel is a bug in one of them: both are written from the same description in the
+kernel's comments.
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "block_quantized_weight_q8_amd", "csrc")
+K_BATCH_MAX, K_STEP_K, K_TILE_ROWS = 16, 64, 16
+
+
+def batch_shapes():
+    src = open(os.path.join(CSRC, "batch.hip")).read()
+    shapes = {}
+    for name in ("WideSplitShape", "SplitShape", "WholeShape"):
+        m = re.search(rf"using {name} = Shape<(\d+), (\d+), (\d+), (\d+)>;", src)
+        assert m, name
+        shapes[name] = tuple(int(v) for v in m.groups())
+    wide = int(re.search(r"kWideSplitTiles = (\d+);", src).group(1))
+    split = int(re.search(r"kSplitTiles = (\d+);", src).group(1))
+    max_k = re.search(r"kMaxK = ([^;]+);", src)
+    return shapes, wide, split, max_k
+
+
+SHAPES, WIDE_TILES, SPLIT_TILES, _ = batch_shapes()
+
+
+def shape_for(n):
+    tiles = (n + K_TILE_ROWS - 1) // K_TILE_ROWS
+    if tiles <= WIDE_TILES:
+        return SHAPES["WideSplitShape"]
+    return SHAPES["SplitShape"] if tiles <= SPLIT_TILES else SHAPES["WholeShape"]
+
+
+def batch_staging(N, K, B, W, S, TK):
+    """The staged activation: codes swizzled per vector, scales [block][vector], and each
+    wave's weight scales; every read slot holds what the consuming lane expects."""
+    nb = K // 32
+    codes_area = K_BATCH_MAX * TK
+    dx_area = (TK // 32) * K_BATCH_MAX * 4
+    wsc_tile = K_TILE_ROWS * (TK // 32) * 4
+    k0 = 0
+    while k0 < K:
+        kt = min(K - k0, TK)
+        nbt, cpv = kt // 32, kt // 16
+        rowc16 = (cpv + 15) & ~15
+        steps = (kt + K_STEP_K - 1) // K_STEP_K
+        written = {}
+        for p in range(B * rowc16):
+            b = p // rowc16
+            c = (p - b * rowc16) ^ (b & 15)
+            bb, cc = min(b, B - 1), (c if c < cpv else 0)
+            src = bb * K + k0 + 16 * cc
+            assert 0 <= src and src + 16 <= B * K
+            assert 16 * p + 16 <= codes_area
+            written[p] = (bb, cc)
+        for t in range(nbt * K_BATCH_MAX):
+            blk, b = divmod(t, K_BATCH_MAX)
+            assert min(b, B - 1) * nb + k0 // 32 + blk < B * nb
+            assert 4 * t + 4 <= dx_area
+        for st in range(steps):
+            hi = st * K_STEP_K + 32 < kt
+            assert 2 * st < nbt and (not hi or 2 * st + 1 < nbt)
+            for j in range(16):
+                for q in range(4):
+                    if j < B and (q < 2 or hi):
+                        c = 4 * st + q
+                        assert c < cpv
+                        assert written[j * rowc16 + (c ^ j)] == (j, c)
+        for split in range(S):
+            sb, se = steps * split // S, steps * (split + 1) // S
+            nbw = 2 * (se - sb)
+            assert K_TILE_ROWS * 4 * 2 * sb + 4 * K_TILE_ROWS * nbw <= wsc_tile
+            blk0 = k0 // 32 + 2 * sb
+            for t in range(K_TILE_ROWS * nbw):
+                bo = t % nbw
+                assert (blk0 + bo if blk0 + bo < nb else blk0) < nb
+        k0 += TK
+
+
+def batch_rows(N, K, B, W, S):
+    """Weight rows as a wave-uniform base plus a 32-bit lane offset, clamped for rows past N
+    (including a tile wholly past N); outputs [B][N]."""
+    nb = K // 32
+    tiles = (N + K_TILE_ROWS - 1) // K_TILE_ROWS
+    tpg = W // S
+    groups = (tiles + tpg - 1) // tpg
+    for g in range(groups):
+        for wave in range(W):
+            tile = wave // S
+            row0 = (g * tpg + tile) * K_TILE_ROWS
+            rbase = row0 if row0 < N else N - 1
+            for j in range(16):
+                row = row0 + j
+                jr = (row if row < N else N - 1) - rbase
+                assert 0 <= jr < 16
+                assert jr * K < 2**32
+                if K:
+                    assert rbase * K + jr * K + K <= N * K
+                    assert rbase * nb + jr * nb + nb <= N * nb
+                for b in range(16):
+                    if row < N and b < B:
+                        assert b * N + row < B * N
+
+
+BATCH_CASES = [(16, 64, 1), (17, 96, 3), (100, 1024, 16), (1024, 2048, 8), (300, 3584, 5), (33, 5120, 16),
+               (4111, 160, 2), (7168, 1024, 16), (1030, 2048, 6), (1, 96, 1), (15, 96, 16), (4097, 96, 16),
+               (40001, 96, 5), (64, 2080, 7), (64, 4128, 16), (32785, 64, 16), (1, 64, 16), (1024, 3584, 16)]
+
+
+@pytest.mark.parametrize("n,k,b", BATCH_CASES)
+def test_batch_kernel_addressing(n, k, b):
+    W, S, P, TK = shape_for(n)
+    batch_rows(n, k, b, W, S)
+    # staging is independent of N: check every shape on this K and B
+    for W_, S_, P_, TK_ in SHAPES.values():
+        batch_staging(n, k, b, W_, S_, TK_)
+
+
+def test_batch_shape_constants_are_consistent():
+    for W, S, P, TK in SHAPES.values():
+        assert W % S == 0 and 1 <= W <= 16
+        assert TK % K_STEP_K == 0 and (TK // 16) % 16 == 0
+        lds = 16 + (TK // 32) * K_BATCH_MAX * 4 + K_BATCH_MAX * TK + (W // S) * K_TILE_ROWS * (TK // 32) * 4
+        assert lds <= 160 * 1024
+        assert W * 64 * 4 * 4 <= K_BATCH_MAX * TK  # split partial sums fit the code area
+
+
+# --------------------------------------------------------------------------- gemv_kernel
+
+
+def gateup_epilogue(F, K):
+    """Workgroup b owns gate rows 32b..32b+31 (waves 0..7, 4 rows each) and the same up rows
+    (waves 8..15); the stacked row space is [gate (F) | up (F)]; LDS s_gu[64]; outputs
+    qa[32b + j] and da[b]."""
+    n_total = 2 * F
+    seen = set()
+    for blk in range(F // 32):
+        gu_slots = set()
+        for wave in range(16):
+            row0 = 32 * blk + 4 * wave if wave < 8 else n_total // 2 + 32 * blk + 4 * (wave - 8)
+            for i in range(4):
+                g = row0 + i
+                assert g < n_total
+                part, local = (0, g) if g < F else (1, g - F)
+                assert 0 <= local < F
+                assert local * K + K <= F * K  # the row's bytes within its part
+                seen.add(g)
+                slot = (0 if wave < 8 else 32) + 4 * (wave & 7) + i
+                assert 0 <= slot < 64
+                gu_slots.add(slot)
+                # gate row j pairs with up row j in the same slot offset
+                assert slot % 32 == local % 32 and local // 32 == blk
+        assert gu_slots == set(range(64))
+        for lane in range(64):
+            j = lane & 31
+            if lane < 32:
+                assert 32 * blk + j < F
+        assert blk < F // 32
+    assert seen == set(range(n_total))
+
+
+@pytest.mark.parametrize("f,k", [(32, 32), (64, 96), (3584, 1024), (96, 16384), (4096 + 32, 64)])
+def test_gateup_epilogue_addressing(f, k):
+    gateup_epilogue(f, k)
+
+
+def fused_prologue_loads(K, threads, passes, two):
+    """Every lane loads x (and the second input: gamma, or the up half of [gate | up]) at
+    e < K ? e : K - 4, so with K >= 32 all loads are in bounds and the values used are
+    exactly those with e < K; block sums and codes go to LDS index e >> 5 < K / 32."""
+    assert K >= 32 and K % 32 == 0
+    xlen = 2 * K if two == "silu" else K
+    used = set()
+    for t in range(threads):
+        for p in range(passes):
+            e = 4 * t + p * 4 * threads
+            ec = e if e < K else K - 4
+            assert 0 <= ec and ec + 4 <= K
+            if two == "silu":
+                assert K + ec + 4 <= xlen
+            if e - (t & 7) * 4 < K:  # the 8-lane group of the block is in range
+                assert e < K
+                assert (e >> 5) < K // 32
+                used.update(range(e, e + 4))
+        # the reload loop past the register passes
+        e = 4 * t + passes * 4 * threads
+        while e < K:
+            assert e + 4 <= K and (e >> 5) < K // 32
+            used.update(range(e, e + 4))
+            e += 4 * threads
+    assert used == set(range(K))
+
+
+@pytest.mark.parametrize("k", [32, 96, 1024, 2080, 3584, 16384])
+@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("two", [None, "norm", "silu"])
+def test_fused_prologue_addressing(k, waves, two):
+    fused_prologue_loads(k, waves * 64, 4, two)
+
+
+def test_fused_prologue_constants():
+    src = open(os.path.join(CSRC, "q8gemv.hip")).read()
+    assert re.search(r"constexpr int kXPasses = 4;", src)
+    assert re.search(r"constexpr int kMaxFusedK = 16384;", src)
+    assert "e < K ? e : K - 4" in src
