@@ -35,6 +35,9 @@ Other workloads (per-call figures; a step is one call):
                         per layer QKV with its normalization, out (+residual), gate+up with silu*up
                         quantized in its epilogue, down (+residual); then final norm and head. 98
                         launches per token fused, 194 unfused (timed too; both bit-identical)
+  q8-layers-0.8b-b16    the same layers for 16 decode streams at once: per layer 4 q8_gemv_batch launches
+                        and 4 batched neighbour-step launches (normalize+quantize, quantize,
+                        normalize+quantize, silu*up+quantize); 194 launches per step of 16 tokens
 
 Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
 then K timed steps between two synchronizations, measured with HIP events on the
@@ -57,7 +60,8 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
 WORKLOADS = ["q8-stack-0.8b", "q8-stack-0.8b-b16", "q8-gateup-7168x1024", "q8-head-151936x1024-b16",
              "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120",
-             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584", "q8-mlp-0.8b", "q8-layers-0.8b"]
+             "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584", "q8-mlp-0.8b", "q8-layers-0.8b",
+             "q8-layers-0.8b-b16"]
 NORM_EPS = 1e-6  # RMS-normalization epsilon of the neighbour-step workloads
 BATCH = 16  # decode streams of the -b16 workloads
 
@@ -1102,6 +1106,142 @@ def run_layers(args, torch, q8, np):
     }
 
 
+def run_layers_b16(args, torch, q8, np):
+    """The 0.8B decode layers with their neighbour steps for 16 streams (Q8BatchLayerChain)."""
+    import oracle
+    import synth
+    from block_quantized_weight_q8_amd.layers import Q8BatchLayerChain
+    from block_quantized_weight_q8_amd.stack import Q8DecodeStack
+
+    orc = oracle.get()
+    nb = BATCH
+    t0 = time.time()
+    ops = synth.q8_stack_08b()
+    host = synth.q8_stack_inputs(ops)
+    inputs = synth.layer_chain_inputs()
+    binp = synth.layer_chain_batch_inputs(nb)
+    bc = Q8BatchLayerChain(Q8DecodeStack(ops, host), inputs, binp, eps=NORM_EPS)
+    log(f"[bench] generated {len(ops)} projections and {nb} streams of layer inputs in {time.time() - t0:.1f}s")
+    k, f, L = bc.hidden, bc.ffn, bc.layers
+    norm_q = nb * (4 * k + k + 2 * (k // 32)) + 4 * k
+    per_layer = (2 * norm_q + nb * synth.q8_quantize_bytes(2048) + nb * (8 * f + f + 2 * (f // 32))
+                 + synth.q8_batch_gemv_bytes(4096, k, nb) + synth.q8_batch_gemv_bytes(k, 2048, nb, True)
+                 + synth.q8_batch_gemv_bytes(2 * f, k, nb) + synth.q8_batch_gemv_bytes(k, f, nb, True))
+    step_bytes = L * per_layer + norm_q + synth.q8_batch_gemv_bytes(ops[-1].n, k, nb)
+    # parity: every step of sampled layers and streams against the oracle on the GPU's own inputs
+    tr = []
+    bc.step(trace=tr)
+    t = {(n, l): x.numpy() for n, l, x in tr}
+    worst = 0.0
+
+    def rel(y, yr, S):
+        return float(np.max(np.abs(np.asarray(y, np.float64) - yr) / S))
+
+    for l in (0, L // 2, L - 1):
+        qkv, out, gu, down = (host[4 * l + j] for j in range(4))
+        for v in (0, nb - 1):
+            h_in, h_mid, g = t[("h_in", l)][v], t[("h_mid", l)][v], t[("gu", l)][v]
+            rq, rd = orc.quantize_act(orc.rmsnorm(h_in, inputs["gamma_attn"][l], NORM_EPS))
+            cb = t[("qkv_codes", l)][v]
+            if not (np.array_equal(cb[:k].view(np.int8), rq) and np.array_equal(cb[k:].view(np.uint16), rd)):
+                raise SystemExit(f"parity: layer {l} stream {v} normalized codes differ from the oracle")
+            worst = max(worst, rel(t[("qkv", l)][v], *orc.q8_gemv(qkv["qw"], qkv["dw"], rq, rd)))
+            worst = max(worst, rel(h_mid, *orc.q8_gemv(out["qw"], out["dw"], *orc.quantize_act(binp["attn"][l][v]),
+                                                       h_in)))
+            mq, md = orc.quantize_act(orc.rmsnorm(h_mid, inputs["gamma_mlp"][l], NORM_EPS))
+            worst = max(worst, rel(g, *orc.q8_gemv(gu["qw"], gu["dw"], mq, md)))
+            aq, ad = orc.quantize_act(orc.silu_mul(g))
+            cb = t[("a_codes", l)][v]
+            if not (np.array_equal(cb[:f].view(np.int8), aq) and np.array_equal(cb[f:].view(np.uint16), ad)):
+                raise SystemExit(f"parity: layer {l} stream {v} activation codes differ from the oracle")
+            h_next = t[("h_in", l + 1)][v] if l + 1 < L else t[("h_out", l)][v]
+            worst = max(worst, rel(h_next, *orc.q8_gemv(down["qw"], down["dw"], aq, ad, h_mid)))
+    rows = np.unique(np.concatenate([[0, ops[-1].n - 1], np.random.default_rng(7).integers(0, ops[-1].n, 256)]))
+    for v in (0, nb - 1):
+        fq, fd = orc.quantize_act(orc.rmsnorm(t[("h_out", L - 1)][v], inputs["gamma_final"], NORM_EPS))
+        worst = max(worst, rel(t[("logits", L)][v][rows],
+                               *orc.q8_gemv(host[-1]["qw"][rows], host[-1]["dw"][rows], fq, fd)))
+    if worst > 1e-5:
+        raise SystemExit(f"parity: batched layer chain off by {worst:.2e} * S")
+    log(f"[bench] parity: layers 0, {L // 2}, {L - 1} and the head, streams 0 and {nb - 1}, against the oracle "
+        f"step by step: codes exact, worst |err|/S = {worst:.2e}")
+    probe = probe_gbps(q8, torch)
+    t_step = graph_seconds(torch, bc.step, args.steps, args.warmup)
+    log(f"[bench] {nb} streams through the layer chain ({bc.launches_per_token_step()} launches): "
+        f"{t_step * 1e6:.1f} us/step, {nb / t_step:.0f} tok/s")
+    # per GEMV launch group (the library's configuration for each shape)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    launches = []  # (config, fn, bytes)
+    for l in range(L):
+        launches += [
+            (q8.batch_config(4096), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l), bc.qx, bc.dx, y=bc.qkv),
+             synth.q8_batch_gemv_bytes(4096, k, nb)),
+            (q8.batch_config(k), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 1), bc.qo, bc.do, y=bc.h, residual=bc.h),
+             synth.q8_batch_gemv_bytes(k, 2048, nb, True)),
+            (q8.batch_config(2 * f), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 2), bc.qx, bc.dx, y=bc.gu),
+             synth.q8_batch_gemv_bytes(2 * f, k, nb)),
+            (q8.batch_config(k), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 3), bc.qa, bc.da, y=bc.h, residual=bc.h),
+             synth.q8_batch_gemv_bytes(k, f, nb, True)),
+        ]
+    launches.append((q8.batch_config(ops[-1].n),
+                     lambda: q8.q8_gemv_batch(*bc._w(len(ops) - 1), bc.qx, bc.dx, y=bc.logits),
+                     synth.q8_batch_gemv_bytes(ops[-1].n, k, nb)))
+    groups = {}
+    for cfg, fn, b in launches:
+        groups.setdefault(cfg, []).append((fn, b))
+    per = {}
+    for (ks, sf), items in groups.items():
+        name = f"batch_kernel<{ks}, {sf}>"
+        fn = (lambda items=items: [it[0]() for it in items])
+        tg = (graph_seconds(torch, fn, max(5, args.steps // 2), args.warmup) if len(items) >= 8
+              else cold_seconds(torch, q8, fn, flush_buf)) / len(items)
+        per[name] = [len(items), tg, sum(it[1] for it in items) / len(items)]
+    for name, (c, tg, nbytes) in sorted(per.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        log(f"[bench] {name}: {c} launches/step, {tg * 1e6:.2f} us each, {nbytes / tg / 1e9:.0f} GB/s")
+    dname, (dc, dt_, db) = max(per.items(), key=lambda kv: kv[1][0] * kv[1][1])
+    cpu = None
+    if not args.no_cpu_baseline:
+        nth = cpu_threads()
+        done, c0 = 0, time.perf_counter()
+        while time.perf_counter() - c0 < 10.0:
+            v = done % nb  # one token of stream v at a time (the oracle works one vector at a time)
+            h = binp["h"][v].astype(np.float32)
+            for l in range(L):
+                qkv, out, gu, down = (host[4 * l + j] for j in range(4))
+                orc.q8_gemv(qkv["qw"], qkv["dw"], *orc.quantize_act(orc.rmsnorm(h, inputs["gamma_attn"][l], NORM_EPS)),
+                            nthreads=nth)
+                h = orc.q8_gemv(out["qw"], out["dw"], *orc.quantize_act(binp["attn"][l][v]), h,
+                                nthreads=nth)[0].astype(np.float32)
+                g = orc.q8_gemv(gu["qw"], gu["dw"], *orc.quantize_act(orc.rmsnorm(h, inputs["gamma_mlp"][l], NORM_EPS)),
+                                nthreads=nth)[0].astype(np.float32)
+                h = orc.q8_gemv(down["qw"], down["dw"], *orc.quantize_act(orc.silu_mul(g)), h,
+                                nthreads=nth)[0].astype(np.float32)
+            orc.q8_gemv(host[-1]["qw"], host[-1]["dw"],
+                        *orc.quantize_act(orc.rmsnorm(h, inputs["gamma_final"], NORM_EPS)), nthreads=nth)
+            done += 1
+        dt_c = time.perf_counter() - c0
+        cpu = {"value": round(done * (step_bytes / nb) / dt_c / 1e9, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+               "sample": f"{done} single-stream tokens of the 24-layer chain and head (the oracle has no batched "
+                         f"form beyond one vector at a time) in {dt_c:.1f} s", "tok_per_s": round(done / dt_c, 2),
+               "cpu": cpu_model()}
+        log(f"[bench] oracle on {nth} host threads: {cpu['tok_per_s']} tok/s")
+    value = step_bytes / t_step / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "q8-layers-0.8b-b16", "streams": nb, "layers": L, "hidden": k, "ffn": f,
+                   "vocab": ops[-1].n, "launches_per_step": bc.launches_per_token_step(), "bytes_per_step": step_bytes,
+                   "attention": "not part of this path: a seeded f32 stand-in per layer and stream"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2), "tok_per_s": round(nb / t_step, 1),
+        "probe_GBps": round(probe, 1),
+        "roofline": {"bound": "hbm", "kernel": dname, "achieved": round(db / dt_ / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(db / dt_ / 1e9 / HBM_PEAK_GBPS, 4), "avg_launch_us": round(dt_ * 1e6, 3),
+                     "bytes_per_launch": round(db), "launches_per_step": dc, "traffic": traffic_for(dname)},
+        "cpu_baseline": cpu,
+    }
+
+
 def pmc_workload(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
@@ -1192,6 +1332,8 @@ def main():
         out = run_mlp(args, torch, q8, np)
     elif args.workload == "q8-layers-0.8b":
         out = run_layers(args, torch, q8, np)
+    elif args.workload == "q8-layers-0.8b-b16":
+        out = run_layers_b16(args, torch, q8, np)
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)

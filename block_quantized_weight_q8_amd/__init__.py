@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH):
     lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
     lib.q8_rmsnorm_quantize_act.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I64, _P]
     lib.q8_silu_mul_quantize_act.argtypes = [_P, _P, _P, _I64, _P]
+    lib.q8_rmsnorm_quantize_act_batch.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P]
+    lib.q8_silu_mul_quantize_act_batch.argtypes = [_P, _P, _P, _I64, _I64, _P]
     lib.gemv_stacked_rmsnorm.argtypes = [ctypes.POINTER(_Part), ctypes.c_int, _P, _P, ctypes.c_float, _I64, _P]
     lib.q8_gemv_silu_mul.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
     lib.q8_gateup_silu_quantize.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P]
@@ -110,7 +112,8 @@ def load_library(path: str = LIB_PATH):
     for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
                "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
-               "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize"):
+               "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
+               "q8_rmsnorm_quantize_act_batch", "q8_silu_mul_quantize_act_batch"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -170,34 +173,47 @@ def q8_quantize_act(x, qx=None, dx=None, stream=None):
 
 def q8_rmsnorm_quantize_act(x, gamma, eps, qx=None, dx=None, stream=None):
     """Quantize (x * r) * gamma, r = 1/sqrt(mean(x^2) + eps), into Q8_0 codes qx int8 [K] and
-    binary16 scales dx [K/32]. x, gamma f32 [K], K <= 16384."""
-    k = x.shape[0] if x.dim() == 1 else -1
-    if k < 0 or k % 32:
-        raise ValueError("x must be 1-D with a length that is a multiple of 32")
+    binary16 scales dx [K/32]. x, gamma f32 [K], K <= 16384. With x [B, K], each row is
+    normalized and quantized on its own (one launch): qx [B, K], dx [B, K/32]."""
+    if x.dim() not in (1, 2) or x.shape[-1] % 32:
+        raise ValueError("x must be [K] or [B, K] with K a multiple of 32")
+    k = x.shape[-1]
+    lead = tuple(x.shape[:-1])
     if qx is None:
-        qx = torch.empty(k, dtype=torch.int8, device=x.device)
+        qx = torch.empty(lead + (k,), dtype=torch.int8, device=x.device)
     if dx is None:
-        dx = torch.empty(k // 32, dtype=torch.float16, device=x.device)
-    st = load_library().q8_rmsnorm_quantize_act(
-        _ptr(x, "x", _F32), _ptr(gamma, "gamma", _F32, (k,)), float(eps), _ptr(qx, "qx", _I8, (k,)),
-        _ptr(dx, "dx", _H16, (k // 32,)), k, _stream(stream))
-    _check("q8_rmsnorm_quantize_act", st)
+        dx = torch.empty(lead + (k // 32,), dtype=torch.float16, device=x.device)
+    lib = load_library()
+    args = (_ptr(x, "x", _F32), _ptr(gamma, "gamma", _F32, (k,)), float(eps), _ptr(qx, "qx", _I8, lead + (k,)),
+            _ptr(dx, "dx", _H16, lead + (k // 32,)), k)
+    if lead:
+        st = lib.q8_rmsnorm_quantize_act_batch(*args, lead[0], _stream(stream))
+        _check("q8_rmsnorm_quantize_act_batch", st)
+    else:
+        st = lib.q8_rmsnorm_quantize_act(*args, _stream(stream))
+        _check("q8_rmsnorm_quantize_act", st)
     return qx, dx
 
 
 def q8_silu_mul_quantize_act(gu, qx=None, dx=None, stream=None):
-    """Quantize silu(gate) * up, gu = [gate | up] f32 [2K], into qx int8 [K] and dx [K/32]."""
-    k2 = gu.shape[0] if gu.dim() == 1 else -1
-    if k2 < 0 or k2 % 64:
-        raise ValueError("gu must be 1-D with a length that is a multiple of 64")
-    k = k2 // 2
+    """Quantize silu(gate) * up, gu = [gate | up] f32 [2K], into qx int8 [K] and dx [K/32].
+    With gu [B, 2K], each row on its own (one launch): qx [B, K], dx [B, K/32]."""
+    if gu.dim() not in (1, 2) or gu.shape[-1] % 64:
+        raise ValueError("gu must be [2K] or [B, 2K] with K a multiple of 32")
+    k = gu.shape[-1] // 2
+    lead = tuple(gu.shape[:-1])
     if qx is None:
-        qx = torch.empty(k, dtype=torch.int8, device=gu.device)
+        qx = torch.empty(lead + (k,), dtype=torch.int8, device=gu.device)
     if dx is None:
-        dx = torch.empty(k // 32, dtype=torch.float16, device=gu.device)
-    st = load_library().q8_silu_mul_quantize_act(
-        _ptr(gu, "gu", _F32), _ptr(qx, "qx", _I8, (k,)), _ptr(dx, "dx", _H16, (k // 32,)), k, _stream(stream))
-    _check("q8_silu_mul_quantize_act", st)
+        dx = torch.empty(lead + (k // 32,), dtype=torch.float16, device=gu.device)
+    lib = load_library()
+    args = (_ptr(gu, "gu", _F32), _ptr(qx, "qx", _I8, lead + (k,)), _ptr(dx, "dx", _H16, lead + (k // 32,)), k)
+    if lead:
+        st = lib.q8_silu_mul_quantize_act_batch(*args, lead[0], _stream(stream))
+        _check("q8_silu_mul_quantize_act_batch", st)
+    else:
+        st = lib.q8_silu_mul_quantize_act(*args, _stream(stream))
+        _check("q8_silu_mul_quantize_act", st)
     return qx, dx
 
 

@@ -63,6 +63,7 @@ constexpr bool is_fused(Dt dt) { return dt == Dt::Q8F32 || dt == Dt::Q8NORM || d
 constexpr bool is_16bit(Dt dt) { return dt == Dt::BF16 || dt == Dt::F16; }
 
 constexpr int kMaxFusedK = 16384;  // LDS bytes for the codes of a fused launch
+constexpr int64_t kMaxBatchVectors = 65535;  // vectors of one batched neighbour-step launch (grid dimension)
 
 // ---- neighbour-step prologues ------------------------------------------------
 // The quantization decision is taken on f32 values, so the oracle and every
@@ -478,11 +479,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
 }
 
 // Quantize silu(gate) * up (gu = [gate | up], K values each): the Q8SILU
-// prologue as its own launch.
+// prologue as its own launch. Vector v = blockIdx.y of a batch: gu [v][2K],
+// qx [v][K], dx [v][K/32].
 __global__ __launch_bounds__(256) void silu_quantize_kernel(const float *__restrict__ gu, int8_t *__restrict__ qx,
                                                             uint16_t *__restrict__ dx, int64_t K)
 {
     const int lane = threadIdx.x & (kWave - 1);
+    const int64_t v = blockIdx.y;
+    gu += v * 2 * K;
+    qx += v * K;
+    dx += v * (K / 32);
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     const bool active = e < K;
     const float4 g = active ? *reinterpret_cast<const float4 *>(gu + e) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -495,8 +501,9 @@ __global__ __launch_bounds__(256) void silu_quantize_kernel(const float *__restr
 }
 
 // Quantize (x * r) * gamma with the Q8NORM prologue's arithmetic and order, as
-// one workgroup of kNormThreads (K <= kMaxFusedK): block sums of squares, their
-// total, then the values.
+// one workgroup of kNormThreads per vector (K <= kMaxFusedK): block sums of
+// squares, their total, then the values. Vector v = blockIdx.x of a batch:
+// x [v][K], qx [v][K], dx [v][K/32]; gamma is shared.
 constexpr int kNormThreads = 1024;
 __global__ __launch_bounds__(kNormThreads) void norm_quantize_kernel(const float *__restrict__ x,
                                                                      const float *__restrict__ gamma, float eps,
@@ -505,6 +512,10 @@ __global__ __launch_bounds__(kNormThreads) void norm_quantize_kernel(const float
 {
     __shared__ double s_bss[kMaxFusedK / 32];
     const int lane = threadIdx.x & (kWave - 1);
+    const int64_t v = blockIdx.x;
+    x += v * K;
+    qx += v * K;
+    dx += v * (K / 32);
     for (int64_t e = (int64_t)threadIdx.x * 4; e < K; e += 4 * kNormThreads) {
         const double b = block_sum8(sq4(*reinterpret_cast<const float4 *>(x + e)));
         if ((lane & 7) == 0) s_bss[e >> 5] = b;
@@ -855,16 +866,17 @@ q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, cons
     return run(dtype, parts, nparts, x, dx, K, stream);
 }
 
-q8g_status q8_rmsnorm_quantize_act(const float *x, const float *gamma, float eps, int8_t *qx, uint16_t *dx, int64_t K,
-                                   void *stream)
+q8g_status q8_rmsnorm_quantize_act_batch(const float *x, const float *gamma, float eps, int8_t *qx, uint16_t *dx,
+                                         int64_t K, int64_t B, void *stream)
 {
-    if (K < 0 || K > kMaxFusedK || K % 32) return Q8G_ERR_SHAPE;
+    if (K < 0 || K > kMaxFusedK || K % 32 || B < 0 || B > kMaxBatchVectors) return Q8G_ERR_SHAPE;
     if (!eps_ok(eps)) return Q8G_ERR_ARG;
-    if (K == 0) return Q8G_OK;
+    if (K == 0 || B == 0) return Q8G_OK;
     if (!x || !gamma || !qx || !dx) return Q8G_ERR_NULL;
     if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(qx, 16) || !aligned(dx, 2)) return Q8G_ERR_ALIGN;
-    if (overlap(qx, K, x, 4 * K) || overlap(qx, K, gamma, 4 * K) || overlap(dx, K / 16, x, 4 * K) ||
-        overlap(dx, K / 16, gamma, 4 * K) || overlap(qx, K, dx, K / 16))
+    const int64_t xb = 4 * K * B, qb = K * B, db = (K / 16) * B;
+    if (overlap(qx, qb, x, xb) || overlap(qx, qb, gamma, 4 * K) || overlap(dx, db, x, xb) ||
+        overlap(dx, db, gamma, 4 * K) || overlap(qx, qb, dx, db))
         return Q8G_ERR_OVERLAP;
     const float *xc = x, *gc = gamma;
     float ec = eps;
@@ -872,19 +884,27 @@ q8g_status q8_rmsnorm_quantize_act(const float *x, const float *gamma, float eps
     uint16_t *dc = dx;
     int64_t kc = K;
     void *args[] = {&xc, &gc, &ec, &qc, &dc, &kc};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&norm_quantize_kernel), dim3(1),
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&norm_quantize_kernel), dim3((unsigned)B),
                                          dim3(kNormThreads), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
 
-q8g_status q8_silu_mul_quantize_act(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, void *stream)
+q8g_status q8_rmsnorm_quantize_act(const float *x, const float *gamma, float eps, int8_t *qx, uint16_t *dx, int64_t K,
+                                   void *stream)
 {
-    if (K < 0 || K > kMaxElems / 2 || K % 32) return Q8G_ERR_SHAPE;
-    if (K == 0) return Q8G_OK;
+    return q8_rmsnorm_quantize_act_batch(x, gamma, eps, qx, dx, K, 1, stream);
+}
+
+q8g_status q8_silu_mul_quantize_act_batch(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, int64_t B,
+                                          void *stream)
+{
+    if (K < 0 || K % 32 || B < 0 || B > kMaxBatchVectors) return Q8G_ERR_SHAPE;
+    if (B > 0 && K > kMaxElems / 2 / B) return Q8G_ERR_SHAPE;
+    if (K == 0 || B == 0) return Q8G_OK;
     if (!gu || !qx || !dx) return Q8G_ERR_NULL;
     if (!aligned(gu, 16) || !aligned(qx, 16) || !aligned(dx, 2)) return Q8G_ERR_ALIGN;
-    if (overlap(qx, K, gu, 8 * K) || overlap(dx, K / 16, gu, 8 * K) || overlap(qx, K, dx, K / 16))
-        return Q8G_ERR_OVERLAP;
+    const int64_t gb = 8 * K * B, qb = K * B, db = (K / 16) * B;
+    if (overlap(qx, qb, gu, gb) || overlap(dx, db, gu, gb) || overlap(qx, qb, dx, db)) return Q8G_ERR_OVERLAP;
     const int64_t blocks = (K / 4 + 255) / 256;
     if (blocks > 0x7FFFFFFF) return Q8G_ERR_SHAPE;
     const float *gc = gu;
@@ -892,9 +912,15 @@ q8g_status q8_silu_mul_quantize_act(const float *gu, int8_t *qx, uint16_t *dx, i
     uint16_t *dc = dx;
     int64_t kc = K;
     void *args[] = {&gc, &qc, &dc, &kc};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&silu_quantize_kernel), dim3((unsigned)blocks),
-                                         dim3(256), args, 0, static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void *>(&silu_quantize_kernel), dim3((unsigned)blocks, (unsigned)B),
+                        dim3(256), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
+q8g_status q8_silu_mul_quantize_act(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, void *stream)
+{
+    return q8_silu_mul_quantize_act_batch(gu, qx, dx, K, 1, stream);
 }
 
 q8g_status gemv_stacked_rmsnorm(const q8g_part *parts, int nparts, const float *x, const float *gamma, float eps,

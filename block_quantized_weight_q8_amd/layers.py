@@ -17,13 +17,18 @@ seeded stand-in per layer). One token, fused (4 launches per layer):
 then the final normalization (q8_rmsnorm_quantize_act) and the head (q8_gemv).
 Unfused (8 launches per layer) runs every normalization, activation and quantize as
 its own launch. Both give the same bits.
+
+Q8BatchLayerChain runs the same layers for nb decode streams at once over the same
+weights (8 launches per layer): every projection is one q8_gemv_batch over the nb
+vectors, each neighbour step one batched launch (normalize + quantize, silu * up +
+quantize, quantize), and the residual streams are updated in place.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import (gemv_stacked, gemv_stacked_rmsnorm, q8_gateup_silu_quantize, q8_gemv, q8_quantize_act,
+from . import (gemv_stacked, gemv_stacked_rmsnorm, q8_gateup_silu_quantize, q8_gemv, q8_gemv_batch, q8_quantize_act,
                q8_rmsnorm_quantize_act, q8_silu_mul_quantize_act)
 
 
@@ -132,3 +137,73 @@ class Q8LayerChain:
 
     def launches_per_token(self, fused: bool = True) -> int:
         return self.layers * (4 if fused else 8) + 2
+
+
+class Q8BatchLayerChain:
+    """nb decode streams through the layers of a Q8DecodeStack (weights shared, not copied).
+    inputs: synth.layer_chain_inputs (its normalization weights serve every stream);
+    batch_inputs: synth.layer_chain_batch_inputs (per stream the residual stream entering
+    layer 0, h f32 [nb, hidden], and per layer the attention stand-in, f32 [nb, attn_width])."""
+
+    def __init__(self, stack, inputs, batch_inputs, eps: float = 1e-6):
+        self.stack = stack
+        self.eps = float(eps)
+        dev = stack.device
+        ops = stack.ops
+        self.layers = (len(ops) - 1) // 4
+        self.hidden = ops[0].k
+        self.ffn = ops[2].parts[0]
+        self.nb = batch_inputs["h"].shape[0]
+        nb, k, f = self.nb, self.hidden, self.ffn
+        self.h0 = _dev(batch_inputs["h"], dev)
+        self.h = torch.empty_like(self.h0)
+        self.attn = [_dev(a, dev) for a in batch_inputs["attn"]]
+        self.gamma_attn = [_dev(g, dev) for g in inputs["gamma_attn"]]
+        self.gamma_mlp = [_dev(g, dev) for g in inputs["gamma_mlp"]]
+        self.gamma_final = _dev(inputs["gamma_final"], dev)
+        self.qx = torch.empty((nb, k), dtype=torch.int8, device=dev)
+        self.dx = torch.empty((nb, k // 32), dtype=torch.float16, device=dev)
+        aw = ops[1].k
+        self.qo = torch.empty((nb, aw), dtype=torch.int8, device=dev)
+        self.do = torch.empty((nb, aw // 32), dtype=torch.float16, device=dev)
+        self.qa = torch.empty((nb, f), dtype=torch.int8, device=dev)
+        self.da = torch.empty((nb, f // 32), dtype=torch.float16, device=dev)
+        self.qkv = torch.empty((nb, ops[0].n), dtype=torch.float32, device=dev)
+        self.gu = torch.empty((nb, 2 * f), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((nb, ops[-1].n), dtype=torch.float32, device=dev)
+
+    def _w(self, i):
+        b = self.stack.bufs[i]
+        return b["qw"], b["dw"]
+
+    def step(self, stream=None, trace=None):
+        eps = self.eps
+
+        def snap(name, l, t):
+            if trace is not None:
+                torch.cuda.synchronize()
+                trace.append((name, l, t.detach().cpu().clone()))
+
+        for l in range(self.layers):
+            h_in = self.h0 if l == 0 else self.h
+            snap("h_in", l, h_in)
+            q8_rmsnorm_quantize_act(h_in, self.gamma_attn[l], eps, qx=self.qx, dx=self.dx, stream=stream)
+            snap("qkv_codes", l, torch.cat([self.qx.view(torch.uint8), self.dx.view(torch.uint8)], dim=1))
+            q8_gemv_batch(*self._w(4 * l), self.qx, self.dx, y=self.qkv, stream=stream)
+            snap("qkv", l, self.qkv)
+            q8_quantize_act(self.attn[l].view(-1), self.qo.view(-1), self.do.view(-1), stream=stream)
+            q8_gemv_batch(*self._w(4 * l + 1), self.qo, self.do, y=self.h, residual=h_in, stream=stream)
+            snap("h_mid", l, self.h)
+            q8_rmsnorm_quantize_act(self.h, self.gamma_mlp[l], eps, qx=self.qx, dx=self.dx, stream=stream)
+            q8_gemv_batch(*self._w(4 * l + 2), self.qx, self.dx, y=self.gu, stream=stream)
+            snap("gu", l, self.gu)
+            q8_silu_mul_quantize_act(self.gu, self.qa, self.da, stream=stream)
+            snap("a_codes", l, torch.cat([self.qa.view(torch.uint8), self.da.view(torch.uint8)], dim=1))
+            q8_gemv_batch(*self._w(4 * l + 3), self.qa, self.da, y=self.h, residual=self.h, stream=stream)
+        snap("h_out", self.layers - 1, self.h)
+        q8_rmsnorm_quantize_act(self.h, self.gamma_final, eps, qx=self.qx, dx=self.dx, stream=stream)
+        q8_gemv_batch(*self._w(len(self.stack.ops) - 1), self.qx, self.dx, y=self.logits, stream=stream)
+        snap("logits", self.layers, self.logits)
+
+    def launches_per_token_step(self) -> int:
+        return self.layers * 8 + 2

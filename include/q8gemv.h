@@ -167,6 +167,17 @@ q8g_status q8_rmsnorm_quantize_act(const float *x, const float *gamma, float eps
  * K % 32 == 0. */
 q8g_status q8_silu_mul_quantize_act(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, void *stream);
 
+/* The same two steps for B vectors in one launch (the inputs of q8_gemv_batch):
+ * vector b is row b of x f32 [B][K] (gamma shared) or of gu f32 [B][2K] (gate
+ * then up: the layout q8_gemv_batch writes for a stacked gate+up matrix), and
+ * row b of qx int8 [B][K] and dx uint16 [B][K/32]. Each vector is normalized and
+ * quantized on its own, exactly as the single-vector call does it.
+ * 0 <= B <= 65535; B == 0 enqueues nothing. */
+q8g_status q8_rmsnorm_quantize_act_batch(const float *x, const float *gamma, float eps, int8_t *qx, uint16_t *dx,
+                                         int64_t K, int64_t B, void *stream);
+q8g_status q8_silu_mul_quantize_act_batch(const float *gu, int8_t *qx, uint16_t *dx, int64_t K, int64_t B,
+                                          void *stream);
+
 /* Stacked Q8_0 projection of RMSnorm(x) * gamma: one launch normalizes and
  * quantizes x in every workgroup, then runs the dot products. K <= 16384.
  * Part p's result is identical, bit for bit, to q8_rmsnorm_quantize_act then

@@ -165,6 +165,16 @@ def layer_chain_inputs(layers: int = 24, hidden: int = 1024, attn_width: int = 2
     return out
 
 
+def layer_chain_batch_inputs(nb: int, layers: int = 24, hidden: int = 1024, attn_width: int = 2048,
+                             tag: int = TAG_LAYERS):
+    """Per-stream inputs of the batched decode-layer chain: the residual streams entering
+    layer 0, f32 [nb, hidden], and per layer the attention stand-ins, f32 [nb, attn_width]."""
+    g = rng_for(tag, 1)
+    h = np.stack([activation_f32(g, hidden) for _ in range(nb)])
+    attn = [np.stack([activation_f32(g, attn_width) for _ in range(nb)]) for _ in range(layers)]
+    return {"h": h, "attn": attn}
+
+
 def q8_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
     """Algorithmic HBM bytes of one Q8_0 GEMV: codes + scales + quantized activation + f32 out (+ residual)."""
     b = n * k + n * (k // QBLOCK) * 2 + k + (k // QBLOCK) * 2 + n * 4

@@ -48,6 +48,8 @@ def lib():
     L.gemv_stacked_rmsnorm.argtypes = [ctypes.POINTER(Part), ctypes.c_int, P, P, ctypes.c_float, I64, P]
     L.q8_gemv_silu_mul.argtypes = [P, P, P, P, P, I64, I64, P]
     L.q8_gateup_silu_quantize.argtypes = [P, P, P, P, I64, P, P, I64, P, P, P]
+    L.q8_rmsnorm_quantize_act_batch.argtypes = [P, P, ctypes.c_float, P, P, I64, I64, P]
+    L.q8_silu_mul_quantize_act_batch.argtypes = [P, P, P, I64, I64, P]
     L.q8_gateup_rmsnorm_silu_quantize.argtypes = [P, P, P, P, I64, P, P, ctypes.c_float, I64, P, P, P]
     L.q8g_status_str.argtypes = [ctypes.c_int]
     L.q8g_status_str.restype = ctypes.c_char_p
@@ -61,7 +63,8 @@ def test_every_declared_symbol_is_exported(lib):
     for expected in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
                      "q8g_status_str", "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act",
                      "gemv_stacked_rmsnorm", "q8_gemv_silu_mul", "q8_gateup_silu_quantize",
-                     "q8_gateup_rmsnorm_silu_quantize", "q8g_probe_read", "q8g_flush"):
+                     "q8_gateup_rmsnorm_silu_quantize", "q8_rmsnorm_quantize_act_batch",
+                     "q8_silu_mul_quantize_act_batch", "q8g_probe_read", "q8g_flush"):
         assert expected in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -221,6 +224,24 @@ def test_silu_mul_quantize_validation(lib):
     assert q(X, QX, DX + 1, 64, None) == ERR_ALIGN
     assert q(X, X + 4 * 64, DX, 64, None) == ERR_OVERLAP  # codes inside the up half
     assert q(X, QX, QX + 32, 64, None) == ERR_OVERLAP
+
+
+def test_batched_neighbour_quantize_validation(lib):
+    n = lib.q8_rmsnorm_quantize_act_batch
+    G = R
+    assert n(X, G, 1e-6, QX, DX, 64, -1, None) == ERR_SHAPE
+    assert n(X, G, 1e-6, QX, DX, 64, 65536, None) == ERR_SHAPE
+    assert n(X, G, 1e-6, QX, DX, 48, 2, None) == ERR_SHAPE
+    assert n(X, G, -1.0, QX, DX, 64, 2, None) == ERR_ARG
+    assert n(None, None, 1e-6, None, None, 64, 0, None) == OK  # B == 0
+    assert n(X, G, 1e-6, X + 4 * 64, DX, 64, 2, None) == ERR_OVERLAP  # codes inside vector 1 of x
+    assert n(X, G, 1e-6, QX, QX + 64, 64, 2, None) == ERR_OVERLAP  # scales inside vector 1's codes
+    s = lib.q8_silu_mul_quantize_act_batch
+    assert s(X, QX, DX, 64, -1, None) == ERR_SHAPE
+    assert s(X, QX, DX, 48, 2, None) == ERR_SHAPE
+    assert s(None, None, None, 64, 0, None) == OK
+    assert s(X, X + 8 * 64 + 16, DX, 64, 2, None) == ERR_OVERLAP  # codes inside vector 1's gate
+    assert s(X + 4, QX, DX, 64, 2, None) == ERR_ALIGN
 
 
 def test_fused_neighbour_gemv_validation(lib):
