@@ -155,6 +155,31 @@ def graph_seconds(torch, fn, reps, warmup):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
+def graph_trials(torch, fn, reps, trials):
+    """Capture fn into a HIP graph; seconds per replay in each of `trials` runs of `reps` replays."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    return out
+
+
 def cold_seconds(torch, q8, fn, flush_buf, reps=10):
     """A few launches (too few to amortize the events): one graph replay after a
     1 GiB cache-evicting write, bracketed by HIP events; median of reps."""
@@ -237,6 +262,7 @@ def run_stack(args, torch, q8, np):
 
     probe = probe_gbps(q8, torch)
     log(f"[bench] pure-read probe: {probe:.0f} GB/s")
+    env_before = gpu_environment(torch)
 
     def time_graph(fn, reps):
         return graph_seconds(torch, fn, reps, args.warmup)
@@ -289,6 +315,23 @@ def run_stack(args, torch, q8, np):
 
     if args.breakdown:
         eager_breakdown(stack, ops, q8, torch, bytes_gemv, bytes_quant)
+
+    # the reported mode again, as 10 trials of the same replays (spread), and eagerly (no graph)
+    fused_best = t_fused <= min(t_graph, t_persist)
+    trials = graph_trials(torch, (lambda: stack.step(fused=True)) if fused_best else (lambda: stack.step(fused=False)),
+                          max(5, args.steps // 5), 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stack.step(fused=fused_best)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        stack.step(fused=fused_best)
+    e1.record()
+    torch.cuda.synchronize()
+    t_eager = e0.elapsed_time(e1) * 1e-3 / 5
+    log(f"[bench] {'fused' if fused_best else 'quantize + GEMV'} step over 10 trials: median "
+        f"{np.median(trials) * 1e6:.1f} us (p10 {np.percentile(trials, 10) * 1e6:.1f}, p90 "
+        f"{np.percentile(trials, 90) * 1e6:.1f}); eager, without a graph: {t_eager * 1e6:.1f} us")
 
     # the step that is reported, and the roofline of its dominant kernel
     best = min(("fused", t_fused), ("graph", t_graph), ("decode_stack", t_persist), key=lambda m: m[1])
@@ -360,7 +403,11 @@ def run_stack(args, torch, q8, np):
         "probe_GBps": round(probe, 1),
         "pct_of_probe": round(100 * value / probe, 2),
         "modes_ms_per_step": {"fused_graph": round(t_fused * 1e3, 4), "quantize_gemv_graph": round(t_graph * 1e3, 4),
-                              "decode_stack": round(t_persist * 1e3, 4)},
+                              "decode_stack": round(t_persist * 1e3, 4), "eager_no_graph": round(t_eager * 1e3, 4)},
+        "trials_ms_per_step": {"trials": len(trials), "median": round(float(np.median(trials)) * 1e3, 4),
+                               "p10": round(float(np.percentile(trials, 10)) * 1e3, 4),
+                               "p90": round(float(np.percentile(trials, 90)) * 1e3, 4)},
+        "environment": {"before": env_before, "after": gpu_environment(torch)},
 
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -434,13 +481,11 @@ def eager_breakdown(stack, ops, q8, torch, bytes_gemv, bytes_quant, steps=10):
             f"{bsum / tsum / 1e9:.0f} GB/s algorithmic")
 
 
-def cpu_baseline_stack(ops, host, orc, min_seconds=10.0):
-    """The oracle as it stands, on the host cores, over whole tokens of the same
-    stack inputs (quantize + GEMV for all 97 projections), repeated until about
-    `min_seconds` of CPU work has been timed."""
+def oracle_stack_tokens(ops, host, orc, nth, min_seconds):
+    """Whole tokens of the stack through the oracle on nth threads until about min_seconds
+    have been timed: (tokens, algorithmic bytes, seconds)."""
     import synth
 
-    nth = cpu_threads()
     nbytes, tokens = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -451,13 +496,46 @@ def cpu_baseline_stack(ops, host, orc, min_seconds=10.0):
         tokens += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
-    dt = time.perf_counter() - t0
+    return tokens, nbytes, time.perf_counter() - t0
+
+
+def cpu_baseline_stack(ops, host, orc, min_seconds=10.0):
+    """The oracle as it stands, on the host cores, over whole tokens of the same
+    stack inputs (quantize + GEMV for all 97 projections), repeated until about
+    `min_seconds` of CPU work has been timed; then on one thread for about half as long."""
+    nth = cpu_threads()
+    tokens, nbytes, dt = oracle_stack_tokens(ops, host, orc, nth, min_seconds)
     gbps = nbytes / dt / 1e9
     log(f"[bench] oracle on {nth} host threads ({cpu_model()}): {gbps:.2f} GB/s, {tokens} tokens in {dt:.1f}s")
+    t1, b1, d1 = oracle_stack_tokens(ops, host, orc, 1, min_seconds / 2)
+    log(f"[bench] oracle on 1 host thread: {b1 / d1 / 1e9:.2f} GB/s, {t1} tokens in {d1:.1f}s")
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
             "sample": f"{tokens} whole tokens of the 0.8B-shaped stack (97 quantizes + 97 GEMVs each), "
                       f"{nbytes} algorithmic bytes in {dt:.1f} s",
-            "tok_per_s": round(tokens / dt, 2), "cpu": cpu_model()}
+            "tok_per_s": round(tokens / dt, 2), "cpu": cpu_model(),
+            "one_thread": {"value": round(b1 / d1 / 1e9, 3), "unit": "GB/s", "tok_per_s": round(t1 / d1, 2),
+                           "sample": f"{t1} whole tokens in {d1:.1f} s"}}
+
+
+def gpu_environment(torch):
+    """Versions, GPU clocks and the processes on the GPU (best effort, through rocm-smi
+    run as a child process): a contended or down-clocked GPU makes a run worthless."""
+    import subprocess
+
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    for key, path in (("rocm", "/opt/rocm/.info/version"), ("amdgpu_driver", "/sys/module/amdgpu/version")):
+        try:
+            with open(path) as f:
+                env[key] = f.read().strip()
+        except OSError:
+            env[key] = None
+    for key, flag in (("clocks", "--showclocks"), ("gpu_pids", "--showpids")):
+        try:
+            r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=30)
+            env[key] = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else None
+        except (OSError, ValueError, subprocess.SubprocessError):
+            env[key] = None
+    return env
 
 
 # ----------------------------------------------------------------------------- 16 streams
