@@ -1320,7 +1320,7 @@ def run_layers_b16(args, torch, q8, np):
     }
 
 
-def pmc_workload(args, torch, q8, np):
+def counter_run(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
     decode steps of the fused per-projection path, two steps of the 16-stream stack, and
@@ -1366,7 +1366,7 @@ def pmc_workload(args, torch, q8, np):
         q8.q8_gateup_silu_quantize(w[:3584], dwt[:3584], w[3584:], dwt[3584:], torch.from_numpy(x).cuda(),
                                    gamma=torch.from_numpy(gamma).cuda(), eps=NORM_EPS)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_workload": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps, "
+    print(json.dumps({"counter_run": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps, "
                                       "2 steps of 16 streams, 4 + 4 + 4 neighbour-step launches"}), flush=True)
 
 
@@ -1378,7 +1378,7 @@ def main():
     ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="eager per-launch timing of the per-projection path")
-    ap.add_argument("--pmc-workload", action="store_true",
+    ap.add_argument("--counter-run", action="store_true",
                     help="untimed run for rocprofv3 --pmc passes (calibration read/write + two decode steps)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -1397,8 +1397,8 @@ def main():
     q8.load_library()
     log(f"[bench] device: {torch.cuda.get_device_name(0)}; workload {args.workload}; kernel sources "
         + ", ".join(f"{k} {kernel_source_digest(k)}" for k in KERNEL_SOURCES))
-    if args.pmc_workload:
-        pmc_workload(args, torch, q8, np)
+    if args.counter_run:
+        counter_run(args, torch, q8, np)
         return
     if args.workload == "q8-stack-0.8b":
         out = run_stack(args, torch, q8, np)
