@@ -16,9 +16,11 @@
  *        is quantized once and shared; projections that read the same input are
  *        stacked; the residual add is folded into the matmul.
  *   [H]  "One level down: #002 the same compiler on a GPU", sections "Emitting
- *        for a GPU" (the bf16 gate+up matvec, rows of 16-byte chunks),
- *        "The numerical contract" (bf16 weights and activations, f32
- *        accumulators) and "The bench" (the same engine in f16).
+ *        for a GPU" (the bf16 gate+up matvec, rows of 16-byte chunks; at
+ *        decode the normalization and the activation are each fused with the
+ *        projection after them), "The numerical contract" (bf16 weights and
+ *        activations, f32 accumulators) and "The bench" (the same engine in f16).
+ *   [P]  section "Q4_K_M" also names a block's RMS normalization and gated MLP.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - weight and activation block scales are IEEE binary16;
@@ -26,7 +28,12 @@
  *     q = rint(fl32(x / d)) with ties to even, using the f32 d, and the stored
  *     scale is binary16(d) rounded to nearest even; an all-zero block gets
  *     d = 0, q = 0;
- *   - the residual is added once, after the whole dot.
+ *   - the residual is added once, after the whole dot;
+ *   - a small batch is the Q8_0 GEMV once per activation vector;
+ *   - RMS normalization: h = fl32(fl32(x * r) * gamma) with r = 1/sqrt(ss/K +
+ *     eps) formed in f64 and rounded once to f32, ss = sum of x^2 in f64;
+ *   - gated activation: a = silu(gate) * up = gate * up / (1 + exp(-gate)),
+ *     formed in f64 and rounded once to f32.
  *
  * Precision: every Q8_0 block term isum·dw·dx is exact in f64 (20 + 11 + 11
  * significant bits); every bf16 product is exact in f64 (8 + 8 bits), every
@@ -41,7 +48,14 @@
  * blocks); the block integer sums against Python-integer brute force and
  * closed forms; the GEMVs against exact rational arithmetic on tiny shapes,
  * against a numpy f64 matmul of the dequantized operands, and against closed
- * forms and invariants.
+ * forms and invariants; the batched GEMV against an exact integer matmul at
+ * unit scales and vector by vector against the single-vector GEMV; the RMS
+ * normalization against an exactly rounded sum of squares (math.fsum) and
+ * closed forms (constant vectors, scale invariance, gamma linearity, eps
+ * dominating); the gated activation against an independent numpy f64
+ * evaluation and closed forms (zero gate or up, saturated gates, the
+ * silu(g) - silu(-g) = g identity). tests/test_oracle_mutants.py plants
+ * mistakes in copies of this file; each must fail a pin.
  */
 #include <math.h>
 #include <pthread.h>
