@@ -99,12 +99,16 @@ using WholeShape = Shape<4, 1, 8, 1024>;
 
 __device__ __forceinline__ v4i as_v4i(const int4 &v) { return v4i{v.x, v.y, v.z, v.w}; }
 
-// s_waitcnt with vmcnt <= n (n < 64), the other counters left alone
-template <int n>
-__device__ __forceinline__ void wait_vmcnt()
+// s_waitcnt with vmcnt <= vm (vm < 64; 63 waits for nothing) and lgkmcnt <= lgkm
+// (lgkm < 16), expcnt left alone. The barriers below are bare s_barrier
+// instructions, and on gfx950 the compiler puts no wait in front of one, so a
+// wave's own LDS writes (lgkmcnt) and direct global-to-LDS copies (vmcnt) are
+// waited for here before other waves may read them.
+template <int vm, int lgkm>
+__device__ __forceinline__ void wait_counts()
 {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    static_assert(vm >= 0 && vm < 64 && lgkm >= 0 && lgkm < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (lgkm << 8));
 }
 
 template <class SH>
@@ -198,16 +202,18 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
 #pragma unroll
         for (int p = 0; p < P; ++p) issue(p, s_begin + p < s_end ? s_begin + p : last);
 
-        // 3. the copies are older than the P weight loads: wait for them only,
-        //    then a bare barrier (LDS needs no memory fence within the
-        //    workgroup; a full __syncthreads would also wait for the weights)
-        wait_vmcnt<P>();
+        // 3. the copies are older than the P weight loads: wait for them (and
+        //    for the zero slot's LDS store) only, then a bare barrier; a full
+        //    __syncthreads would also wait for the weights
+        wait_counts<P, 0>();
         __builtin_amdgcn_s_barrier();
-        //    the staged activation scale bits to f32, in place, once per tile
+        //    the staged activation scale bits to f32, in place, once per tile;
+        //    the rewritten words are complete before the barrier
         for (int t = threadIdx.x; t < dx_pos; t += SH::kThreads) {
             uint32_t *v = reinterpret_cast<uint32_t *>(s_lds + SH::kDxOff) + t;
             *v = __builtin_bit_cast(uint32_t, f16_bits_to_f32((uint16_t)*v));
         }
+        wait_counts<63, 0>();
         __builtin_amdgcn_s_barrier();
 
         auto consume = [&](int p, int st) {
