@@ -289,14 +289,15 @@ __device__ __forceinline__ void compute_batch(const Batch &b, const int8_t *__re
 // Reduce the R row sums of a wave and write them (+ residual, added once).
 // Row i is written by lane lane_of<R>(i); the loop index is a compile-time
 // constant, so every row pointer stays a scalar (no indexed private array).
-template <int R>
+// PRES: some part has a residual, prefetched into res (without PRES no part has one)
+template <int R, bool PRES>
 __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (&rows)[R], const bool (&valid)[R],
-                                                 int lane)
+                                                 const float (&res)[R], int lane)
 {
     const float total = wave_reduce_rows<R>(acc, lane);
 #pragma unroll
     for (int i = 0; i < R; ++i)
-        if (valid[i] && lane == lane_of<R>(i)) *rows[i].y = rows[i].res ? total + *rows[i].res : total;
+        if (valid[i] && lane == lane_of<R>(i)) *rows[i].y = PRES && rows[i].res ? total + res[i] : total;
 }
 
 // y[rows] = W[rows] · x (+ residual) for the R rows owned by each wave.
@@ -313,7 +314,7 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 // (waves 8..15); it writes no f32 output but the 32 codes qa[32b..] and the
 // scale da[b] of a = silu(gate) * up, formed and quantized exactly as
 // q8_silu_mul_quantize_act forms them from the two rows' f32 results.
-template <Dt DT, int R, int WAVES, bool EPI = false>
+template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
                                                             const uint16_t *__restrict__ dx,
                                                             const float *__restrict__ aux, float eps,
@@ -321,6 +322,7 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
                                                             uint16_t *__restrict__ da)
 {
     static_assert(!EPI || (R == 4 && WAVES == 16), "the epilogue needs 32 gate and 32 up rows per workgroup");
+    static_assert(!(EPI && PRES), "the epilogue kind has no residual");
     constexpr bool FUSED = is_fused(DT);
     constexpr bool TWO = DT == Dt::Q8NORM || DT == Dt::Q8SILU;  // a second f32 input per value
     constexpr int kThreadsPerGroup = WAVES * kWave;
@@ -369,6 +371,31 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     for (int r = 0; r < R; ++r) {
         valid[r] = row0 + r < n_total;
         LOCATE(valid[r] ? row0 + r : (has_rows ? row0 : 0), row_bytes, nb, rows[r]);
+    }
+
+    // PRES (launches where some part has a residual): the residuals are requested
+    // before the weights (one wave's loads complete in issue order), so the final
+    // store does not wait for one more memory round trip. Every lane loads (a load
+    // under a condition would be waited for at the branch join); a row without a
+    // residual reads the first word of the activation instead (just requested, so
+    // cached; its value is unused), or its own output element when K == 0 and
+    // there is no activation. The address goes through a vector register so that
+    // this stays a vector load, counted with the other loads (a uniform address
+    // would become a scalar load, whose wait the compiler merges with the LDS
+    // waits of the quantization; a volatile load is waited for at once). Without
+    // a residual the launch keeps the registers this costs (the output heads are
+    // sensitive to occupancy).
+    float res[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) res[r] = 0.0f;
+    if constexpr (PRES) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float *dummy = K > 0 ? static_cast<const float *>(xv) : rows[r].y;
+            uint64_t a = reinterpret_cast<uint64_t>(rows[r].res ? rows[r].res : dummy);
+            asm("" : "+v"(a));
+            res[r] = *reinterpret_cast<const __attribute__((address_space(1))) float *>(a);
+        }
     }
 
     Batch cur, nxt;
@@ -459,7 +486,7 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
             }
         }
     } else {
-        reduce_and_store<R>(acc, rows, valid, lane);
+        reduce_and_store<R, PRES>(acc, rows, valid, res, lane);
     }
 }
 
@@ -550,7 +577,7 @@ struct Input {
     int64_t bytes;
 };
 
-template <Dt DT, int R, int WAVES, bool EPI = false>
+template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false>
 hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const float *aux, float eps, int64_t K,
                        int64_t n_total, hipStream_t s, int8_t *qa = nullptr, uint16_t *da = nullptr)
 {
@@ -570,7 +597,7 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const 
                     &pc.dw[3],  &pc.y[0],   &pc.y[1],   &pc.y[2],   &pc.y[3],   &pc.res[0], &pc.res[1],
                     &pc.res[2], &pc.res[3], &pc.end[0], &pc.end[1], &pc.end[2], &xc,       &dxc,
                     &auxc,      &epsc,      &kc,        &nc,        &qac,       &dac};
-    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES, EPI>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES, EPI, PRES>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(WAVES * kWave), args, 0, s);
 }
 
@@ -627,14 +654,23 @@ struct Prologue {
     float eps;         // Q8NORM: added to the mean square
 };
 
+template <Dt DT, int R, int W>
+hipError_t launch_res(bool pres, const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K,
+                      int64_t n_total, hipStream_t s)
+{
+    return pres ? launch_gemv<DT, R, W, false, true>(p, x, dx, pr.aux, pr.eps, K, n_total, s)
+                : launch_gemv<DT, R, W, false, false>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+}
+
 template <Dt DT, int W>
 hipError_t dispatch_rows(int rows, const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K,
                          int64_t n_total, hipStream_t s)
 {
+    const bool pres = p.res[0] || p.res[1] || p.res[2] || p.res[3];
     switch (rows) {
-    case 4: return launch_gemv<DT, 4, W>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
-    case 2: return launch_gemv<DT, 2, W>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
-    default: return launch_gemv<DT, 1, W>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+    case 4: return launch_res<DT, 4, W>(pres, p, x, dx, pr, K, n_total, s);
+    case 2: return launch_res<DT, 2, W>(pres, p, x, dx, pr, K, n_total, s);
+    default: return launch_res<DT, 1, W>(pres, p, x, dx, pr, K, n_total, s);
     }
 }
 
