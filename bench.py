@@ -348,10 +348,12 @@ def run_stack(args, torch, q8, np):
         for i, op in enumerate(ops):
             fused = mode == "fused" and op.n <= stack.FUSED_MAX_ROWS
             r, w = q8.gemv_config(q8.Q8G_Q8_0_F32 if fused else q8.Q8G_Q8_0, op.n, op.k)
-            groups.setdefault((fused, r, w), []).append(i)
+            # a launch with a residual runs its own kernel variant (the residual requested early)
+            groups.setdefault((fused, r, w, op.residual), []).append(i)
         per = {}
-        for (fused, r, w), idx in groups.items():
-            name = f"gemv_kernel<{'Q8F32' if fused else 'Q8'}, rows_per_wave={r}, waves={w}>"
+        for (fused, r, w, res), idx in groups.items():
+            tag = ", residual" if res else ""
+            name = f"gemv_kernel<{'Q8F32' if fused else 'Q8'}, rows_per_wave={r}, waves={w}{tag}>"
             if fused:
                 nbytes = [synth.q8_gemv_f32x_bytes(ops[i].n, ops[i].k, ops[i].residual) for i in idx]
                 fn = (lambda idx=idx: [stack.launch_op_fused(i) for i in idx])
@@ -1121,14 +1123,14 @@ def run_layers(args, torch, q8, np):
         "q8_rmsnorm_gemv[rows_per_wave=2,waves=8] (QKV)": (
             lambda: [q8.gemv_stacked_rmsnorm(chain.qkv_parts(l), chain.h, chain.gamma_attn[l], NORM_EPS)
                      for l in range(L)], synth.q8_rmsnorm_gemv_bytes(4096, k)),
-        "gemv_kernel<Q8F32, rows_per_wave=1, waves=8> (out)": (
+        "gemv_kernel<Q8F32, rows_per_wave=1, waves=8, residual> (out)": (
             lambda: [q8.gemv_stacked(chain.out_parts(l, chain.h), chain.attn[l]) for l in range(L)],
             synth.q8_gemv_f32x_bytes(k, 2048, residual=True)),
         "q8_gateup_rmsnorm_silu[rows_per_wave=4,waves=16] (gate+up)": (
             lambda: [q8.q8_gateup_silu_quantize(*chain.gate_up(l), chain.h, gamma=chain.gamma_mlp[l], eps=NORM_EPS,
                                                 qa=chain.qa, da=chain.da) for l in range(L)],
             synth.q8_gateup_epilogue_bytes(f, k)),
-        "gemv_kernel<Q8, rows_per_wave=1, waves=4> (down)": (
+        "gemv_kernel<Q8, rows_per_wave=1, waves=4, residual> (down)": (
             lambda: [q8.q8_gemv(chain._b(l, 3)["qw"], chain._b(l, 3)["dw"], chain.qa, chain.da, y=chain.h,
                                 residual=chain.h) for l in range(L)], synth.q8_gemv_bytes(k, f, residual=True)),
     }
