@@ -70,7 +70,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the sources that define each kernel family (a counter summary is valid while they are unchanged)
+# the sources that define each kernel family (a counter summary is valid while their code is unchanged)
 KERNEL_SOURCES = {
     "gemv_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
     "quantize_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
@@ -79,12 +79,37 @@ KERNEL_SOURCES = {
 }
 
 
+def code_tokens(text: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed: what the compiler sees,
+    so that editing a comment does not orphan counters taken on the same code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(files) -> str:
     h = hashlib.sha256()
     for fn in files:
         d = os.path.join(ROOT, "include") if fn.endswith(".h") else os.path.join(ROOT, "block_quantized_weight_q8_amd", "csrc")
-        with open(os.path.join(d, fn), "rb") as f:
-            h.update(fn.encode() + f.read())
+        with open(os.path.join(d, fn), encoding="utf-8") as f:
+            h.update(fn.encode() + code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -33,7 +33,9 @@
 //    tail that wrote rows beyond the output.
 //  * Weights and weight scales are read once per call, so they are loaded
 //    with the nontemporal hint; the activation, shared by every wave, is not.
-//  * No atomics, no LDS staging, no scratch: results depend on the shape only.
+//  * No atomics and no scratch; LDS holds only the quantized activation of the
+//    f32-input kinds (and the reduction slots of the epilogue kind), so results
+//    depend on the shape only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -550,10 +552,10 @@ __global__ __launch_bounds__(kNormThreads) void norm_quantize_kernel(const float
     __syncthreads();
     const float r = rms_scale(blocks_total(s_bss, K / 32, lane), K, eps);
     for (int64_t e = (int64_t)threadIdx.x * 4; e < K; e += 4 * kNormThreads) {
-        const float4 v = *reinterpret_cast<const float4 *>(x + e);
+        const float4 xe = *reinterpret_cast<const float4 *>(x + e);
         const float4 g = *reinterpret_cast<const float4 *>(gamma + e);
         float d;
-        const uint32_t packed = quantize4(prologue_value<Dt::Q8NORM>(v, g, r), &d);
+        const uint32_t packed = quantize4(prologue_value<Dt::Q8NORM>(xe, g, r), &d);
         *reinterpret_cast<uint32_t *>(qx + e) = packed;
         if ((lane & 7) == 0) dx[e >> 5] = scale_bits(d);
     }
@@ -571,11 +573,6 @@ bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
-
-struct Input {
-    const void *p;
-    int64_t bytes;
-};
 
 template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false>
 hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const float *aux, float eps, int64_t K,
