@@ -143,6 +143,22 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
 
     if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(s_lds) = make_uint4(0u, 0u, 0u, 0u);  // the zero slot
 
+    // The residuals of the four outputs this lane stores are requested before
+    // anything else, so the store at the end waits for no further memory round
+    // trip (the first barrier's wait covers them). Every lane loads, clamped into
+    // [B][N]; the values of rows past N and vectors past B are never stored. The
+    // branch is uniform and nothing reads the values before the end, so no wait
+    // is placed at its join.
+    float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (residual) {
+        const int64_t rr = row_ok ? row : N - 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int b = 4 * q + r < B ? 4 * q + r : B - 1;
+            res[r] = residual[(int64_t)b * N + rr];
+        }
+    }
+
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t k0 = 0; k0 < K; k0 += TK) {
         const int kt = (int)(K - k0 < TK ? K - k0 : TK);  // multiple of 32
@@ -268,13 +284,6 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
         __syncthreads();  // the next tile's copies overwrite the staging area
     }
 
-    // residuals of the four outputs this lane stores
-    float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (residual && row_ok) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * q + r < B) res[r] = residual[(int64_t)(4 * q + r) * N + row];
-    }
 
     if constexpr (S > 1) {
         // partial sums of the S waves of a tile, added in split order

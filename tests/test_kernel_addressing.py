@@ -89,7 +89,7 @@ def batch_staging(N, K, B, W, S, TK):
 
 def batch_rows(N, K, B, W, S):
     """Weight rows as a wave-uniform base plus a 32-bit lane offset, clamped for rows past N
-    (including a tile wholly past N); outputs [B][N]."""
+    (including a tile wholly past N); outputs and residuals [B][N]."""
     nb = K // 32
     tiles = (N + K_TILE_ROWS - 1) // K_TILE_ROWS
     tpg = W // S
@@ -109,7 +109,14 @@ def batch_rows(N, K, B, W, S):
                     assert rbase * nb + jr * nb + nb <= N * nb
                 for b in range(16):
                     if row < N and b < B:
-                        assert b * N + row < B * N
+                        assert b * N + row < B * N  # the stored output
+                # the residuals every lane requests up front: vectors 4q..4q+3 of its row,
+                # clamped to vector B-1 and row N-1
+                rr = row if row < N else N - 1
+                for q in range(4):
+                    for r in range(4):
+                        b = 4 * q + r if 4 * q + r < B else B - 1
+                        assert 0 <= b * N + rr < B * N
 
 
 BATCH_CASES = [(16, 64, 1), (17, 96, 3), (100, 1024, 16), (1024, 2048, 8), (300, 3584, 5), (33, 5120, 16),
