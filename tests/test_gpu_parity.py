@@ -529,6 +529,45 @@ def test_q8_fused_stacked_parts(q8):
         assert np.array_equal(u, v)
 
 
+@pytest.mark.parametrize("sizes,with_res", [((3, 4093), (True, False)), ((2048, 1024, 1024), (False, True, False)),
+                                            ((5, 1, 7), (False, True, True)), ((1000, 24), (True, True))])
+def test_q8_fused_stacked_mixed_residuals(q8, orc, sizes, with_res):
+    """Parts with and without a residual in one f32-input launch (the variant that requests
+    the residual before the weights; a row without one reads an activation word instead,
+    including a wave whose rows straddle the two kinds of part): bit-identical to the
+    codes-input launch and to one call per part, within the tolerance of the oracle."""
+    n, k = sum(sizes), 1024
+    print_case("fused stacked mixed residuals", sizes, with_res)
+    qw, dw, x, r = q8_case(n, k, 990 + len(sizes))
+    W, DW, X, Rr = dev(qw), h16(dw), dev(x), dev(r)
+    qx, dx = q8.q8_quantize_act(X)
+
+    def parts():
+        out, off = [], 0
+        for s_, res in zip(sizes, with_res):
+            p_ = {"w": W[off:off + s_], "dw": DW[off:off + s_]}
+            if res:
+                p_["residual"] = Rr[off:off + s_]
+            out.append(p_)
+            off += s_
+        return out
+
+    fused = [host(y) for y in q8.gemv_stacked(parts(), X)]
+    codes = [host(y) for y in q8.gemv_stacked(parts(), qx, dx)]
+    off = 0
+    for i, (s_, res) in enumerate(zip(sizes, with_res)):
+        assert np.array_equal(fused[i], codes[i]), f"part {i}: f32-input and codes-input launches differ"
+        rp = Rr[off:off + s_] if res else None
+        single = host(q8.q8_gemv_f32(W[off:off + s_], DW[off:off + s_], X, residual=rp))
+        assert np.array_equal(fused[i], single), f"part {i} differs from its single call"
+        off += s_
+    yr, S = orc.q8_gemv(qw, dw, *orc.quantize_act(x))
+    mask = np.concatenate([np.full(s_, res) for s_, res in zip(sizes, with_res)])
+    yr = yr + np.where(mask, r.astype(np.float64), 0)
+    S = S + np.where(mask, np.abs(r.astype(np.float64)), 0)
+    within(np.concatenate(fused).astype(np.float64), yr, S, "fused stacked mixed residuals")
+
+
 def test_q8_fused_rejects_long_k(q8, torch_mod):
     torch = torch_mod
     k = 16384 + 32
