@@ -106,11 +106,16 @@ def test_08b_stack_fused_graph_step(q8, orc):
     for b in st.bufs:
         b["y"].fill_(float("nan"))
     st.capture(fused=True)
-    for _ in range(3):
+    for rep in range(3):  # every replay checked, eager work and synchronizations between them
+        for b in st.bufs:
+            b["y"].fill_(float("nan"))
+        torch.cuda.synchronize()
         st.replay()
-    got = [host(b["y"]) for b in st.bufs]
-    for op, r, y in zip(ops, ref, got):
-        assert np.array_equal(r, y), op.name
+        got = [host(b["y"]) for b in st.bufs]
+        for op, r, y in zip(ops, ref, got):
+            assert np.array_equal(r, y), f"replay {rep}: {op.name}"
+        st.step()
+        torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     for op, h, y in zip(ops, hostin, got):
         rq, rd = orc.quantize_act(h["x"])

@@ -197,3 +197,47 @@ def test_fused_step_matches(q8):
     st.step(fused=True)
     for op, r, b in zip(ops, ref, st.bufs):
         assert np.array_equal(r, host(b["y"])), op.name
+
+
+def test_batch_stack_graph_replay(q8, orc):
+    """The 16-stream step as bench.py runs it: captured into a HIP graph and replayed three
+    times, every replay checked bit for bit against the eager step, with eager work and
+    synchronizations between replays; sampled rows against the oracle."""
+    import torch
+
+    from block_quantized_weight_q8_amd.stack import Q8BatchStack, Q8DecodeStack
+
+    print("case: 2-layer stack + 5000-row head, 16 streams, graph replay", flush=True)
+    nb = 16
+    ops = synth.q8_stack_08b(layers=2, vocab=5000)
+    hostin = synth.q8_stack_inputs(ops, synth.TAG_TEST + 5)
+    batch = synth.q8_batch_inputs(ops, nb, synth.TAG_TEST + 6)
+    bs = Q8BatchStack(Q8DecodeStack(ops, hostin), batch)
+    bs.step()
+    ref = [host(b["y"]).copy() for b in bs.bufs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bs.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bs.step()
+    for rep in range(3):
+        for b in bs.bufs:
+            b["y"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        for op, r, b in zip(ops, ref, bs.bufs):
+            assert np.array_equal(host(b["y"]), r), f"replay {rep}: {op.name}"
+        bs.step()
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    for op, h, hb, r in zip(ops, hostin, batch, ref):
+        rows = np.unique(np.concatenate([[0, op.n - 1], rng.integers(0, op.n, 24)]))
+        for v in (0, nb - 1):
+            rq, rd = orc.quantize_act(hb["x"][v])
+            yr, S = orc.q8_gemv(h["qw"][rows], h["dw"][rows], rq, rd, hb["r"][v][rows] if op.residual else None)
+            err = np.abs(r[v][rows].astype(np.float64) - yr)
+            assert np.all(err <= 1e-5 * S), f"{op.name} stream {v}: {err.max()}"
