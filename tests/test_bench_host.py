@@ -41,3 +41,25 @@ def test_every_family_source_exists():
             d = "include" if fn.endswith(".h") else os.path.join("block_quantized_weight_q8_amd", "csrc")
             assert os.path.exists(os.path.join(bench.ROOT, d, fn)), (fam, fn)
         assert len(bench.kernel_source_digest(fam)) == 16
+
+
+def test_more_than_one_gpu_is_refused():
+    """One GPU only: --gpus N > 1 exits with an explanation before touching a device."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_help_lists_every_workload():
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--help"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0
+    for wl in bench.WORKLOADS:
+        assert wl in r.stdout, wl
