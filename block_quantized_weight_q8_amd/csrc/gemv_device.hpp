@@ -22,23 +22,73 @@ constexpr int kChunk = 1024;  // bytes of one row covered by one wave-wide 16-by
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // ---- cross-lane exchange with the lane at xor distance D --------------------
+// All in VALU lane-crossing forms, none through the LDS crossbar (ds_swizzle and
+// ds_bpermute, which these replaced, each cost a round trip on the critical
+// path of every reduction): DPP for 1, 2, 4 and 8, the gfx950 permlane swaps for
+// 16 and 32. Every form was checked on the GPU against lane i ^ D.
+template <int D>
+__device__ __forceinline__ int xchg_int(int v)
+{
+    static_assert(D == 1 || D == 2 || D == 4 || D == 8, "xchg: xor distance 1, 2, 4 or 8");
+    if constexpr (D == 1) {
+        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (D == 2) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (D == 4) {
+        // row_half_mirror (lane 7 - i within 8), then quad_perm [3,2,1,0]: (i ^ 3) ^ 7 = i ^ 4
+        const int m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+        return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);
+    } else {
+        return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8 = i ^ 8 in 16
+    }
+}
+
+// the value of the lane at xor distance D (1, 2, 4 or 8)
 template <int D>
 __device__ __forceinline__ float xchg(float v)
 {
-    const int iv = __builtin_bit_cast(int, v);
-    int r;
-    if constexpr (D == 1)
-        r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-    else if constexpr (D == 2)
-        r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-    else if constexpr (D == 4 || D == 8 || D == 16)
-        r = __builtin_amdgcn_ds_swizzle(iv, (D << 10) | 0x1F);  // bit mode: and 0x1F, xor D
-    else
-        r = __shfl_xor(iv, 32);
-    return __builtin_bit_cast(float, r);
+    return __builtin_bit_cast(float, xchg_int<D>(__builtin_bit_cast(int, v)));
 }
 
-__device__ __forceinline__ int xchg1_int(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+// {a, b} = {this lane's v, the v of the lane at xor distance D}, in an order that may
+// differ between lanes, for combining with a commutative operation (a + b, max):
+// at 16 and 32 a permlane swap of v with itself returns the two values, one per
+// result (odd rows / the upper half take them in the other order), so no lane
+// select is needed; a + b and max(a, b) have the same bits in both orders.
+template <int D>
+__device__ __forceinline__ void lane_pair(int v, int &a, int &b)
+{
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = (int)r[0];
+        b = (int)r[1];
+    } else if constexpr (D == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = (int)r[0];
+        b = (int)r[1];
+    } else {
+        a = v;
+        b = xchg_int<D>(v);
+    }
+}
+
+// v + (v of the lane at xor distance D), the same bits in both lanes
+template <int D>
+__device__ __forceinline__ float xsum(float v)
+{
+    int a, b;
+    lane_pair<D>(__builtin_bit_cast(int, v), a, b);
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// max(v, v of the lane at xor distance D)
+template <int D>
+__device__ __forceinline__ float xmax(float v)
+{
+    int a, b;
+    lane_pair<D>(__builtin_bit_cast(int, v), a, b);
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
 
 // Keep half of v[0..CNT) (the upper half when `upper`), add the partner's copy
 // of that half; the result is in v[0..CNT/2).
@@ -66,12 +116,12 @@ __device__ __forceinline__ float wave_reduce_rows(float (&v)[R], int lane)
     if constexpr (R >= 4) halve<2, R / 2>(v, lane & 2);
     if constexpr (R >= 8) halve<4, R / 4>(v, lane & 4);
     float s = v[0];
-    if constexpr (R < 2) s += xchg<1>(s);
-    if constexpr (R < 4) s += xchg<2>(s);
-    if constexpr (R < 8) s += xchg<4>(s);
-    s += xchg<8>(s);
-    s += xchg<16>(s);
-    s += xchg<32>(s);
+    if constexpr (R < 2) s = xsum<1>(s);
+    if constexpr (R < 4) s = xsum<2>(s);
+    if constexpr (R < 8) s = xsum<4>(s);
+    s = xsum<8>(s);
+    s = xsum<16>(s);
+    s = xsum<32>(s);
     return s;
 }
 
@@ -119,7 +169,7 @@ __device__ __forceinline__ int q8_block_sum(const int4 &w, const int4 &x)
     s = __builtin_amdgcn_sdot4(w.y, x.y, s, false);
     s = __builtin_amdgcn_sdot4(w.z, x.z, s, false);
     s = __builtin_amdgcn_sdot4(w.w, x.w, s, false);
-    return s + xchg1_int(s);
+    return s + xchg_int<1>(s);
 }
 
 // bf16: eight products of one lane's 16 bytes, summed into one chunk partial.
@@ -177,9 +227,9 @@ __device__ __forceinline__ float f16_chunk_dot(const int4 &wv, const float (&xf)
 __device__ __forceinline__ uint32_t quantize4(const float4 &v, float *d_out)
 {
     float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    m = fmaxf(m, xchg<1>(m));
-    m = fmaxf(m, xchg<2>(m));
-    m = fmaxf(m, xchg<4>(m));
+    m = xmax<1>(m);
+    m = xmax<2>(m);
+    m = xmax<4>(m);
     const float d = m / 127.0f;  // correctly rounded f32 division
     *d_out = d;
     uint32_t packed = 0;

@@ -23,8 +23,8 @@
 //    summed into a chunk partial before it joins the lane accumulator, so no
 //    f32 chain grows beyond eight terms plus one per chunk.
 //  * The R row sums of a wave are reduced together by a butterfly: exchanges
-//    at lane distance 1 and 2 (DPP quad_perm), 4, 8 and 16 (ds_swizzle in xor
-//    mode) and 32 (ds_bpermute). While two or more rows remain per lane, each
+//    at lane distance 1, 2, 4 and 8 (DPP) and 16 and 32 (the permlane swaps),
+//    none through the LDS crossbar. While two or more rows remain per lane, each
 //    step keeps half of them and adds the partner's copy of that half, so R
 //    rows cost R-1 exchanges plus the six of a single sum. The tree always
 //    pairs lanes at distance 1, 2, 4, ..., 32, so a row's bits do not depend on
@@ -81,24 +81,26 @@ __device__ __forceinline__ double sq4(const float4 &v)
     return (((double)v.x * v.x + (double)v.y * v.y) + (double)v.z * v.z) + (double)v.w * v.w;
 }
 
-// the f64 value of the lane at xor distance M: both halves through the f32
-// exchange (DPP for 1 and 2, swizzle for 4..16, permute for 32), which keeps
-// the LDS crossbar out of distances 1 and 2 and the address VGPRs out of 4..16
+// v + (the f64 v of the lane at xor distance M): both halves through the same
+// 32-bit lane pairing (lane_pair), so each result half comes from one lane; the
+// sum has the same bits in both lanes
 template <int M>
-__device__ __forceinline__ double xchg64(double v)
+__device__ __forceinline__ double xsum64(double v)
 {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const float lo = xchg<M>(__builtin_bit_cast(float, (uint32_t)u));
-    const float hi = xchg<M>(__builtin_bit_cast(float, (uint32_t)(u >> 32)));
-    return __builtin_bit_cast(double, ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32) |
-                                          __builtin_bit_cast(uint32_t, lo));
+    int alo, blo, ahi, bhi;
+    lane_pair<M>((int)(uint32_t)u, alo, blo);
+    lane_pair<M>((int)(uint32_t)(u >> 32), ahi, bhi);
+    const double a = __builtin_bit_cast(double, ((uint64_t)(uint32_t)ahi << 32) | (uint32_t)alo);
+    const double b = __builtin_bit_cast(double, ((uint64_t)(uint32_t)bhi << 32) | (uint32_t)blo);
+    return a + b;
 }
 
 __device__ __forceinline__ double block_sum8(double p)
 {
-    p += xchg64<1>(p);
-    p += xchg64<2>(p);
-    p += xchg64<4>(p);
+    p = xsum64<1>(p);
+    p = xsum64<2>(p);
+    p = xsum64<4>(p);
     return p;
 }
 
@@ -107,12 +109,12 @@ __device__ __forceinline__ double blocks_total(const double *s_bss, int64_t nb, 
 {
     double t = 0.0;
     for (int64_t b = lane; b < nb; b += kWave) t += s_bss[b];
-    t += xchg64<1>(t);
-    t += xchg64<2>(t);
-    t += xchg64<4>(t);
-    t += xchg64<8>(t);
-    t += xchg64<16>(t);
-    t += xchg64<32>(t);
+    t = xsum64<1>(t);
+    t = xsum64<2>(t);
+    t = xsum64<4>(t);
+    t = xsum64<8>(t);
+    t = xsum64<16>(t);
+    t = xsum64<32>(t);
     return t;
 }
 
@@ -474,11 +476,11 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
             const int j = lane & 31;
             const float a = silu_mul(s_gu[j], s_gu[32 + j]);
             float m = fabsf(a);
-            m = fmaxf(m, xchg<1>(m));
-            m = fmaxf(m, xchg<2>(m));
-            m = fmaxf(m, xchg<4>(m));
-            m = fmaxf(m, xchg<8>(m));
-            m = fmaxf(m, xchg<16>(m));
+            m = xmax<1>(m);
+            m = xmax<2>(m);
+            m = xmax<4>(m);
+            m = xmax<8>(m);
+            m = xmax<16>(m);
             const float d = m / 127.0f;
             float q = 0.0f;
             if (d != 0.0f) q = fminf(fmaxf(__builtin_rintf(a / d), -127.0f), 127.0f);
