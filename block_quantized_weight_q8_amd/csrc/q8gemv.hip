@@ -216,18 +216,28 @@ struct Batch {
 
 // Items j = 0..kBatch-1 of the batch starting at chunk c0: chunk c0 + j / R of
 // row j % R. Lanes past the row end load offset 0 (always in bounds) and are
-// masked when the batch is consumed. With XG the activation is read from global
-// memory here as well; otherwise it is read from LDS when consumed.
-template <Dt DT, int R, bool XG>
+// masked when the batch is consumed. With XG the activation is read from
+// global memory here as well; otherwise it is read from LDS when consumed.
+//
+// ALL (the f32-input kinds): items past the row's last chunk re-read that chunk
+// and are skipped when consumed, so every load is issued unconditionally
+// (nchunk >= 1 there) and the compiler can count the loads in flight. A load
+// under a condition, even a wave-uniform one, makes the wait for the
+// activation loads issued before it assume the condition was false, i.e. wait
+// for these weight loads as well, and the quantization of the activation then
+// starts only when the weights have arrived. The other kinds have nothing to
+// overlap with the weights and skip those items (the re-reads cost them time).
+template <Dt DT, int R, bool XG, bool ALL>
 __device__ __forceinline__ void load_batch(const RowRef (&rows)[R], const char *__restrict__ x,
                                            const uint16_t *__restrict__ dx, int64_t c0, int64_t nchunk,
                                            int64_t row_bytes, int64_t lane_off, Batch &b)
 {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-        const int64_t c = c0 + j / R;
-        const int r = j % R;
-        if (c < nchunk) {  // wave-uniform
+        const bool real = c0 + j / R < nchunk;  // wave-uniform
+        if (ALL || real) {
+            const int64_t c = real ? c0 + j / R : nchunk - 1;
+            const int r = j % R;
             const int64_t off = c * kChunk + lane_off;
             const int64_t o = off < row_bytes ? off : 0;
             b.w[j] = load16_stream(rows[r].w + o);
@@ -318,7 +328,11 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 // (waves 8..15); it writes no f32 output but the 32 codes qa[32b..] and the
 // scale da[b] of a = silu(gate) * up, formed and quantized exactly as
 // q8_silu_mul_quantize_act forms them from the two rows' f32 results.
-template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false>
+// XP: f32 activation passes requested before the weights (1 when one pass of
+// 4 values per thread covers K, else 4; values past them are read after the
+// weights are requested). Loads of passes past K are clamped duplicates, so
+// their number is chosen by the launch rather than fixed.
+template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false, int XP = 4>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
                                                             const uint16_t *__restrict__ dx,
                                                             const float *__restrict__ aux, float eps,
@@ -330,7 +344,7 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     constexpr bool FUSED = is_fused(DT);
     constexpr bool TWO = DT == Dt::Q8NORM || DT == Dt::Q8SILU;  // a second f32 input per value
     constexpr int kThreadsPerGroup = WAVES * kWave;
-    constexpr int kXPasses = 4;  // f32 activation passes requested before the weights
+    constexpr int kXPasses = XP;  // f32 activation passes requested before the weights
     __shared__ __align__(16) int8_t s_qx[FUSED ? kMaxFusedK : 16];
     __shared__ float s_dx[FUSED ? kMaxFusedK / 32 : 4];
     __shared__ double s_bss[DT == Dt::Q8NORM ? kMaxFusedK / 32 : 1];
@@ -403,7 +417,15 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     }
 
     Batch cur, nxt;
-    if (has_rows && nchunk > 0) load_batch<DT, R, !FUSED>(rows, x, dx, 0, nchunk, row_bytes, lane_off, cur);
+    if constexpr (FUSED) {
+        // K >= 32 here and a wave without rows has row 0's table, so the first batch
+        // is requested unconditionally (such a wave reads row 0 and leaves after the
+        // quantization): a condition here would make the quantization's wait for
+        // the activation include these loads
+        load_batch<DT, R, false, true>(rows, x, dx, 0, nchunk, row_bytes, lane_off, cur);
+    } else {
+        if (has_rows && nchunk > 0) load_batch<DT, R, true, false>(rows, x, dx, 0, nchunk, row_bytes, lane_off, cur);
+    }
 
     if constexpr (FUSED) {
         const float *xf = static_cast<const float *>(xv);
@@ -457,7 +479,8 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     const float even = (lane & 1) ? 0.0f : 1.0f;  // Q8_0: the even lane of a pair applies the scale
 
     for (int64_t c0 = 0; c0 < nchunk; c0 += CB) {
-        if (c0 + CB < nchunk) load_batch<DT, R, !FUSED>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);
+        if (c0 + CB < nchunk)
+            load_batch<DT, R, !FUSED, FUSED>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);
         compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
         cur = nxt;
     }
@@ -576,7 +599,7 @@ bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
 
-template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false>
+template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false, int XP = 4>
 hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const float *aux, float eps, int64_t K,
                        int64_t n_total, hipStream_t s, int8_t *qa = nullptr, uint16_t *da = nullptr)
 {
@@ -596,7 +619,7 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const 
                     &pc.dw[3],  &pc.y[0],   &pc.y[1],   &pc.y[2],   &pc.y[3],   &pc.res[0], &pc.res[1],
                     &pc.res[2], &pc.res[3], &pc.end[0], &pc.end[1], &pc.end[2], &xc,       &dxc,
                     &auxc,      &epsc,      &kc,        &nc,        &qac,       &dac};
-    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES, EPI, PRES>);
+    const void *fn = reinterpret_cast<const void *>(&gemv_kernel<DT, R, WAVES, EPI, PRES, XP>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(WAVES * kWave), args, 0, s);
 }
 
@@ -653,12 +676,26 @@ struct Prologue {
     float eps;         // Q8NORM: added to the mean square
 };
 
+// activation passes of an f32-input launch: one when it covers K
+constexpr bool one_pass(int64_t K, int threads) { return K <= 4 * (int64_t)threads; }
+
+template <Dt DT, int R, int W, bool PRES>
+hipError_t launch_xp(const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K, int64_t n_total,
+                     hipStream_t s)
+{
+    if constexpr (is_fused(DT)) {
+        if (one_pass(K, W * kWave))
+            return launch_gemv<DT, R, W, false, PRES, 1>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+    }
+    return launch_gemv<DT, R, W, false, PRES, 4>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+}
+
 template <Dt DT, int R, int W>
 hipError_t launch_res(bool pres, const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K,
                       int64_t n_total, hipStream_t s)
 {
-    return pres ? launch_gemv<DT, R, W, false, true>(p, x, dx, pr.aux, pr.eps, K, n_total, s)
-                : launch_gemv<DT, R, W, false, false>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+    return pres ? launch_xp<DT, R, W, true>(p, x, dx, pr, K, n_total, s)
+                : launch_xp<DT, R, W, false>(p, x, dx, pr, K, n_total, s);
 }
 
 template <Dt DT, int W>
@@ -837,11 +874,13 @@ q8g_status gateup_silu(int kind, const int8_t *qg, const uint16_t *dg, const int
     p.end[1] = 2 * F;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // with K == 0 no activation is read: gate = up = 0, a = 0
+    const bool norm = kind == kKindNorm && K > 0;
     const hipError_t e =
-        (kind == kKindNorm && K > 0)
-            ? launch_gemv<Dt::Q8NORM, 4, 16, true>(p, x, nullptr, gamma, eps, K, 2 * F, s, qa, da)
-            : launch_gemv<Dt::Q8, 4, 16, true>(p, kind == Q8G_Q8_0 ? x : nullptr, kind == Q8G_Q8_0 ? dx : nullptr,
-                                               nullptr, 0.0f, K, 2 * F, s, qa, da);
+        norm && one_pass(K, 16 * kWave)
+            ? launch_gemv<Dt::Q8NORM, 4, 16, true, false, 1>(p, x, nullptr, gamma, eps, K, 2 * F, s, qa, da)
+        : norm ? launch_gemv<Dt::Q8NORM, 4, 16, true, false, 4>(p, x, nullptr, gamma, eps, K, 2 * F, s, qa, da)
+               : launch_gemv<Dt::Q8, 4, 16, true>(p, kind == Q8G_Q8_0 ? x : nullptr, kind == Q8G_Q8_0 ? dx : nullptr,
+                                                  nullptr, 0.0f, K, 2 * F, s, qa, da);
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
 

@@ -208,15 +208,52 @@ def fused_prologue_loads(K, threads, passes, two):
     assert used == set(range(K))
 
 
-@pytest.mark.parametrize("k", [32, 96, 1024, 2080, 3584, 16384])
+def launch_passes(k, threads):
+    """Activation passes the launch picks: one when one pass of 4 values per thread covers K."""
+    return 1 if k <= 4 * threads else 4
+
+
+@pytest.mark.parametrize("k", [32, 96, 1024, 2048, 2080, 3584, 4096, 16384])
 @pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("two", [None, "norm", "silu"])
 def test_fused_prologue_addressing(k, waves, two):
-    fused_prologue_loads(k, waves * 64, 4, two)
+    for passes in (1, 4):  # the launch's choice and the other template, both valid for any K
+        fused_prologue_loads(k, waves * 64, passes, two)
+    assert launch_passes(k, waves * 64) in (1, 4)
+
+
+def weight_batch_items(K, R, kbatch=4, chunk=1024):
+    """The first weight batch of an f32-input launch: item j reads chunk min(j / R, nchunk - 1)
+    of row j % R (clamped, so that every load is issued), lanes past the row end read offset 0;
+    items past the last chunk are skipped when consumed, so each real (row, chunk) is consumed
+    exactly once."""
+    nchunk = (K + chunk - 1) // chunk
+    assert nchunk >= 1
+    consumed = []
+    for j in range(kbatch):
+        c_real = j // R
+        c = c_real if c_real < nchunk else nchunk - 1
+        for lane in range(64):
+            off = c * chunk + 16 * lane
+            o = off if off < K else 0
+            assert 0 <= o and o + 16 <= K  # the 16 bytes lie inside the row
+        if c_real < nchunk:
+            consumed.append((j % R, c_real))
+    expect = [(r, c) for c in range(min(nchunk, kbatch // R)) for r in range(R)]
+    assert sorted(consumed) == sorted(expect)
+
+
+@pytest.mark.parametrize("k", [32, 96, 1024, 2048, 3584, 5120])
+@pytest.mark.parametrize("r", [1, 2, 4])
+def test_first_weight_batch_addressing(k, r):
+    weight_batch_items(k, r)
 
 
 def test_fused_prologue_constants():
     src = open(os.path.join(CSRC, "q8gemv.hip")).read()
-    assert re.search(r"constexpr int kXPasses = 4;", src)
+    assert re.search(r"constexpr int kXPasses = XP;", src)
+    assert "constexpr bool one_pass(int64_t K, int threads) { return K <= 4 * (int64_t)threads; }" in src
     assert re.search(r"constexpr int kMaxFusedK = 16384;", src)
     assert "e < K ? e : K - 4" in src
+    assert "const bool real = c0 + j / R < nchunk;" in src
+    assert "const int64_t c = real ? c0 + j / R : nchunk - 1;" in src
