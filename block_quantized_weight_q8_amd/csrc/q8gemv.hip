@@ -252,6 +252,17 @@ __device__ __forceinline__ void load_batch(const RowRef (&rows)[R], const char *
     }
 }
 
+// The accumulators as they stand, before anything that follows: an empty
+// volatile asm that reads and writes them. A scheduling barrier orders the
+// machine instructions only; arithmetic can be placed after a later load before
+// that, which keeps the batch it reads live across the load.
+template <int R>
+__device__ __forceinline__ void settle(float (&acc)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) asm volatile("" : "+v"(acc[r]));
+}
+
 // Consume a batch. Q8_0: one exact int32 block sum per item (v_dot4 + one DPP
 // add), scaled by dw*dx (exact in f32) with one fma; the odd lane of each block
 // pair and lanes past the row end add zero. bf16: eight exact products summed
@@ -478,11 +489,31 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
     const float even = (lane & 1) ? 0.0f : 1.0f;  // Q8_0: the even lane of a pair applies the scale
 
-    for (int64_t c0 = 0; c0 < nchunk; c0 += CB) {
-        if (c0 + CB < nchunk)
-            load_batch<DT, R, !FUSED, FUSED>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);
+    // Rows of several batches: two batches a trip, cur and nxt taking turns, in a
+    // straight-line body, so no register copy (which would wait for the loads just
+    // issued) stands between a batch's request and its use. The loads are
+    // unconditional (a partial batch re-reads its last chunk), so the wait before
+    // each compute counts only the batch it consumes, and a scheduling barrier
+    // keeps a batch's requests ahead of the compute that precedes them in program
+    // order, so that the other batch stays in flight in full.
+    int64_t c0 = 0;
+    for (; c0 + 2 * CB < nchunk; c0 += 2 * CB) {
+        load_batch<DT, R, !FUSED, true>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);
+        __builtin_amdgcn_sched_barrier(0);
         compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
-        cur = nxt;
+        settle(acc);
+        load_batch<DT, R, !FUSED, true>(rows, x, dx, c0 + 2 * CB, nchunk, row_bytes, lane_off, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch<DT, R, !FUSED>(nxt, s_qx, s_dx, c0 + CB, nchunk, row_bytes, lane_off, even, acc);
+    }
+    // the row's last one or two batches (cur holds chunk c0 on)
+    if (c0 + CB < nchunk) {
+        load_batch<DT, R, !FUSED, true>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
+        compute_batch<DT, R, !FUSED>(nxt, s_qx, s_dx, c0 + CB, nchunk, row_bytes, lane_off, even, acc);
+    } else if (c0 < nchunk) {
+        compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
     }
     if constexpr (EPI) {
         // s_gu[0..31]: gate rows 32b.., s_gu[32..63]: up rows 32b..

@@ -249,6 +249,60 @@ def test_first_weight_batch_addressing(k, r):
     weight_batch_items(k, r)
 
 
+def row_batch_schedule(nchunk, cb):
+    """The main loop of a wave's rows, batch by batch: cur holds the batch at chunk 0 on
+    entry; each trip requests the next batch into nxt, consumes cur, requests the one after
+    into cur, consumes nxt; then the last one or two batches. Returns the (kind, buffer, c0)
+    events in program order."""
+    ev = [("load", "cur", 0)] if nchunk > 0 else []
+    c0 = 0
+    while c0 + 2 * cb < nchunk:
+        ev += [("load", "nxt", c0 + cb), ("use", "cur", c0), ("load", "cur", c0 + 2 * cb), ("use", "nxt", c0 + cb)]
+        c0 += 2 * cb
+    if c0 + cb < nchunk:
+        ev += [("load", "nxt", c0 + cb), ("use", "cur", c0), ("use", "nxt", c0 + cb)]
+    elif c0 < nchunk:
+        ev += [("use", "cur", c0)]
+    return ev
+
+
+@pytest.mark.parametrize("cb", [1, 2, 4, 8])
+def test_row_batch_schedule(cb):
+    """Every chunk of the row is consumed exactly once, from the buffer that holds it; a
+    buffer is refilled only after its batch was consumed; at most two batches are in flight;
+    every load of a batch is in bounds (chunks past the end re-read the last one), and only
+    the row's last batch re-reads."""
+    for nchunk in range(0, 24):
+        held, pending, consumed, rereads = {}, set(), [], 0
+        for kind, b, c0 in row_batch_schedule(nchunk, cb):
+            if kind == "load":
+                assert b not in pending, "a buffer refilled before its batch was consumed"
+                assert 0 <= c0 < nchunk
+                items = [c0 + i for i in range(cb)]
+                clamped = [c if c < nchunk else nchunk - 1 for c in items]
+                assert all(0 <= c < nchunk for c in clamped)
+                rereads += sum(c >= nchunk for c in items)
+                held[b] = c0
+                pending.add(b)
+                assert len(pending) <= 2
+            else:
+                assert held.get(b) == c0 and b in pending
+                pending.discard(b)
+                consumed += [c for c in range(c0, c0 + cb) if c < nchunk]
+        assert consumed == list(range(nchunk))
+        assert not pending
+        assert rereads == (0 if nchunk == 0 else (-nchunk) % cb)
+
+
+def test_row_batch_schedule_matches_source():
+    src = open(os.path.join(CSRC, "q8gemv.hip")).read()
+    assert "for (; c0 + 2 * CB < nchunk; c0 += 2 * CB) {" in src
+    assert "load_batch<DT, R, !FUSED, true>(rows, x, dx, c0 + CB, nchunk, row_bytes, lane_off, nxt);" in src
+    assert "load_batch<DT, R, !FUSED, true>(rows, x, dx, c0 + 2 * CB, nchunk, row_bytes, lane_off, cur);" in src
+    assert "if (c0 + CB < nchunk) {" in src
+    assert "} else if (c0 < nchunk) {" in src
+
+
 def test_fused_prologue_constants():
     src = open(os.path.join(CSRC, "q8gemv.hip")).read()
     assert re.search(r"constexpr int kXPasses = XP;", src)
