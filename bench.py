@@ -33,8 +33,8 @@ Other workloads (per-call figures; a step is one call):
   q8-layers-0.8b        the 24 decode layers of the 0.8B shape with their neighbour steps and the real
                         data flow through the residual stream (attention output a seeded stand-in):
                         per layer QKV with its normalization, out (+residual), gate+up with silu*up
-                        quantized in its epilogue, down (+residual); then final norm and head. 98
-                        launches per token fused, 194 unfused (timed too; both bit-identical)
+                        quantized in its epilogue, down (+residual); then the head with the final
+                        norm in its prologue. 97 launches per token fused, 194 unfused (timed too; both bit-identical)
   q8-layers-0.8b-b16    the same layers for 16 decode streams at once: per layer 4 q8_gemv_batch launches
                         and 4 batched neighbour-step launches (normalize+quantize, quantize,
                         normalize+quantize, silu*up+quantize); 194 launches per step of 16 tokens
@@ -309,7 +309,7 @@ def run_stack(args, torch, q8, np):
     for i, b in enumerate(stack.bufs):
         if not torch.equal(b["y"], ref[i]):
             raise SystemExit(f"parity: fused output of {ops[i].name} differs from quantize + gemv")
-    n_launch_fused = sum(1 if op.n <= stack.FUSED_MAX_ROWS else 2 for op in ops)
+    n_launch_fused = len(ops)
     log(f"[bench] fused quantize+GEMV per projection ({n_launch_fused} launches), graph replay: "
         f"{t_fused * 1e6:.1f} us/token; outputs bit-identical")
 
@@ -371,7 +371,7 @@ def run_stack(args, torch, q8, np):
     else:
         groups = {}
         for i, op in enumerate(ops):
-            fused = mode == "fused" and op.n <= stack.FUSED_MAX_ROWS
+            fused = mode == "fused"
             r, w = q8.gemv_config(q8.Q8G_Q8_0_F32 if fused else q8.Q8G_Q8_0, op.n, op.k)
             # a launch with a residual runs its own kernel variant (the residual requested early)
             groups.setdefault((fused, r, w, op.residual), []).append(i)
@@ -398,8 +398,7 @@ def run_stack(args, torch, q8, np):
                     "avg_launch_us": round(dt_ * 1e6, 3), "bytes_per_launch": round(db),
                     "launches_per_step": dc, "traffic": traffic_for(dname)}
     launches = {"fused": n_launch_fused, "graph": 2 * len(ops), "decode_stack": 1}[mode]
-    mode = {"fused": "hipGraph, one fused quantize+GEMV launch per projection (quantize + GEMV for the head; "
-                     "98 launches per token)",
+    mode = {"fused": "hipGraph, one fused quantize+GEMV launch per projection (97 launches per token)",
             "graph": "hipGraph, q8_quantize_act + GEMV per projection (194 launches per token)",
             "decode_stack": "one q8_decode_stack launch per token"}[mode]
 

@@ -14,9 +14,10 @@ seeded stand-in per layer). One token, fused (4 launches per layer):
     out    gemv_stacked(attn f32), residual h, in place          h += W_o attn
     MLP    q8_gateup_rmsnorm_silu_quantize(h, gamma_mlp)         codes of silu(gate) up
     down   q8_gemv(codes), residual h, in place                  h += W_d a
-then the final normalization (q8_rmsnorm_quantize_act) and the head (q8_gemv).
+then the head with the final normalization in its prologue (gemv_stacked_rmsnorm).
 Unfused (8 launches per layer) runs every normalization, activation and quantize as
-its own launch. Both give the same bits.
+its own launch, and the head as q8_rmsnorm_quantize_act then q8_gemv. Both give the
+same bits.
 
 Q8BatchLayerChain runs the same layers for nb decode streams at once over the same
 weights (8 launches per layer): every projection is one q8_gemv_batch over the nb
@@ -130,13 +131,17 @@ class Q8LayerChain:
             b = self._b(l, 3)
             q8_gemv(b["qw"], b["dw"], self.qa, self.da, y=self.h, residual=self.h, stream=stream)
         snap("h_out", self.layers - 1, self.h)
-        q8_rmsnorm_quantize_act(self.h, self.gamma_final, eps, qx=self.qx, dx=self.dx, stream=stream)
         hb = self.head()
-        q8_gemv(hb["qw"], hb["dw"], self.qx, self.dx, y=hb["y"], stream=stream)
+        if fused:
+            gemv_stacked_rmsnorm([{"w": hb["qw"], "dw": hb["dw"], "y": hb["y"]}], self.h, self.gamma_final, eps,
+                                 stream=stream)
+        else:
+            q8_rmsnorm_quantize_act(self.h, self.gamma_final, eps, qx=self.qx, dx=self.dx, stream=stream)
+            q8_gemv(hb["qw"], hb["dw"], self.qx, self.dx, y=hb["y"], stream=stream)
         snap("logits", self.layers, hb["y"])
 
     def launches_per_token(self, fused: bool = True) -> int:
-        return self.layers * (4 if fused else 8) + 2
+        return self.layers * 4 + 1 if fused else self.layers * 8 + 2
 
 
 class Q8BatchLayerChain:

@@ -106,14 +106,12 @@ class Q8DecodeStack:
         b = self.bufs[i]
         gemv_stacked(b["parts"], b["x"], stream=stream)
 
-    # Above this many rows the fused launch loses: each of its workgroups quantizes
-    # the whole input again for only 16 rows of output, and on MI355X the 151936-row
-    # output head took 38.9 us fused against 26.9 + 1.6 us as quantize + GEMV.
-    FUSED_MAX_ROWS = 65536
-
     def step(self, stream=None, fused=False):
+        # fused: every projection one launch, the 151936-row head included (each of its
+        # workgroups quantizes the whole input again for 16 rows of output, while its first
+        # weights are in flight; on MI355X 27.0 us against 27.2 + 1.6 us as quantize + GEMV)
         for i, op in enumerate(self.ops):
-            if fused and op.n <= self.FUSED_MAX_ROWS:
+            if fused:
                 self.launch_op_fused(i, stream)
             else:
                 self.launch_op(i, stream)

@@ -217,12 +217,11 @@ def q8_gateup_epilogue_bytes(f: int, k: int) -> int:
 def q8_layers_08b_bytes(layers: int = 24, hidden: int = 1024, ffn: int = 3584, vocab: int = 151936) -> int:
     """Algorithmic bytes of one token of the fused decode-layer chain: per layer the QKV launch
     with its normalization, the out projection (f32 input, residual), the gate+up launch with
-    its epilogue and the down projection (codes input, residual); then the final normalization
-    with quantize and the head."""
+    its epilogue and the down projection (codes input, residual); then the head with the final
+    normalization in its prologue."""
     per_layer = (q8_rmsnorm_gemv_bytes(4096, hidden) + q8_gemv_f32x_bytes(hidden, 2048, residual=True)
                  + q8_gateup_epilogue_bytes(ffn, hidden) + q8_gemv_bytes(hidden, ffn, residual=True))
-    head = 8 * hidden + hidden + 2 * (hidden // QBLOCK) + q8_gemv_bytes(vocab, hidden)
-    return layers * per_layer + head
+    return layers * per_layer + q8_rmsnorm_gemv_bytes(vocab, hidden)
 
 
 def q8_quantize_bytes(k: int) -> int:
