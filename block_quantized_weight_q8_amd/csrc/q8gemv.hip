@@ -219,14 +219,15 @@ struct Batch {
 // masked when the batch is consumed. With XG the activation is read from
 // global memory here as well; otherwise it is read from LDS when consumed.
 //
-// ALL (the f32-input kinds): items past the row's last chunk re-read that chunk
-// and are skipped when consumed, so every load is issued unconditionally
-// (nchunk >= 1 there) and the compiler can count the loads in flight. A load
-// under a condition, even a wave-uniform one, makes the wait for the
-// activation loads issued before it assume the condition was false, i.e. wait
-// for these weight loads as well, and the quantization of the activation then
-// starts only when the weights have arrived. The other kinds have nothing to
-// overlap with the weights and skip those items (the re-reads cost them time).
+// ALL: items past the row's last chunk re-read that chunk and are skipped when
+// consumed, so every load is issued unconditionally (nchunk >= 1) and the
+// compiler can count the loads in flight. A load under a condition, even a
+// wave-uniform one, makes the wait for the loads issued before it assume the
+// condition was false, i.e. wait for these loads as well. Used for every batch
+// after the first (the row loop), and for the first batch of the f32-input
+// kinds, whose activation quantization then overlaps the weights in flight. The
+// first batch of the other kinds has nothing to overlap with and skips those
+// items (the re-reads cost them time).
 template <Dt DT, int R, bool XG, bool ALL>
 __device__ __forceinline__ void load_batch(const RowRef (&rows)[R], const char *__restrict__ x,
                                            const uint16_t *__restrict__ dx, int64_t c0, int64_t nchunk,
