@@ -102,6 +102,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_gemv_silu_mul.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
     lib.q8_gateup_silu_quantize.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P]
     lib.q8_gateup_rmsnorm_silu_quantize.argtypes = [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_float, _I64, _P, _P, _P]
+    lib.q8_gateup_silu.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P]
+    lib.q8_gateup_rmsnorm_silu.argtypes = [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_float, _I64, _P, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
     lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
@@ -113,6 +115,7 @@ def load_library(path: str = LIB_PATH):
                "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
                "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
+               "q8_gateup_silu", "q8_gateup_rmsnorm_silu",
                "q8_rmsnorm_quantize_act_batch", "q8_silu_mul_quantize_act_batch"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -391,6 +394,32 @@ def q8_gateup_silu_quantize(w_gate, dw_gate, w_up, dw_up, x, dx=None, gamma=None
         fn = "q8_gateup_rmsnorm_silu_quantize"
     _check(fn, st)
     return qa, da
+
+
+def q8_gateup_silu(w_gate, dw_gate, w_up, dw_up, x, dx=None, gamma=None, eps=None, a=None, stream=None):
+    """Gate+up projection (Q8_0, F rows each) with a = silu(gate) * up formed in the epilogue and
+    returned in f32 [F] (the input of an f32-input down projection, which quantizes it). x as for
+    q8_gateup_silu_quantize: int8 codes [K] with dx, or f32 [K] with gamma and eps."""
+    if w_gate.dim() != 2 or w_up.shape != w_gate.shape:
+        raise ValueError("w_gate and w_up must both be [F, K]")
+    f, k = w_gate.shape
+    if a is None:
+        a = torch.empty(f, dtype=torch.float32, device=w_gate.device)
+    lib = load_library()
+    common = (_ptr(w_gate, "w_gate", _I8), _ptr(dw_gate, "dw_gate", _H16, (f, k // 32)), _ptr(w_up, "w_up", _I8),
+              _ptr(dw_up, "dw_up", _H16, (f, k // 32)), f)
+    if gamma is None:
+        st = lib.q8_gateup_silu(*common, _ptr(x, "x", _I8, (k,)), _ptr(dx, "dx", _H16, (k // 32,)), k,
+                                _ptr(a, "a", _F32, (f,)), _stream(stream))
+        fn = "q8_gateup_silu"
+    else:
+        if eps is None:
+            raise ValueError("eps is required with gamma")
+        st = lib.q8_gateup_rmsnorm_silu(*common, _ptr(x, "x", _F32, (k,)), _ptr(gamma, "gamma", _F32, (k,)),
+                                        float(eps), k, _ptr(a, "a", _F32, (f,)), _stream(stream))
+        fn = "q8_gateup_rmsnorm_silu"
+    _check(fn, st)
+    return a
 
 
 def _q8_parts(parts, k):

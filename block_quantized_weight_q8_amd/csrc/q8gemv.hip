@@ -334,25 +334,29 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 // its order are the same for all three kinds, so a Q8F32 launch is
 // bit-identical to q8_quantize_act followed by a Q8 launch.
 //
-// EPI: the gate+up projection with the gated activation and its quantization in
-// the epilogue (parts 0 and 1 are gate and up, F = n_total / 2 rows each).
-// Workgroup b owns gate rows 32b..32b+31 (waves 0..7) and the same up rows
-// (waves 8..15); it writes no f32 output but the 32 codes qa[32b..] and the
-// scale da[b] of a = silu(gate) * up, formed and quantized exactly as
-// q8_silu_mul_quantize_act forms them from the two rows' f32 results.
+// EPI (nonzero): the gate+up projection with the gated activation in the
+// epilogue (parts 0 and 1 are gate and up, F = n_total / 2 rows each). A
+// workgroup owns P = R * WAVES / 2 gate rows P*b.. (its first WAVES / 2 waves)
+// and the same up rows (the other half), and forms a = silu(gate) * up from the
+// rows' f32 results as q8_silu_mul_quantize_act forms it. EPI 1 (R = 4, 16
+// waves, P = 32): a is quantized as one Q8_0 block, written as the 32 codes
+// qa[32b..] and the scale da[b]. EPI 2: a itself is written, in f32, to part
+// 0's output (y0[P*b + j]); nothing else is written.
 // XP: f32 activation passes requested before the weights (1 when one pass of
 // 4 values per thread covers K, else 4; values past them are read after the
 // weights are requested). Loads of passes past K are clamped duplicates, so
 // their number is chosen by the launch rather than fixed.
-template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false, int XP = 4>
+template <Dt DT, int R, int WAVES, int EPI = 0, bool PRES = false, int XP = 4>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
                                                             const uint16_t *__restrict__ dx,
                                                             const float *__restrict__ aux, float eps,
                                                             int64_t K, int64_t n_total, int8_t *__restrict__ qa,
                                                             uint16_t *__restrict__ da)
 {
-    static_assert(!EPI || (R == 4 && WAVES == 16), "the epilogue needs 32 gate and 32 up rows per workgroup");
-    static_assert(!(EPI && PRES), "the epilogue kind has no residual");
+    static_assert(EPI != 1 || (R == 4 && WAVES == 16), "the quantizing epilogue needs 32 gate and 32 up rows");
+    static_assert(EPI == 0 || (WAVES % 2 == 0 && R * WAVES / 2 <= 32), "gate and up waves in equal numbers");
+    static_assert(!(EPI && PRES), "the epilogue kinds have no residual");
+    constexpr int P = R * WAVES / 2;  // EPI: gate+up row pairs per workgroup
     constexpr bool FUSED = is_fused(DT);
     constexpr bool TWO = DT == Dt::Q8NORM || DT == Dt::Q8SILU;  // a second f32 input per value
     constexpr int kThreadsPerGroup = WAVES * kWave;
@@ -365,9 +369,9 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
     // wave-uniform by construction; readfirstlane lets the compiler keep the
     // row bookkeeping and the part table in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t row0 = !EPI       ? ((int64_t)blockIdx.x * WAVES + wave) * R
-                         : wave < 8 ? 32 * (int64_t)blockIdx.x + R * wave
-                                    : n_total / 2 + 32 * (int64_t)blockIdx.x + R * (wave - 8);
+    const int64_t row0 = !EPI               ? ((int64_t)blockIdx.x * WAVES + wave) * R
+                         : wave < WAVES / 2 ? P * (int64_t)blockIdx.x + R * wave
+                                            : n_total / 2 + P * (int64_t)blockIdx.x + R * (wave - WAVES / 2);
     const bool has_rows = row0 < n_total;  // wave-uniform
     if (!FUSED && !has_rows) return;
 
@@ -517,14 +521,18 @@ __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const 
         compute_batch<DT, R, !FUSED>(cur, s_qx, s_dx, c0, nchunk, row_bytes, lane_off, even, acc);
     }
     if constexpr (EPI) {
-        // s_gu[0..31]: gate rows 32b.., s_gu[32..63]: up rows 32b..
-        __shared__ __align__(16) float s_gu[64];
+        // s_gu[0..P-1]: gate rows P*b.., s_gu[P..2P-1]: the same up rows
+        __shared__ __align__(16) float s_gu[2 * P];
         const float total = wave_reduce_rows<R>(acc, lane);
 #pragma unroll
         for (int i = 0; i < R; ++i)
-            if (lane == lane_of<R>(i)) s_gu[(wave < 8 ? 0 : 32) + R * (wave & 7) + i] = total;
+            if (lane == lane_of<R>(i)) s_gu[(wave < WAVES / 2 ? 0 : P) + R * (wave % (WAVES / 2)) + i] = total;
         __syncthreads();
-        if (wave == 0) {
+        if constexpr (EPI == 2) {
+            // a[P*b + j] = silu(gate) * up: wave 0's first row is gate row P*b, so its
+            // output pointer is a + P*b
+            if (wave == 0 && lane < P) rows[0].y[lane] = silu_mul(s_gu[lane], s_gu[P + lane]);
+        } else if (wave == 0) {
             // one value per lane (lanes 32..63 repeat 0..31): a = silu(gate) * up, then
             // the block's quantization with quantize4's arithmetic (max |a| over the
             // 32 lanes, d = fl32(max / 127), q = rint(fl32(a / d)))
@@ -631,13 +639,13 @@ bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
 
-template <Dt DT, int R, int WAVES, bool EPI = false, bool PRES = false, int XP = 4>
+template <Dt DT, int R, int WAVES, int EPI = 0, bool PRES = false, int XP = 4>
 hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const float *aux, float eps, int64_t K,
                        int64_t n_total, hipStream_t s, int8_t *qa = nullptr, uint16_t *da = nullptr)
 {
     const int64_t rows_per_block = (int64_t)R * WAVES;
-    // EPI: one workgroup per 32 gate rows and the matching 32 up rows
-    const int64_t blocks = EPI ? n_total / 64 : (n_total + rows_per_block - 1) / rows_per_block;
+    // EPI: one workgroup per R * WAVES / 2 gate rows and the matching up rows
+    const int64_t blocks = EPI ? n_total / rows_per_block : (n_total + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     Parts pc = p;
     const void *xc = x;
@@ -717,9 +725,9 @@ hipError_t launch_xp(const Parts &p, const void *x, const uint16_t *dx, Prologue
 {
     if constexpr (is_fused(DT)) {
         if (one_pass(K, W * kWave))
-            return launch_gemv<DT, R, W, false, PRES, 1>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+            return launch_gemv<DT, R, W, 0, PRES, 1>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
     }
-    return launch_gemv<DT, R, W, false, PRES, 4>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+    return launch_gemv<DT, R, W, 0, PRES, 4>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
 }
 
 template <Dt DT, int R, int W>
@@ -860,35 +868,59 @@ q8g_status run(int dt, const q8g_part *parts, int nparts, const void *x, const u
 
 bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }  // finite, not negative (NaN fails)
 
-// Gate+up projection (F rows each, Q8_0) with silu(gate) * up quantized in the
-// epilogue. kind: Q8G_Q8_0 (x = codes + dx) or kKindNorm (x f32, normalized with
-// gamma and eps in the prologue).
+// Launch shape of the f32 silu(gate) * up epilogue (EPI 2): R rows per wave,
+// W waves, R * W / 2 gate+up row pairs per workgroup (a divisor of 32)
+#ifndef Q8G_SILU_ROWS
+#define Q8G_SILU_ROWS 2
+#endif
+#ifndef Q8G_SILU_WAVES
+#define Q8G_SILU_WAVES 8
+#endif
+static_assert(32 % (Q8G_SILU_ROWS * Q8G_SILU_WAVES / 2) == 0, "row pairs per workgroup divide 32");
+
+template <Dt DT, int R, int W, int EPI>
+hipError_t launch_epi(const Parts &p, const void *x, const uint16_t *dx, const float *gamma, float eps, int64_t K,
+                      int64_t F, hipStream_t s, int8_t *qa, uint16_t *da)
+{
+    if constexpr (is_fused(DT))
+        if (one_pass(K, W * kWave)) return launch_gemv<DT, R, W, EPI, false, 1>(p, x, dx, gamma, eps, K, 2 * F, s, qa, da);
+    return launch_gemv<DT, R, W, EPI, false, 4>(p, x, dx, gamma, eps, K, 2 * F, s, qa, da);
+}
+
+// Gate+up projection (F rows each, Q8_0) with a = silu(gate) * up formed in the
+// epilogue: quantized there (qa, da; a == nullptr) or written in f32 (a; qa and
+// da nullptr). kind: Q8G_Q8_0 (x = codes + dx) or kKindNorm (x f32, normalized
+// with gamma and eps in the prologue).
 q8g_status gateup_silu(int kind, const int8_t *qg, const uint16_t *dg, const int8_t *qu, const uint16_t *du, int64_t F,
                        const void *x, const uint16_t *dx, const float *gamma, float eps, int8_t *qa, uint16_t *da,
-                       int64_t K, void *stream)
+                       float *a, int64_t K, void *stream)
 {
     if (F < 0 || F % 32 || F > kMaxElems / 2 || K < 0 || K % 32 || K > kMaxElems) return Q8G_ERR_SHAPE;
     if (K > 0 && F > kMaxElems / K) return Q8G_ERR_SHAPE;
     if (kind == kKindNorm && (K > kMaxFusedK)) return Q8G_ERR_SHAPE;
     if (kind == kKindNorm && !eps_ok(eps)) return Q8G_ERR_ARG;
     if (F == 0) return Q8G_OK;
-    if (!qa || !da) return Q8G_ERR_NULL;
+    const bool f32_out = a != nullptr;
+    if (!f32_out && (!qa || !da)) return Q8G_ERR_NULL;
     if (K > 0 && (!qg || !dg || !qu || !du || !x || (kind == Q8G_Q8_0 && !dx) || (kind == kKindNorm && !gamma)))
         return Q8G_ERR_NULL;
     if (!aligned(qg, 16) || !aligned(qu, 16) || !aligned(dg, 2) || !aligned(du, 2) || !aligned(x, 16) ||
-        !aligned(qa, 16) || !aligned(da, 2) || (kind == Q8G_Q8_0 && !aligned(dx, 2)) ||
-        (kind == kKindNorm && !aligned(gamma, 16)))
+        (!f32_out && (!aligned(qa, 16) || !aligned(da, 2))) || (f32_out && !aligned(a, 4)) ||
+        (kind == Q8G_Q8_0 && !aligned(dx, 2)) || (kind == kKindNorm && !aligned(gamma, 16)))
         return Q8G_ERR_ALIGN;
     const int64_t wbytes = F * K, dwbytes = F * (K / 32) * 2;
     const int64_t xbytes = kind == kKindNorm ? 4 * K : K;
     const int64_t dxbytes = kind == Q8G_Q8_0 ? (K / 32) * 2 : 0;
     const int64_t gbytes = kind == kKindNorm ? 4 * K : 0;
-    const int64_t qabytes = F, dabytes = (F / 32) * 2;
+    const int64_t qabytes = F, dabytes = (F / 32) * 2, abytes = 4 * F;
     const void *ins[6] = {qg, dg, qu, du, x, kind == Q8G_Q8_0 ? static_cast<const void *>(dx) : gamma};
     const int64_t inbytes[6] = {wbytes, dwbytes, wbytes, dwbytes, xbytes, kind == Q8G_Q8_0 ? dxbytes : gbytes};
-    for (int i = 0; i < 6; ++i)
-        if (overlap(qa, qabytes, ins[i], inbytes[i]) || overlap(da, dabytes, ins[i], inbytes[i])) return Q8G_ERR_OVERLAP;
-    if (overlap(qa, qabytes, da, dabytes)) return Q8G_ERR_OVERLAP;
+    for (int i = 0; i < 6; ++i) {
+        if (f32_out && overlap(a, abytes, ins[i], inbytes[i])) return Q8G_ERR_OVERLAP;
+        if (!f32_out && (overlap(qa, qabytes, ins[i], inbytes[i]) || overlap(da, dabytes, ins[i], inbytes[i])))
+            return Q8G_ERR_OVERLAP;
+    }
+    if (!f32_out && overlap(qa, qabytes, da, dabytes)) return Q8G_ERR_OVERLAP;
 
     Parts p;
     for (int i = 0; i < kMaxParts; ++i) {
@@ -904,15 +936,18 @@ q8g_status gateup_silu(int kind, const int8_t *qg, const uint16_t *dg, const int
     p.w[1] = qu;
     p.dw[1] = du;
     p.end[1] = 2 * F;
+    p.y[0] = a;  // EPI 2 writes a through part 0's output; EPI 1 writes no f32 output
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // with K == 0 no activation is read: gate = up = 0, a = 0
     const bool norm = kind == kKindNorm && K > 0;
+    const void *xq = kind == Q8G_Q8_0 ? x : nullptr;
+    const uint16_t *dxq = kind == Q8G_Q8_0 ? dx : nullptr;
+    constexpr int SR = Q8G_SILU_ROWS, SW = Q8G_SILU_WAVES;
     const hipError_t e =
-        norm && one_pass(K, 16 * kWave)
-            ? launch_gemv<Dt::Q8NORM, 4, 16, true, false, 1>(p, x, nullptr, gamma, eps, K, 2 * F, s, qa, da)
-        : norm ? launch_gemv<Dt::Q8NORM, 4, 16, true, false, 4>(p, x, nullptr, gamma, eps, K, 2 * F, s, qa, da)
-               : launch_gemv<Dt::Q8, 4, 16, true>(p, kind == Q8G_Q8_0 ? x : nullptr, kind == Q8G_Q8_0 ? dx : nullptr,
-                                                  nullptr, 0.0f, K, 2 * F, s, qa, da);
+        f32_out ? (norm ? launch_epi<Dt::Q8NORM, SR, SW, 2>(p, x, nullptr, gamma, eps, K, F, s, nullptr, nullptr)
+                        : launch_epi<Dt::Q8, SR, SW, 2>(p, xq, dxq, nullptr, 0.0f, K, F, s, nullptr, nullptr))
+                : (norm ? launch_epi<Dt::Q8NORM, 4, 16, 1>(p, x, nullptr, gamma, eps, K, F, s, qa, da)
+                        : launch_epi<Dt::Q8, 4, 16, 1>(p, xq, dxq, nullptr, 0.0f, K, F, s, qa, da));
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
 
@@ -1048,14 +1083,32 @@ q8g_status q8_gateup_silu_quantize(const int8_t *qw_gate, const uint16_t *dw_gat
                                    const uint16_t *dw_up, int64_t F, const int8_t *qx, const uint16_t *dx, int64_t K,
                                    int8_t *qa, uint16_t *da, void *stream)
 {
-    return gateup_silu(Q8G_Q8_0, qw_gate, dw_gate, qw_up, dw_up, F, qx, dx, nullptr, 0.0f, qa, da, K, stream);
+    return gateup_silu(Q8G_Q8_0, qw_gate, dw_gate, qw_up, dw_up, F, qx, dx, nullptr, 0.0f, qa, da, nullptr, K, stream);
 }
 
 q8g_status q8_gateup_rmsnorm_silu_quantize(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
                                            const uint16_t *dw_up, int64_t F, const float *x, const float *gamma,
                                            float eps, int64_t K, int8_t *qa, uint16_t *da, void *stream)
 {
-    return gateup_silu(kKindNorm, qw_gate, dw_gate, qw_up, dw_up, F, x, nullptr, gamma, eps, qa, da, K, stream);
+    return gateup_silu(kKindNorm, qw_gate, dw_gate, qw_up, dw_up, F, x, nullptr, gamma, eps, qa, da, nullptr, K,
+                       stream);
+}
+
+q8g_status q8_gateup_silu(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up, const uint16_t *dw_up,
+                          int64_t F, const int8_t *qx, const uint16_t *dx, int64_t K, float *a, void *stream)
+{
+    if (!a && F > 0) return Q8G_ERR_NULL;
+    return gateup_silu(Q8G_Q8_0, qw_gate, dw_gate, qw_up, dw_up, F, qx, dx, nullptr, 0.0f, nullptr, nullptr, a, K,
+                       stream);
+}
+
+q8g_status q8_gateup_rmsnorm_silu(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
+                                  const uint16_t *dw_up, int64_t F, const float *x, const float *gamma, float eps,
+                                  int64_t K, float *a, void *stream)
+{
+    if (!a && F > 0) return Q8G_ERR_NULL;
+    return gateup_silu(kKindNorm, qw_gate, dw_gate, qw_up, dw_up, F, x, nullptr, gamma, eps, nullptr, nullptr, a, K,
+                       stream);
 }
 
 q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows, int *waves)

@@ -12,8 +12,8 @@ the residual stream h (attention itself is not part of this path; its output is 
 seeded stand-in per layer). One token, fused (4 launches per layer):
     QKV    gemv_stacked_rmsnorm(h, gamma_attn)                 q, k, v
     out    gemv_stacked(attn f32), residual h, in place          h += W_o attn
-    MLP    q8_gateup_rmsnorm_silu_quantize(h, gamma_mlp)         codes of silu(gate) up
-    down   q8_gemv(codes), residual h, in place                  h += W_d a
+    MLP    q8_gateup_rmsnorm_silu(h, gamma_mlp)                  a = silu(gate) up, f32
+    down   gemv_stacked(a f32), residual h, in place             h += W_d a
 then the head with the final normalization in its prologue (gemv_stacked_rmsnorm).
 Unfused (8 launches per layer) runs every normalization, activation and quantize as
 its own launch, and the head as q8_rmsnorm_quantize_act then q8_gemv. Both give the
@@ -29,7 +29,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (gemv_stacked, gemv_stacked_rmsnorm, q8_gateup_silu_quantize, q8_gemv, q8_gemv_batch, q8_quantize_act,
+from . import (gemv_stacked, gemv_stacked_rmsnorm, q8_gateup_silu, q8_gemv, q8_gemv_batch, q8_quantize_act,
                q8_rmsnorm_quantize_act, q8_silu_mul_quantize_act)
 
 
@@ -71,6 +71,7 @@ class Q8LayerChain:
         self.qa = torch.empty(f, dtype=torch.int8, device=dev)
         self.da = torch.empty(f // 32, dtype=torch.float16, device=dev)
         self.gu = torch.empty(2 * f, dtype=torch.float32, device=dev)
+        self.a = torch.empty(f, dtype=torch.float32, device=dev)  # silu(gate) * up, f32
 
     def _b(self, l, j):
         return self.stack.bufs[4 * l + j]
@@ -110,8 +111,9 @@ class Q8LayerChain:
             if fused:
                 gemv_stacked_rmsnorm(self.qkv_parts(l), h_in, self.gamma_attn[l], eps, stream=stream)
                 gemv_stacked(self.out_parts(l, h_in), self.attn[l], stream=stream)
-                q8_gateup_silu_quantize(*self.gate_up(l), self.h, gamma=self.gamma_mlp[l], eps=eps, qa=self.qa,
-                                        da=self.da, stream=stream)
+                q8_gateup_silu(*self.gate_up(l), self.h, gamma=self.gamma_mlp[l], eps=eps, a=self.a, stream=stream)
+                if trace is not None:  # the codes the down projection forms from a, for the snapshots
+                    q8_quantize_act(self.a, self.qa, self.da, stream=stream)
             else:
                 q8_rmsnorm_quantize_act(h_in, self.gamma_attn[l], eps, qx=self.qx, dx=self.dx, stream=stream)
                 snap("qkv_codes", l, torch.cat([self.qx.view(torch.uint8), self.dx.view(torch.uint8)]))
@@ -129,7 +131,10 @@ class Q8LayerChain:
             snap("qkv", l, self._b(l, 0)["y"])
             snap("a_codes", l, torch.cat([self.qa.view(torch.uint8), self.da.view(torch.uint8)]))
             b = self._b(l, 3)
-            q8_gemv(b["qw"], b["dw"], self.qa, self.da, y=self.h, residual=self.h, stream=stream)
+            if fused:  # f32 input, quantized in the launch
+                gemv_stacked([{"w": b["qw"], "dw": b["dw"], "y": self.h, "residual": self.h}], self.a, stream=stream)
+            else:
+                q8_gemv(b["qw"], b["dw"], self.qa, self.da, y=self.h, residual=self.h, stream=stream)
         snap("h_out", self.layers - 1, self.h)
         hb = self.head()
         if fused:

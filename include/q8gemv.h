@@ -217,6 +217,27 @@ q8g_status q8_gateup_rmsnorm_silu_quantize(const int8_t *qw_gate, const uint16_t
                                            const uint16_t *dw_up, int64_t F, const float *x, const float *gamma,
                                            float eps, int64_t K, int8_t *qa, uint16_t *da, void *stream);
 
+/* Gate+up projection with the gated activation in the epilogue, written in f32
+ * ([H] Emitting for a GPU: the activation fused with the projection; [P]
+ * Q4_K_M: the gated MLP): for F gate rows and the F matching up rows,
+ *   a[j] = silu(g[j]) * u[j]         (f32, exactly as q8_silu_mul_quantize_act forms it)
+ * with g, u as gemv_stacked computes them. a f32 [F] (4-byte aligned) is the
+ * input of an f32-input down projection (gemv_stacked with Q8G_Q8_0_F32
+ * parts), which quantizes it in its prologue: the codes it forms are
+ * bit-identical to those of q8_gateup_silu_quantize. Without the quantization,
+ * a workgroup needs only matching gate and up rows, not a whole 32-value block
+ * of a, so the launch spreads over more workgroups. F % 32 == 0, K % 32 == 0;
+ * weights and activation as for q8_gateup_silu_quantize; a may not overlap
+ * any input. Q8G_ERR_NULL if a is NULL (F > 0). */
+q8g_status q8_gateup_silu(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up, const uint16_t *dw_up,
+                          int64_t F, const int8_t *qx, const uint16_t *dx, int64_t K, float *a, void *stream);
+
+/* The same with RMSnorm(x) * gamma as the input (x, gamma f32 [K], K <= 16384),
+ * normalized and quantized in the prologue exactly as q8_rmsnorm_quantize_act. */
+q8g_status q8_gateup_rmsnorm_silu(const int8_t *qw_gate, const uint16_t *dw_gate, const int8_t *qw_up,
+                                  const uint16_t *dw_up, int64_t F, const float *x, const float *gamma, float eps,
+                                  int64_t K, float *a, void *stream);
+
 /* ---- a whole decode step in one launch ------------------------------------
  * "Filling in the blanks: Inference using Phobos", section Fast Decode, lists
  * the launch-level steps of a fast decode pass: replay the pass as one unit,

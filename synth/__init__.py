@@ -214,13 +214,20 @@ def q8_gateup_epilogue_bytes(f: int, k: int) -> int:
     return 2 * f * k + 2 * (2 * f) * (k // QBLOCK) + 8 * k + f + 2 * (f // QBLOCK)
 
 
+def q8_gateup_silu_f32_bytes(f: int, k: int) -> int:
+    """Algorithmic bytes of the gate+up launch with the normalization in its prologue and
+    a = silu(gate) * up written in f32 in its epilogue: both weight planes of 2f rows, x and
+    gamma f32 [k], a f32 [f] out."""
+    return 2 * f * k + 2 * (2 * f) * (k // QBLOCK) + 8 * k + 4 * f
+
+
 def q8_layers_08b_bytes(layers: int = 24, hidden: int = 1024, ffn: int = 3584, vocab: int = 151936) -> int:
     """Algorithmic bytes of one token of the fused decode-layer chain: per layer the QKV launch
     with its normalization, the out projection (f32 input, residual), the gate+up launch with
-    its epilogue and the down projection (codes input, residual); then the head with the final
-    normalization in its prologue."""
+    its f32 epilogue (a = silu(gate) * up written in f32) and the down projection (f32 input,
+    residual); then the head with the final normalization in its prologue."""
     per_layer = (q8_rmsnorm_gemv_bytes(4096, hidden) + q8_gemv_f32x_bytes(hidden, 2048, residual=True)
-                 + q8_gateup_epilogue_bytes(ffn, hidden) + q8_gemv_bytes(hidden, ffn, residual=True))
+                 + q8_gateup_silu_f32_bytes(ffn, hidden) + q8_gemv_f32x_bytes(hidden, ffn, residual=True))
     return layers * per_layer + q8_rmsnorm_gemv_bytes(vocab, hidden)
 
 

@@ -51,6 +51,8 @@ def lib():
     L.q8_rmsnorm_quantize_act_batch.argtypes = [P, P, ctypes.c_float, P, P, I64, I64, P]
     L.q8_silu_mul_quantize_act_batch.argtypes = [P, P, P, I64, I64, P]
     L.q8_gateup_rmsnorm_silu_quantize.argtypes = [P, P, P, P, I64, P, P, ctypes.c_float, I64, P, P, P]
+    L.q8_gateup_silu.argtypes = [P, P, P, P, I64, P, P, I64, P, P]
+    L.q8_gateup_rmsnorm_silu.argtypes = [P, P, P, P, I64, P, P, ctypes.c_float, I64, P, P]
     L.q8g_status_str.argtypes = [ctypes.c_int]
     L.q8g_status_str.restype = ctypes.c_char_p
     L.q8g_probe_read.argtypes = [P, I64, P, P]
@@ -63,7 +65,8 @@ def test_every_declared_symbol_is_exported(lib):
     for expected in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
                      "q8g_status_str", "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act",
                      "gemv_stacked_rmsnorm", "q8_gemv_silu_mul", "q8_gateup_silu_quantize",
-                     "q8_gateup_rmsnorm_silu_quantize", "q8_rmsnorm_quantize_act_batch",
+                     "q8_gateup_rmsnorm_silu_quantize", "q8_gateup_silu", "q8_gateup_rmsnorm_silu",
+                     "q8_rmsnorm_quantize_act_batch",
                      "q8_silu_mul_quantize_act_batch", "q8g_probe_read", "q8g_flush"):
         assert expected in names
     for n in names:
@@ -291,6 +294,27 @@ def test_gateup_epilogue_validation(lib):
     assert n(W, DW, WU, DU, 64, X, None, 1e-6, 64, QA, DA, None) == ERR_NULL
     assert n(W, DW, WU, DU, 64, X, G + 4, 1e-6, 64, QA, DA, None) == ERR_ALIGN
     assert n(W, DW, WU, DU, 64, X, G, 1e-6, 64, G + 64, DA, None) == ERR_OVERLAP  # codes in gamma
+
+
+def test_gateup_f32_epilogue_validation(lib):
+    g = lib.q8_gateup_silu
+    WU, DU = W + 0x1000000, DW + 0x1000000
+    A = Y
+    assert g(W, DW, WU, DU, 48, QX, DX, 64, A, None) == ERR_SHAPE  # F % 32
+    assert g(W, DW, WU, DU, 64, QX, DX, 48, A, None) == ERR_SHAPE  # K % 32
+    assert g(None, None, None, None, 0, None, None, 64, None, None) == OK  # F == 0
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, None, None) == ERR_NULL
+    assert g(W, DW, WU, DU, 64, QX, None, 64, A, None) == ERR_NULL
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, A + 2, None) == ERR_ALIGN
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, WU + 64, None) == ERR_OVERLAP  # a in the up weights
+    assert g(W, DW, WU, DU, 64, QX, DX, 64, DX, None) == ERR_OVERLAP
+    n = lib.q8_gateup_rmsnorm_silu
+    G = R
+    assert n(W, DW, WU, DU, 64, X, G, 1e-6, 16384 + 32, A, None) == ERR_SHAPE
+    assert n(W, DW, WU, DU, 64, X, G, -1.0, 64, A, None) == ERR_ARG
+    assert n(W, DW, WU, DU, 64, X, None, 1e-6, 64, A, None) == ERR_NULL
+    assert n(W, DW, WU, DU, 64, X, G + 4, 1e-6, 64, A, None) == ERR_ALIGN
+    assert n(W, DW, WU, DU, 64, X, G, 1e-6, 64, G + 64, None) == ERR_OVERLAP  # a in gamma
 
 
 def test_probe_validation(lib):

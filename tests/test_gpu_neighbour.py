@@ -304,6 +304,82 @@ def test_gateup_epilogue_separate_matrices_and_mlp_chain(q8, orc):
     within(y_epi, yr, S, "mlp chain")
 
 
+@pytest.mark.parametrize("f,k", EPI_SHAPES)
+@pytest.mark.parametrize("norm", [False, True])
+def test_gateup_f32_epilogue(q8, orc, f, k, norm):
+    """a = silu(gate) * up written in f32 by the gate+up launch: bit for bit the oracle's silu*up of
+    the same rows as gemv_stacked computes them, and quantized (q8_quantize_act) into exactly the
+    codes and scales the quantizing epilogue writes."""
+    if norm and k > 16384:
+        pytest.skip("the normalizing prologue takes K <= 16384")
+    print_case("gate+up f32 silu epilogue", f, k, "rmsnorm in" if norm else "codes in")
+    g, qw, dw = gateup_case(f, k, 3 * f + k + (1 if norm else 0))
+    x, gamma = synth.activation_f32(g, k), synth.norm_gamma(g, k)
+    W, DW, X, G = dev(qw), h16(dw), dev(x), dev(gamma)
+    if norm:
+        a = q8.q8_gateup_silu(W[:f], DW[:f], W[f:], DW[f:], X, gamma=G, eps=EPS)
+        qa, da = q8.q8_gateup_silu_quantize(W[:f], DW[:f], W[f:], DW[f:], X, gamma=G, eps=EPS)
+        qx, dx = q8.q8_rmsnorm_quantize_act(X, G, EPS)
+    else:
+        qx, dx = q8.q8_quantize_act(X)
+        a = q8.q8_gateup_silu(W[:f], DW[:f], W[f:], DW[f:], qx, dx)
+        qa, da = q8.q8_gateup_silu_quantize(W[:f], DW[:f], W[f:], DW[f:], qx, dx)
+    yg, yu = q8.gemv_stacked([{"w": W[:f], "dw": DW[:f]}, {"w": W[f:], "dw": DW[f:]}], qx, dx)
+    gu = np.concatenate([host(yg), host(yu)])
+    ah = host(a)
+    assert np.array_equal(ah, orc.silu_mul(gu)), f"{np.count_nonzero(ah != orc.silu_mul(gu))} values differ"
+    q2, d2 = q8.q8_quantize_act(a)
+    assert np.array_equal(host(q2), host(qa)) and np.array_equal(bits(d2), bits(da))
+
+
+def test_gateup_f32_epilogue_mlp_chain(q8, orc):
+    """The MLP block as the f32 epilogue then the f32-input down projection (residual in place)
+    equals the quantizing-epilogue chain bit for bit."""
+    print_case("mlp chain, f32 epilogue")
+    f, k = 3584, 1024
+    g = synth.rng_for(synth.TAG_NEIGHBOUR, 5111)
+    qg, dg = synth.q8_weights(g, f, k)
+    qu, du = synth.q8_weights(g, f, k)
+    qd, dd = synth.q8_weights(g, k, f)
+    x, gamma, r = synth.activation_f32(g, k), synth.norm_gamma(g, k), synth.residual_f32(g, k)
+    Wg, Dg, Wu, Du, Wd, Dd = dev(qg), h16(dg), dev(qu), h16(du), dev(qd), h16(dd)
+    X, G = dev(x), dev(gamma)
+    qa, da = q8.q8_gateup_silu_quantize(Wg, Dg, Wu, Du, X, gamma=G, eps=EPS)
+    y_epi = host(q8.q8_gemv(Wd, Dd, qa, da, residual=dev(r)))
+    a = q8.q8_gateup_silu(Wg, Dg, Wu, Du, X, gamma=G, eps=EPS)
+    h = dev(r)
+    q8.gemv_stacked([{"w": Wd, "dw": Dd, "y": h, "residual": h}], a)
+    assert np.array_equal(host(h), y_epi)
+    rq, rd = orc.quantize_act(host(a))
+    yr, S = orc.q8_gemv(qd, dd, rq, rd, r)
+    within(y_epi, yr, S, "mlp chain, f32 epilogue")
+
+
+def test_gateup_f32_epilogue_k0_and_guards(q8):
+    import torch
+
+    print_case("gate+up f32 epilogue K=0 and guards")
+    f = 64
+    w = torch.empty((f, 0), dtype=torch.int8, device="cuda")
+    dw = torch.empty((f, 0), dtype=torch.float16, device="cuda")
+    buf = torch.full((f + 64,), 7.0, dtype=torch.float32, device="cuda")
+    q8.q8_gateup_silu(w, dw, w, dw, torch.empty(0, dtype=torch.int8, device="cuda"),
+                      torch.empty(0, dtype=torch.float16, device="cuda"), a=buf[:f])
+    assert (host(buf[:f]) == 0).all() and (host(buf[f:]) == 7.0).all()
+    k = 1024
+    g, qw, dwn = gateup_case(f, k, 78)
+    W, DW = dev(qw), h16(dwn)
+    x = dev(synth.activation_f32(g, k))
+    buf = torch.full((f + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[f:] = 7.0
+    q8.q8_gateup_silu(W[:f], DW[:f], W[f:], DW[f:], x, gamma=dev(synth.norm_gamma(g, k)), eps=EPS, a=buf[:f])
+    hb = host(buf)
+    assert not np.isnan(hb[:f]).any() and (hb[f:] == 7.0).all()
+    with pytest.raises(q8.Q8GemvError) as e:
+        q8.q8_gateup_silu(W[:48], DW[:48], W[f:f + 48], DW[f:f + 48], x, gamma=x.clone(), eps=EPS)
+    assert e.value.status == 2
+
+
 def test_gateup_epilogue_k0_and_guards(q8):
     import torch
 
