@@ -1064,7 +1064,7 @@ def run_mlp(args, torch, q8, np):
     if t32 <= t:
         t_rep, per, b_front, t_rep_front = t32, b1f + b2f, b1f, t32_front
         chain = "q8_gateup_rmsnorm_silu (a in f32), then the f32-input down projection (residual)"
-        kname = "q8_gateup_rmsnorm_silu_f32[rows_per_wave=2,waves=8]"
+        kname = "q8_gateup_rmsnorm_silu_f32[rows_per_wave=4,waves=8]"
     else:
         t_rep, per, b_front, t_rep_front = t, b1 + b2, b1, t_front
         chain = "q8_gateup_rmsnorm_silu_quantize, then q8_gemv (down, residual)"
@@ -1173,7 +1173,7 @@ def run_layers(args, torch, q8, np):
         "gemv_kernel<Q8F32, rows_per_wave=1, waves=8, residual> (out)": (
             lambda: [q8.gemv_stacked(chain.out_parts(l, chain.h), chain.attn[l]) for l in range(L)],
             synth.q8_gemv_f32x_bytes(k, 2048, residual=True)),
-        "q8_gateup_rmsnorm_silu_f32[rows_per_wave=2,waves=8] (gate+up)": (
+        "q8_gateup_rmsnorm_silu_f32[rows_per_wave=4,waves=8] (gate+up)": (
             lambda: [q8.q8_gateup_silu(*chain.gate_up(l), chain.h, gamma=chain.gamma_mlp[l], eps=NORM_EPS, a=chain.a)
                      for l in range(L)], synth.q8_gateup_silu_f32_bytes(f, k)),
         "gemv_kernel<Q8F32, rows_per_wave=1, waves=8, residual> (down)": (
@@ -1414,9 +1414,14 @@ def counter_run(args, torch, q8, np):
         dwt = torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16)
         q8.q8_gateup_silu_quantize(w[:3584], dwt[:3584], w[3584:], dwt[3584:], torch.from_numpy(x).cuda(),
                                    gamma=torch.from_numpy(gamma).cuda(), eps=NORM_EPS)
+        qw, dw = synth.q8_weights(g, 2 * 3584, 1024)
+        w = torch.from_numpy(qw).cuda()
+        dwt = torch.from_numpy(dw.view(np.int16)).cuda().view(torch.float16)
+        q8.q8_gateup_silu(w[:3584], dwt[:3584], w[3584:], dwt[3584:], torch.from_numpy(x).cuda(),
+                          gamma=torch.from_numpy(gamma).cuda(), eps=NORM_EPS)
     torch.cuda.synchronize()
     print(json.dumps({"counter_run": "probe 1 GiB read, flush 1 GiB write, 2 fused decode steps, "
-                                      "2 steps of 16 streams, 4 + 4 + 4 neighbour-step launches"}), flush=True)
+                                      "2 steps of 16 streams, 4 + 4 + 4 + 4 neighbour-step launches"}), flush=True)
 
 
 def main():
