@@ -343,8 +343,8 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[R], const RowRef (
 // qa[32b..] and the scale da[b]. EPI 2: a itself is written, in f32, to part
 // 0's output (y0[P*b + j]); nothing else is written.
 // XP: f32 activation passes requested before the weights (1 when one pass of
-// 4 values per thread covers K, else 4; values past them are read after the
-// weights are requested). Loads of passes past K are clamped duplicates, so
+// 4 values per thread covers K, 2 when two do, else 4; values past them are
+// read after the weights are requested). Loads of passes past K are clamped duplicates, so
 // their number is chosen by the launch rather than fixed.
 template <Dt DT, int R, int WAVES, int EPI = 0, bool PRES = false, int XP = 4>
 __global__ __launch_bounds__(WAVES *kWave) void gemv_kernel(PARTS_PARAMS, const void *__restrict__ xv,
@@ -718,6 +718,7 @@ struct Prologue {
 
 // activation passes of an f32-input launch: one when it covers K
 constexpr bool one_pass(int64_t K, int threads) { return K <= 4 * (int64_t)threads; }
+constexpr bool two_passes(int64_t K, int threads) { return K <= 8 * (int64_t)threads; }
 
 template <Dt DT, int R, int W, bool PRES>
 hipError_t launch_xp(const Parts &p, const void *x, const uint16_t *dx, Prologue pr, int64_t K, int64_t n_total,
@@ -726,6 +727,8 @@ hipError_t launch_xp(const Parts &p, const void *x, const uint16_t *dx, Prologue
     if constexpr (is_fused(DT)) {
         if (one_pass(K, W * kWave))
             return launch_gemv<DT, R, W, 0, PRES, 1>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
+        if (two_passes(K, W * kWave))
+            return launch_gemv<DT, R, W, 0, PRES, 2>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
     }
     return launch_gemv<DT, R, W, 0, PRES, 4>(p, x, dx, pr.aux, pr.eps, K, n_total, s);
 }

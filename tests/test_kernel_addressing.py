@@ -209,17 +209,18 @@ def fused_prologue_loads(K, threads, passes, two):
 
 
 def launch_passes(k, threads):
-    """Activation passes the launch picks: one when one pass of 4 values per thread covers K."""
-    return 1 if k <= 4 * threads else 4
+    """Activation passes the f32-input GEMV launch picks: one when one pass of 4 values per thread
+    covers K, two when two do, else four (the gate+up epilogue launch: one, else four)."""
+    return 1 if k <= 4 * threads else 2 if k <= 8 * threads else 4
 
 
 @pytest.mark.parametrize("k", [32, 96, 1024, 2048, 2080, 3584, 4096, 16384])
 @pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("two", [None, "norm", "silu"])
 def test_fused_prologue_addressing(k, waves, two):
-    for passes in (1, 4):  # the launch's choice and the other template, both valid for any K
+    for passes in (1, 2, 4):  # the launch's choice and the other templates, all valid for any K
         fused_prologue_loads(k, waves * 64, passes, two)
-    assert launch_passes(k, waves * 64) in (1, 4)
+    assert launch_passes(k, waves * 64) in (1, 2, 4)
 
 
 def weight_batch_items(K, R, kbatch=4, chunk=1024):
@@ -307,6 +308,7 @@ def test_fused_prologue_constants():
     src = open(os.path.join(CSRC, "q8gemv.hip")).read()
     assert re.search(r"constexpr int kXPasses = XP;", src)
     assert "constexpr bool one_pass(int64_t K, int threads) { return K <= 4 * (int64_t)threads; }" in src
+    assert "constexpr bool two_passes(int64_t K, int threads) { return K <= 8 * (int64_t)threads; }" in src
     assert re.search(r"constexpr int kMaxFusedK = 16384;", src)
     assert "e < K ? e : K - 4" in src
     assert "const bool real = c0 + j / R < nchunk;" in src
