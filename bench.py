@@ -230,9 +230,14 @@ def cold_seconds(torch, q8, fn, flush_buf, reps=10):
     return sorted(ts)[len(ts) // 2]
 
 
+HOST_SHARE_THREADS = 16  # one GPU's share of the host's cores on the measuring machine
+
+
 def cpu_threads():
+    """Threads for the oracle baseline: the host's cores, capped at one GPU's share of them
+    (the measuring machine runs one GPU per 16 cores and limits a job to that share)."""
     n = os.cpu_count() or 1
-    return max(1, min(16, n))  # one GPU's share of the host
+    return max(1, min(HOST_SHARE_THREADS, n))
 
 
 def cpu_model():
@@ -466,7 +471,8 @@ def cpu_baseline_single(dt, first, n, k, per, orc, np, min_seconds=10.0, nb=1):
     dt_ = time.perf_counter() - t0
     gbps = calls * per / dt_ / 1e9
     log(f"[bench] oracle on {nth} host threads: {gbps:.2f} GB/s, {calls} calls in {dt_:.1f}s")
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "host_cores": os.cpu_count(),
+            "threads_note": f"min(host cores, {HOST_SHARE_THREADS}): one GPU's share of the host", "kind": "oracle",
             "sample": f"{calls} whole {n}x{k} calls, {calls * per} algorithmic bytes in {dt_:.1f} s",
             "cpu": cpu_model()}
 
@@ -536,7 +542,8 @@ def cpu_baseline_stack(ops, host, orc, min_seconds=10.0):
     log(f"[bench] oracle on {nth} host threads ({cpu_model()}): {gbps:.2f} GB/s, {tokens} tokens in {dt:.1f}s")
     t1, b1, d1 = oracle_stack_tokens(ops, host, orc, 1, min_seconds / 2)
     log(f"[bench] oracle on 1 host thread: {b1 / d1 / 1e9:.2f} GB/s, {t1} tokens in {d1:.1f}s")
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": nth, "host_cores": os.cpu_count(),
+            "threads_note": f"min(host cores, {HOST_SHARE_THREADS}): one GPU's share of the host", "kind": "oracle",
             "sample": f"{tokens} whole tokens of the 0.8B-shaped stack (97 quantizes + 97 GEMVs each), "
                       f"{nbytes} algorithmic bytes in {dt:.1f} s",
             "tok_per_s": round(tokens / dt, 2), "cpu": cpu_model(),
@@ -556,13 +563,27 @@ def gpu_environment(torch):
                 env[key] = f.read().strip()
         except OSError:
             env[key] = None
-    for key, flag in (("clocks", "--showclocks"), ("gpu_pids", "--showpids")):
-        try:
-            r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=30)
-            env[key] = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else None
-        except (OSError, ValueError, subprocess.SubprocessError):
-            env[key] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        env["clocks"] = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        env["clocks"] = None
+    env.update(gpu_processes())
     return env
+
+
+def gpu_processes():
+    """Processes holding a GPU context, from the kernel driver's list (one directory per
+    process under /sys/class/kfd/kfd/proc). Another process on the GPU during a timed run
+    halves what it measures, so the record lists them; `gpu_pids_check` says whether the
+    list could be read at all."""
+    root = "/sys/class/kfd/kfd/proc"
+    try:
+        pids = sorted(int(d) for d in os.listdir(root) if d.isdigit())
+    except OSError as e:
+        return {"gpu_pids": None, "gpu_pids_check": f"unavailable: {e.strerror}"}
+    others = [p for p in pids if p != os.getpid()]
+    return {"gpu_pids": pids, "gpu_pids_check": "ok" if not others else f"other processes on the GPU: {others}"}
 
 
 # ----------------------------------------------------------------------------- 16 streams
@@ -1469,6 +1490,20 @@ def main():
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)
+    teardown(torch, q8)
+
+
+def teardown(torch, q8):
+    """Release every GPU object while the runtime is alive: graphs, plans and buffers of the
+    workload were local to it; collect them, return the cached memory, then unload the
+    library so that its code object is unregistered now rather than by a process-exit
+    handler that runs after a profiler has already shut the runtime down."""
+    import gc
+
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    q8.unload_library()
 
 
 if __name__ == "__main__":

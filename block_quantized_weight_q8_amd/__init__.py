@@ -70,7 +70,8 @@ class _StackOp(ctypes.Structure):
     ]
 
 
-STACK_SYNC_WORDS = 64 + 16 * 1024
+STACK_SYNC_WORDS = 20480
+STACK_MAX_OPS = 256
 STACK_ERR_WORD = 16
 STACK_MAX_K = 16384
 
@@ -120,6 +121,20 @@ def load_library(path: str = LIB_PATH):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def unload_library():
+    """Unload libq8gemv.so (its code object is unregistered from the HIP runtime at once).
+    Only for process teardown: nothing of the library may be in flight or referenced by a
+    graph, and every later call loads it again."""
+    global _lib
+    if _lib is None:
+        return
+    import _ctypes
+
+    handle = _lib._handle
+    _lib = None
+    _ctypes.dlclose(handle)
 
 
 def _check(fn: str, status: int):

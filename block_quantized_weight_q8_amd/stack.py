@@ -1,16 +1,17 @@
 """A decode step of stacked Q8_0 projections, run through the C ABI.
 
-"Filling in the blanks: Inference using Phobos", section Fast Decode, lists the
-launch-level steps of a fast decode pass: record the pass once and replay it as a
-graph, never allocate while recording, quantize an activation once and share it,
-stack projections that read the same input, fold the residual add into the matmul.
-This module lays one step out two ways over the same buffers, allocated up front:
+"Filling in the blanks: Inference using Phobos", section Fast Decode, describes the
+decode pass as recorded once and replayed (with nothing allocated during recording), with
+each activation quantized a single time, projections with a common input run together and
+the residual joined to the product's output.
+This module lays one step out three ways over the same buffers, allocated up front:
   * per projection one q8_quantize_act and one gemv_stacked (or q8_gemv) launch on
     one stream, in dependency order; the step can be captured into a HIP graph;
   * per projection one gemv_stacked launch that quantizes the f32 input itself
     (except matrices with very many rows, where quantize + GEMV is faster);
   * the whole step as one q8_decode_stack launch (persistent workgroups, a device-wide
-    barrier between projections, the next projection's weights fetched during it).
+    barrier between projections, each input quantized once by the workgroups of the
+    projection before it, the next projection's weights fetched during the barrier).
 All three produce bit-identical outputs. Q8BatchStack runs nb decode streams at once
 over the same weights: per projection one q8_quantize_act over all nb inputs and one
 q8_gemv_batch launch (stacked parts are row ranges of one matrix, so one launch

@@ -239,18 +239,20 @@ q8g_status q8_gateup_rmsnorm_silu(const int8_t *qw_gate, const uint16_t *dw_gate
                                   int64_t K, float *a, void *stream);
 
 /* ---- a whole decode step in one launch ------------------------------------
- * "Filling in the blanks: Inference using Phobos", section Fast Decode, lists
- * the launch-level steps of a fast decode pass: replay the pass as one unit,
- * quantize an activation once and share it, stack projections that read the
- * same input, fold the residual add into the matmul. q8_decode_stack runs a
- * sequence of stacked Q8_0 projections as ONE cooperative launch: projection
- * i starts reading its activation only after every output of projection i-1
- * is written (a device-wide barrier), while the weights of the next
- * projection, which depend on no activation, are already being fetched.
- * Each projection quantizes its f32 input exactly as q8_quantize_act does and
- * computes each output row with the same instructions as gemv_stacked, so
+ * [P] Fast Decode describes the decode pass as one replayed unit in which each
+ * activation is quantized a single time and reused, projections with a common
+ * input run together, and the residual joins the product's output.
+ * q8_decode_stack runs a sequence of stacked Q8_0 projections as ONE
+ * cooperative launch, in order: projection i reads its input only after every
+ * workgroup has finished projection i-1 (a device-wide barrier), while the
+ * weights of projection i, which depend on no activation, are fetched during
+ * that barrier. The input of projection i is quantized once, by the
+ * workgroups of projection i-1, with the arithmetic of q8_quantize_act, and
+ * each output row is computed with the same instructions as gemv_stacked, so
  * every output is bit-identical to q8_quantize_act + gemv_stacked on the same
- * inputs. */
+ * inputs. An input or residual may be an earlier projection's output (a real
+ * decode chain): such a projection waits until those outputs are visible and
+ * reads and quantizes its input itself. */
 typedef struct {
     const float *x;     /* f32 [K] input of this projection (16-byte aligned) */
     int8_t *qx;         /* optional: the quantized codes int8 [K] are also written here (or NULL) */
@@ -262,25 +264,31 @@ typedef struct {
 } q8g_stack_op;
 
 #define Q8G_STACK_MAX_K 16384
-/* uint32 words of the synchronization workspace: 64 + 16 per workgroup, for
- * up to 1024 workgroups (one per compute unit). */
-#define Q8G_STACK_SYNC_WORDS (64 + 16 * 1024)
+/* projections of one launch (their descriptors are staged on chip) */
+#define Q8G_STACK_MAX_OPS 256
+/* uint32 words of the synchronization workspace: a barrier count, an error
+ * word, 16 barrier counters and two areas for a quantized input of up to
+ * Q8G_STACK_MAX_K values. */
+#define Q8G_STACK_SYNC_WORDS 20480
 /* word of the workspace that is nonzero if a launch gave up waiting (its
  * outputs are then incomplete; zero the workspace before the next launch). */
 #define Q8G_STACK_ERR_WORD 16
 
 /* Run nops projections in order in one launch.
- * ops:     host array, validated here (same rules as gemv_stacked per op; no
- *          output may overlap any weight, scale or activation input of any op,
- *          or another output).
+ * ops:     host array of nops <= Q8G_STACK_MAX_OPS descriptors, validated here
+ *          (same rules as gemv_stacked per op; no output may overlap any
+ *          weight or scale of any op, the input or residual of the same or an
+ *          earlier op, or another output; an output may be a later op's input
+ *          or residual).
  * ops_dev: device copy of the same nops descriptors (same bytes), read by the
  *          kernel; the caller keeps it alive until the launch completes.
- * sync:    device workspace of Q8G_STACK_SYNC_WORDS uint32, zero-filled by the
- *          caller before its first use; it carries a launch counter between
- *          launches, so launches sharing it must be ordered (one stream).
+ * sync:    device workspace of Q8G_STACK_SYNC_WORDS uint32 (64-byte aligned),
+ *          zero-filled by the caller before its first use; it carries a barrier
+ *          count between launches, so launches sharing it must be ordered (one
+ *          stream) and run on one device.
  * The launch needs one resident workgroup per compute unit (cooperative
- * launch); if the device cannot guarantee that, Q8G_ERR_LAUNCH is returned
- * and nothing runs. */
+ * launch, at most 1024 compute units); if the device cannot guarantee that,
+ * Q8G_ERR_LAUNCH is returned and nothing runs. */
 q8g_status q8_decode_stack(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, int nops, uint32_t *sync,
                            void *stream);
 

@@ -97,14 +97,33 @@ def test_odd_shapes_and_repeated_launches(q8, orc):
 
 
 def test_single_projection(q8, orc):
-    """One op: no barrier inside the launch; the workspace count still advances."""
+    """One op: no barrier inside the launch, so the workspace's barrier count and
+    counters stay zero over three launches."""
     print("case: single projection", flush=True)
     ops = [synth.Gemv("only", (4096,), 1024)]
     hostin, st, ref, got = run_both(q8, ops, synth.TAG_TEST + 3, launches=3)
     assert np.array_equal(ref[0][0], got[0][0])
     check_oracle(orc, ops, hostin, got)
-    flags = host(st.plan.sync)[64::16][:256]
-    assert np.all(flags == flags[0]) and flags[0] == 3
+    ws = host(st.plan.sync)
+    assert ws[0] == 0 and np.all(ws[64:64 + 16 * 64:64] == 0)
+
+
+def test_workspace_counts_barriers(q8):
+    """Three launches of a 5-op stack: the barrier count is 3 * 4, and each of the 16
+    counters holds 12 times the number of workgroups that add to it."""
+    import torch
+
+    print("case: barrier count over three launches", flush=True)
+    ops = synth.q8_stack_08b(layers=1, vocab=2000)
+    hostin, st, ref, got = run_both(q8, ops, synth.TAG_TEST + 7, launches=3)
+    for (y0, _, _), (y1, _, _) in zip(ref, got):
+        assert np.array_equal(y0, y1)
+    ws = host(st.plan.sync).view(np.uint32)
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    nb = 3 * (len(ops) - 1)
+    assert ws[0] == nb
+    per = np.array([(G - c + 15) // 16 for c in range(16)], dtype=np.int64)
+    assert np.array_equal(ws[64:64 + 16 * 64:64].astype(np.int64), nb * per)
 
 
 def test_full_08b_stack(q8, orc):
