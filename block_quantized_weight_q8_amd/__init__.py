@@ -110,10 +110,12 @@ def load_library(path: str = LIB_PATH):
     lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
     lib.q8g_flush.argtypes = [_P, _I64, ctypes.c_uint32, _P]
     lib.q8_decode_stack.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
+    lib.q8_decode_stack_static.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
     lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
                                     ctypes.POINTER(ctypes.c_int)]
     for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
                "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
+               "q8_decode_stack_static",
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
                "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
                "q8_gateup_silu", "q8_gateup_rmsnorm_silu",
@@ -524,6 +526,14 @@ class DecodeStackPlan:
         st = load_library().q8_decode_stack(self.host, self.dev.data_ptr(), self.nops, self.sync.data_ptr(),
                                             _stream(stream))
         _check("q8_decode_stack", st)
+
+    def run_static(self, stream=None, status=None):
+        """Enqueue one launch through q8_decode_stack_static: the library's own static
+        workspace instead of self.sync (cleared by the call itself). status: None or an
+        int32 device tensor of one element that a launch which gave up waiting sets to 1."""
+        sp = _ptr(status, "status", (torch.int32,), (1,), optional=True)
+        st = load_library().q8_decode_stack_static(self.host, self.dev.data_ptr(), self.nops, sp, _stream(stream))
+        _check("q8_decode_stack_static", st)
 
     def error_flag(self) -> int:
         """Nonzero if a launch gave up waiting at a barrier (synchronizes)."""

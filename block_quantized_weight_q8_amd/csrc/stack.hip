@@ -50,6 +50,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gemv_device.hpp"
 #include "q8gemv.h"
 
@@ -863,6 +865,23 @@ q8g_status launch_stack(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, in
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
 
+// whether [p, p + bytes) overlaps any input or output of any op
+bool touches_any(const q8g_stack_op *ops, int nops, const void *p, int64_t bytes)
+{
+    for (int i = 0; i < nops; ++i) {
+        const q8g_stack_op &a = ops[i];
+        if (overlap(p, bytes, a.x, a.K * 4) || overlap(p, bytes, a.qx, a.K) || overlap(p, bytes, a.dx, a.K / 16))
+            return true;
+        for (int q = 0; q < a.nparts; ++q) {
+            const q8g_part &pt = a.parts[q];
+            if (overlap(p, bytes, pt.w, pt.n * a.K) || overlap(p, bytes, pt.dw, pt.n * (a.K / 32) * 2) ||
+                overlap(p, bytes, pt.y, pt.n * 4) || overlap(p, bytes, pt.residual, pt.n * 4))
+                return true;
+        }
+    }
+    return false;
+}
+
 q8g_status check_call(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, int nops)
 {
     if (nops < 0) return Q8G_ERR_ARG;
@@ -882,4 +901,61 @@ extern "C" q8g_status q8_decode_stack(const q8g_stack_op *ops, const q8g_stack_o
     if (!sync) return Q8G_ERR_NULL;
     if (!aligned(sync, 64)) return Q8G_ERR_ALIGN;
     return launch_stack(ops, ops_dev, nops, sync, nullptr, static_cast<hipStream_t>(stream));
+}
+
+// ---- the same step for callers that cannot allocate --------------------------
+// The synchronization workspace lives in this file-scope array instead of a
+// caller buffer. In host code `scratch` is only a stand-in for the symbol: its
+// device address (one per device) comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) uint32_t scratch[Q8G_STACK_SYNC_WORDS];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch[kMaxDevices];  // device address of `scratch` on each device, once taken
+
+q8g_status scratch_on(int dev, uint32_t **out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return Q8G_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return Q8G_ERR_LAUNCH;
+        g_scratch[dev] = static_cast<uint32_t *>(p);
+    }
+    *out = g_scratch[dev];
+    return Q8G_OK;
+}
+
+// zero n words (a kernel, not a memset node, so that a captured graph replays it faithfully)
+__global__ __launch_bounds__(1024) void zero_words(uint32_t *__restrict__ p, int n)
+{
+    for (int i = blockIdx.x * 1024 + threadIdx.x; i < n; i += gridDim.x * 1024) p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" q8g_status q8_decode_stack_static(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, int nops,
+                                             uint32_t *status, void *stream)
+{
+    const q8g_status st = check_call(ops, ops_dev, nops);
+    if (st != Q8G_OK || nops == 0) return st;
+    if (status && !aligned(status, 4)) return Q8G_ERR_ALIGN;
+    if (status && touches_any(ops, nops, status, 4)) return Q8G_ERR_OVERLAP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return Q8G_ERR_LAUNCH;
+    uint32_t *ws = nullptr;
+    const q8g_status sst = scratch_on(dev, &ws);
+    if (sst != Q8G_OK) return sst;
+    // every call starts from a cleared workspace: no state carries over between calls
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *p = ws;
+    int n = Q8G_STACK_SYNC_WORDS;
+    void *zargs[] = {&p, &n};
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&zero_words), dim3((n + 1023) / 1024), dim3(1024), zargs, 0, s) !=
+        hipSuccess)
+        return Q8G_ERR_LAUNCH;
+    return launch_stack(ops, ops_dev, nops, ws, status, s);
 }

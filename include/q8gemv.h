@@ -22,7 +22,8 @@
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; nothing is synchronized, allocated or freed, and no
  *     environment variable is read. The library holds no mutable global
- *     state, so calls are thread-safe and may be captured into a HIP graph.
+ *     state apart from q8_decode_stack_static's per-device workspace, so the
+ *     other calls are thread-safe and may be captured into a HIP graph.
  *   - Q8_0 data is stored as two planes: codes int8 [N][K] row-major and scale
  *     bits (IEEE binary16) [N][K/32] row-major; scale b of row n covers codes
  *     32b..32b+31 of that row. A quantized activation is codes int8 [K] plus
@@ -291,6 +292,27 @@ typedef struct {
  * Q8G_ERR_LAUNCH is returned and nothing runs. */
 q8g_status q8_decode_stack(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, int nops, uint32_t *sync,
                            void *stream);
+
+/* ---- the same step for callers that cannot allocate ------------------------
+ * For callers that may not call hipMalloc or any allocating routine: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. q8_decode_stack_static is q8_decode_stack without the `sync`
+ * argument: its synchronization workspace is a static device array of
+ * Q8G_STACK_SYNC_WORDS uint32 inside the library (one copy per device, held
+ * until the process ends). Each call enqueues a small kernel that clears that
+ * array, then the same launch as q8_decode_stack, so outputs are bit-identical
+ * to q8_decode_stack's and no state carries over from one call to the next.
+ * Nothing is allocated or freed.
+ * status: NULL, or a device uint32 (4-byte aligned) that the launch sets to 1
+ *         if it gave up waiting (its outputs are then incomplete); the library
+ *         never clears it.
+ * Limits: those of q8_decode_stack (Q8G_STACK_MAX_K, one workgroup per compute
+ * unit on at most 1024 compute units, at most 256 devices); beyond them the
+ * call returns an error and enqueues nothing.
+ * All calls on one device share its array: calls that overlap in time on one
+ * device (other streams, other threads) race on it and must not be issued. */
+q8g_status q8_decode_stack_static(const q8g_stack_op *ops, const q8g_stack_op *ops_dev, int nops, uint32_t *status,
+                                  void *stream);
 
 /* Launch configuration the library picks for a GEMV over n_total rows of K
  * (all parts of a stacked call together): output rows per wave and waves per

@@ -369,3 +369,16 @@ def test_decode_stack_validation(lib):
     # op 1 writing op 0's input (read before op 1 runs): a race-free chain is the other way round
     assert f(ops((X, 64, [(W, DW, 8, Y, None)]), (X + 0x100000, 64, [(W, DW, 16, X, None)])), DEV, 2, SYNC,
              None) == ERR_OVERLAP
+
+    # the same step over the library's static workspace: the same checks, plus the status word
+    h = lib.q8_decode_stack_static
+    h.argtypes = [ctypes.POINTER(Op), P, ctypes.c_int, P, P]
+    h.restype = ctypes.c_int
+    assert h(good, DEV, -1, None, None) == ERR_ARG
+    assert h(good, DEV, 0, None, None) == OK
+    assert h(good, None, 1, None, None) == ERR_NULL
+    assert h(good, DEV + 4, 1, None, None) == ERR_ALIGN
+    assert h(good, DEV, 1, SYNC + 2, None) == ERR_ALIGN  # status
+    assert h(good, DEV, 1, Y + 4, None) == ERR_OVERLAP  # status over an output
+    assert h(ops((X, 48, [(W, DW, 8, Y, None)])), DEV, 1, None, None) == ERR_SHAPE
+    assert h(ops((X, 64, [(W, DW, 8, X, None)])), DEV, 1, None, None) == ERR_OVERLAP
