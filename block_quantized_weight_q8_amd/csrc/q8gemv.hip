@@ -201,11 +201,8 @@ struct RowRef {
 // batch's loads in flight together, and the next batch is requested before the
 // current one is consumed: a multi-chunk row costs about one memory round trip,
 // not one per chunk.
-#ifndef Q8G_BATCH
-#define Q8G_BATCH 4
-#endif
-constexpr int kBatch = Q8G_BATCH;
-static_assert(kBatch == 4 || kBatch == 8, "a batch holds 4 or 8 items (a multiple of R)");
+constexpr int kBatch = 4;
+static_assert(kBatch == 4, "a batch holds 4 items (a multiple of R)");
 
 struct Batch {
     int4 w[kBatch];      // weight bytes of item j (16 per lane)
@@ -667,19 +664,7 @@ hipError_t launch_gemv(const Parts &p, const void *x, const uint16_t *dx, const 
 // rows per wave R as many as keep at least ~8 waves per compute unit busy (at
 // most 2 for bf16); 4 waves per workgroup, except fused launches over fewer
 // than 32768 rows, where 8 waves share the activation quantization.
-#ifndef Q8G_WAVES
-#define Q8G_WAVES 4
-#endif
-#ifndef Q8G_FUSED_WAVES
-#define Q8G_FUSED_WAVES 0  // 0: by shape
-#endif
-#ifndef Q8G_FUSED_ROWS
-#define Q8G_FUSED_ROWS 0  // 0: by shape
-#endif
-#ifndef Q8G_BF16_ROWS
-#define Q8G_BF16_ROWS 0  // 0: by shape
-#endif
-constexpr int kWavesPerGroup = Q8G_WAVES;
+constexpr int kWavesPerGroup = 4;
 constexpr int64_t kFusedWideRows = 32768;
 
 int rows_per_wave(int64_t n_total)
@@ -701,12 +686,8 @@ Config pick_config(q8g_dtype dt, int64_t n_total)
     if (dt == Q8G_BF16 || dt == Q8G_F16) {
         // 16-bit rows are twice as long: two rows per wave already keep 4 KiB in flight
         if (c.rows > 2) c.rows = 2;
-        if (Q8G_BF16_ROWS) c.rows = Q8G_BF16_ROWS;
     }
-    if (dt == Q8G_Q8_0_F32) {
-        if (Q8G_FUSED_ROWS) c.rows = Q8G_FUSED_ROWS;
-        c.waves = Q8G_FUSED_WAVES ? Q8G_FUSED_WAVES : (n_total < kFusedWideRows ? 8 : 4);
-    }
+    if (dt == Q8G_Q8_0_F32) c.waves = n_total < kFusedWideRows ? 8 : 4;
     return c;
 }
 
@@ -876,13 +857,8 @@ bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }  // finite, not
 // Measured on MI355X over the 0.8B MLP (F = 3584, K = 1024): R = 4, W = 8
 // (16 pairs, 224 workgroups) 4.0 us; R = 4, W = 4 4.1; R = 2, W = 8 4.4;
 // R = 2, W = 16 5.0; R = 1, W = 8 6.3.
-#ifndef Q8G_SILU_ROWS
-#define Q8G_SILU_ROWS 4
-#endif
-#ifndef Q8G_SILU_WAVES
-#define Q8G_SILU_WAVES 8
-#endif
-static_assert(32 % (Q8G_SILU_ROWS * Q8G_SILU_WAVES / 2) == 0, "row pairs per workgroup divide 32");
+constexpr int kSiluRows = 4, kSiluWaves = 8;
+static_assert(32 % (kSiluRows * kSiluWaves / 2) == 0, "row pairs per workgroup divide 32");
 
 template <Dt DT, int R, int W, int EPI>
 hipError_t launch_epi(const Parts &p, const void *x, const uint16_t *dx, const float *gamma, float eps, int64_t K,
@@ -948,7 +924,7 @@ q8g_status gateup_silu(int kind, const int8_t *qg, const uint16_t *dg, const int
     const bool norm = kind == kKindNorm && K > 0;
     const void *xq = kind == Q8G_Q8_0 ? x : nullptr;
     const uint16_t *dxq = kind == Q8G_Q8_0 ? dx : nullptr;
-    constexpr int SR = Q8G_SILU_ROWS, SW = Q8G_SILU_WAVES;
+    constexpr int SR = kSiluRows, SW = kSiluWaves;
     const hipError_t e =
         f32_out ? (norm ? launch_epi<Dt::Q8NORM, SR, SW, 2>(p, x, nullptr, gamma, eps, K, F, s, nullptr, nullptr)
                         : launch_epi<Dt::Q8, SR, SW, 2>(p, xq, dxq, nullptr, 0.0f, K, F, s, nullptr, nullptr))

@@ -111,8 +111,10 @@ def test_silu_mul_quantize_special(q8, orc):
 # --------------------------------------------------------------------------- fused into the GEMV
 
 
+# (300, 7) x 2560 and x 3584: 8 waves per workgroup with two activation passes (2048 < K <= 4096)
 NORM_SHAPES = [((1,), 32), ((2048, 1024, 1024), 1024), ((3584, 3584), 1024), ((300, 7), 2048),
-               ((9,), 16384), ((8200,), 1024), ((40000,), 2080), ((200003,), 64), ((5, 6, 7, 8), 96)]
+               ((9,), 16384), ((8200,), 1024), ((40000,), 2080), ((200003,), 64), ((5, 6, 7, 8), 96),
+               ((300, 7), 2560), ((300, 7), 3584)]
 
 
 @pytest.mark.parametrize("sizes,k", NORM_SHAPES)
@@ -138,7 +140,8 @@ def test_rmsnorm_gemv_fused_equals_two_launches(q8, orc, sizes, k):
         within(fused[i], yr, S, f"rmsnorm part {i} {sizes[i]}x{k}")
 
 
-SILU_SHAPES = [(1, 32), (7, 96), (1024, 3584), (4096, 2048), (8200, 1024), (40000, 2080), (5, 16384)]
+# 40000 x 1056: 4 waves per workgroup with two activation passes
+SILU_SHAPES = [(1, 32), (7, 96), (1024, 3584), (4096, 2048), (8200, 1024), (40000, 2080), (5, 16384), (40000, 1056)]
 
 
 @pytest.mark.parametrize("n,k", SILU_SHAPES)

@@ -497,8 +497,10 @@ def test_misaligned_and_overlap_raise(q8, torch_mod):
 # --------------------------------------------------------------------------- fused quantize + GEMV
 
 
+# 40000 x 1056: 4 waves per workgroup (n >= 32768) with two activation passes of 4 values per
+# thread (1024 < K <= 2048)
 @pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (300, 1024), (1025, 3584), (4096, 1024), (64, 1024 + 96),
-                                 (9, 16384), (8200, 1024), (200003, 64), (40000, 2080)])
+                                 (9, 16384), (8200, 1024), (200003, 64), (40000, 2080), (40000, 1056)])
 def test_q8_fused_equals_quantize_then_gemv(q8, orc, n, k):
     """The f32-input launch (quantized inside) is bit-identical to q8_quantize_act + q8_gemv."""
     print_case("fused f32 gemv", n, k)
