@@ -6,8 +6,9 @@ shares no code with the HIP library. Arrays are numpy; results are f64.
 
 What it computes is stated, with its sources, at the top of oracle.c:
 the Q8_0 activation quantizer, the per-block int32 dot, the Q8_0 GEMV (single
-vector and small batch), the bf16 and f16 GEMVs, and the RMS-normalization and
-gated-activation steps folded into a projection's prologue, of "Filling in the blanks: Inference using Phobos" (section Fast
+vector and small batch), the bf16 and f16 GEMVs, the RMS-normalization and
+gated-activation steps folded into a projection's prologue, and the PTQ1_0
+ternary GEMV with its Hadamard-rotated activation, of "Filling in the blanks: Inference using Phobos" (section Fast
 Decode) and "One level down: #002 the same compiler on a GPU" (sections
 Emitting for a GPU and The numerical contract).
 """
@@ -73,6 +74,18 @@ def _bind(lib):
     lib.orc_rmsnorm.restype = None
     lib.orc_silu_mul.argtypes = [_P, _I64, _P]
     lib.orc_silu_mul.restype = None
+    lib.orc_quantize_blocks.argtypes = [_P, _I64, _I64, _P, _P]
+    lib.orc_quantize_blocks.restype = None
+    lib.orc_ptq1_decode.argtypes = [_P, _I64, _P, _P]
+    lib.orc_ptq1_decode.restype = None
+    lib.orc_hadamard128.argtypes = [_P, _I64, _P]
+    lib.orc_hadamard128.restype = None
+    lib.orc_ptq1_activation.argtypes = [_P, _I64, _P, _P, _P]
+    lib.orc_ptq1_activation.restype = None
+    lib.orc_ptq1_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P]
+    lib.orc_ptq1_gemv.restype = None
+    lib.orc_ptq1_gemv_mt.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int]
+    lib.orc_ptq1_gemv_mt.restype = ctypes.c_int
     return lib
 
 
@@ -196,6 +209,76 @@ class Oracle:
             self.lib.orc_q8_gemv_batch(pw, pdw, pq, pdx, pr, n, k, b, y.ctypes.data, s.ctypes.data)
         return y, s
 
+    # PTQ1_0: ternary weights, 128 per 28-byte block, Hadamard-rotated activation
+    PTQ1_BLOCK = 128
+    PTQ1_BYTES = 28
+
+    def quantize_blocks(self, x, block):
+        """The activation quantizer over blocks of `block` values: (codes int8, scale bits)."""
+        x, px = _c(x, np.float32)
+        k = x.shape[0]
+        if x.ndim != 1 or k % block:
+            raise ValueError("x must be 1-D with length a multiple of the block")
+        qx = np.empty(k, np.int8)
+        dx = np.empty(k // block, np.uint16)
+        self.lib.orc_quantize_blocks(px, k, block, qx.ctypes.data, dx.ctypes.data)
+        return qx, dx
+
+    def ptq1_decode(self, w):
+        """Trits int8 [N, K] and scale bits uint16 [N, K/128] of PTQ1_0 rows w uint8 [N, 28 K/128]."""
+        w, pw = _c(w, np.uint8)
+        n, nbytes = w.shape
+        assert nbytes % self.PTQ1_BYTES == 0
+        nb = nbytes // self.PTQ1_BYTES
+        t = np.empty((n, nb * self.PTQ1_BLOCK), np.int8)
+        sc = np.empty((n, nb), np.uint16)
+        self.lib.orc_ptq1_decode(pw, n * nb, t.ctypes.data, sc.ctypes.data)
+        return t, sc
+
+    def hadamard128(self, x):
+        """f32 H x / sqrt(128) per 128-value block (Sylvester order), from f64 sums."""
+        x, px = _c(x, np.float32)
+        k = x.shape[0]
+        assert x.ndim == 1 and k % self.PTQ1_BLOCK == 0
+        out = np.empty(k, np.float32)
+        self.lib.orc_hadamard128(px, k, out.ctypes.data)
+        return out
+
+    def ptq1_activation(self, x):
+        """(rotated f32, codes int8 [K], scale bits [K/128]) of an activation x f32 [K]."""
+        x, px = _c(x, np.float32)
+        k = x.shape[0]
+        assert x.ndim == 1 and k % self.PTQ1_BLOCK == 0
+        rot = np.empty(k, np.float32)
+        qx = np.empty(k, np.int8)
+        dx = np.empty(k // self.PTQ1_BLOCK, np.uint16)
+        self.lib.orc_ptq1_activation(px, k, rot.ctypes.data, qx.ctypes.data, dx.ctypes.data)
+        return rot, qx, dx
+
+    def ptq1_gemv(self, w, qx, dx, residual=None, nthreads: int = 0):
+        """(y, S) in f64 for PTQ1_0 rows w uint8 [N, 28 K/128] and the rotated, quantized
+        activation qx int8 [K], dx [K/128]."""
+        w, pw = _c(w, np.uint8)
+        qx, pq = _c(qx, np.int8)
+        dx, pdx = _c(dx, np.uint16)
+        n = w.shape[0]
+        k = qx.shape[0]
+        assert k % self.PTQ1_BLOCK == 0 and w.shape == (n, k // self.PTQ1_BLOCK * self.PTQ1_BYTES)
+        assert dx.shape == (k // self.PTQ1_BLOCK,)
+        pr = None
+        if residual is not None:
+            residual, pr = _c(residual, np.float32)
+            assert residual.shape == (n,)
+        y = np.empty(n, np.float64)
+        s = np.empty(n, np.float64)
+        if nthreads:
+            rc = self.lib.orc_ptq1_gemv_mt(pw, pq, pdx, pr, n, k, y.ctypes.data, s.ctypes.data, nthreads)
+            if rc < 0:
+                raise MemoryError("oracle thread setup failed")
+        else:
+            self.lib.orc_ptq1_gemv(pw, pq, pdx, pr, n, k, y.ctypes.data, s.ctypes.data)
+        return y, s
+
     def f16_gemv(self, w, x, residual=None, nthreads: int = 0):
         return self._16bit_gemv("f16", w, x, residual, nthreads)
 
@@ -264,3 +347,11 @@ def rmsnorm(x, gamma, eps):
 
 def silu_mul(gu):
     return get().silu_mul(gu)
+
+
+def ptq1_activation(x):
+    return get().ptq1_activation(x)
+
+
+def ptq1_gemv(w, qx, dx, residual=None, nthreads: int = 0):
+    return get().ptq1_gemv(w, qx, dx, residual, nthreads)

@@ -20,7 +20,10 @@
  *        decode the normalization and the activation are each fused with the
  *        projection after them), "The numerical contract" (bf16 weights and
  *        activations, f32 accumulators) and "The bench" (the same engine in f16).
- *   [P]  section "Q4_K_M" also names a block's RMS normalization and gated MLP.
+ *   [P]  section "Q4_K_M" also names a block's RMS normalization and gated MLP;
+ *        section "PrismML Ternary-Bonsai" the PTQ1_0 ternary format (128
+ *        weights in 28 bytes, a Hadamard-rotated activation shared by the
+ *        projections that read it; its footnote 11 names the rotation's origin).
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - weight and activation block scales are IEEE binary16;
@@ -34,6 +37,8 @@
  *     eps) formed in f64 and rounded once to f32, ss = sum of x^2 in f64;
  *   - gated activation: a = silu(gate) * up = gate * up / (1 + exp(-gate)),
  *     formed in f64 and rounded once to f32.
+ *   - PTQ1_0: the block layout, rotation and activation blocking stated at the
+ *     PTQ1_0 section below.
  *
  * Precision: every Q8_0 block term isum·dw·dx is exact in f64 (20 + 11 + 11
  * significant bits); every bf16 product is exact in f64 (8 + 8 bits), every
@@ -129,34 +134,40 @@ uint16_t orc_f32_to_f16(float value)
 
 /* ---- activation quantization ([P] Fast Decode: quantize an activation once
  * into the same block format as the weights) ------------------------------ */
-void orc_quantize_act(const float *x, int64_t K, int8_t *qx, uint16_t *dx)
+void orc_quantize_blocks(const float *x, int64_t K, int64_t block, int8_t *qx, uint16_t *dx)
 {
-    for (int64_t b = 0; b < K / ORC_QBLOCK; ++b) {
-        const float *xb = x + b * ORC_QBLOCK;
+    for (int64_t b = 0; b < K / block; ++b) {
+        const float *xb = x + b * block;
         float amax = 0.0f;
-        for (int i = 0; i < ORC_QBLOCK; ++i) {
+        for (int64_t i = 0; i < block; ++i) {
             float a = fabsf(xb[i]);
             if (a > amax)
                 amax = a;
         }
         float d = amax / 127.0f;
         if (d == 0.0f) {
-            for (int i = 0; i < ORC_QBLOCK; ++i)
-                qx[b * ORC_QBLOCK + i] = 0;
+            for (int64_t i = 0; i < block; ++i)
+                qx[b * block + i] = 0;
             dx[b] = 0;
             continue;
         }
-        for (int i = 0; i < ORC_QBLOCK; ++i) {
+        for (int64_t i = 0; i < block; ++i) {
             float t = xb[i] / d;
             float r = rintf(t);
             if (r > 127.0f)
                 r = 127.0f;
             if (r < -127.0f)
                 r = -127.0f;
-            qx[b * ORC_QBLOCK + i] = (int8_t)r;
+            qx[b * block + i] = (int8_t)r;
         }
         dx[b] = orc_f32_to_f16(d);
     }
+}
+
+/* Q8_0: blocks of 32 values */
+void orc_quantize_act(const float *x, int64_t K, int8_t *qx, uint16_t *dx)
+{
+    orc_quantize_blocks(x, K, ORC_QBLOCK, qx, dx);
 }
 
 /* ---- neighbour steps folded into a projection's prologue ([H] Emitting for a
@@ -288,10 +299,114 @@ void orc_q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, c
                     S + b * N);
 }
 
+/* ---- PTQ1_0 ternary blocks ([P] PrismML Ternary-Bonsai: weights -1, 0 or +1;
+ * 128 weights in 28 bytes; the activation rotated by a Hadamard transform, which
+ * spreads outliers over the whole block; the rotated activation computed once and
+ * shared by every projection that reads the same input). The pages give no byte
+ * layout; the readings (listed in the design notes) are:
+ *   - a block is 26 bytes of base-3 digits followed by its binary16 scale s
+ *     (2 bytes, little-endian); weight i (0..127) of the block is
+ *     s * (digit_i - 1), digit_i being digit i % 5, least significant first, of
+ *     byte i / 5 (byte 25 holds weights 125..127); a row is K/128 blocks;
+ *   - the rotation of each 128-value block of x is H x / sqrt(128), H the
+ *     Sylvester-ordered Hadamard matrix, H[i][j] = (-1)^popcount(i & j); each
+ *     output is the f64 sum over j in ascending order, divided by sqrt(128) in
+ *     f64 and rounded once to f32;
+ *   - the rotated activation is quantized with the quantizer above in blocks
+ *     of 128 values, one scale per weight block;
+ *   - y[n] = sum_b isum(n, b) * f16(s[n][b]) * f16(dx[b]) (+ r[n]), with
+ *     isum(n, b) = sum_i t[n][128b + i] * q[128b + i] exact (|isum| <= 16256);
+ *     every term is exact in f64 (14 + 11 + 11 significant bits). */
+#define ORC_PTQ1_BLOCK 128
+#define ORC_PTQ1_BYTES 28
+#define ORC_PTQ1_TRIT_BYTES 26
+
+/* binary16 scale bits of the block at blk (little-endian, after the trits) */
+uint16_t orc_ptq1_scale(const uint8_t *blk)
+{
+    return (uint16_t)(blk[ORC_PTQ1_TRIT_BYTES] | (blk[ORC_PTQ1_TRIT_BYTES + 1] << 8));
+}
+
+/* trit (-1, 0, +1) of weight i of the block at blk */
+int orc_ptq1_trit(const uint8_t *blk, int i)
+{
+    int v = blk[i / 5];
+    for (int k = 0; k < i % 5; ++k)
+        v /= 3;
+    return v % 3 - 1;
+}
+
+/* the blocks' trits and scale bits, for checking the packing */
+void orc_ptq1_decode(const uint8_t *w, int64_t nblocks, int8_t *t, uint16_t *s)
+{
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const uint8_t *blk = w + b * ORC_PTQ1_BYTES;
+        for (int i = 0; i < ORC_PTQ1_BLOCK; ++i)
+            t[b * ORC_PTQ1_BLOCK + i] = (int8_t)orc_ptq1_trit(blk, i);
+        s[b] = orc_ptq1_scale(blk);
+    }
+}
+
+static int orc_parity(unsigned v)
+{
+    int p = 0;
+    for (; v; v >>= 1)
+        p ^= (int)(v & 1u);
+    return p;
+}
+
+void orc_hadamard128(const float *x, int64_t K, float *out)
+{
+    const double norm = sqrt((double)ORC_PTQ1_BLOCK);
+    for (int64_t b = 0; b < K / ORC_PTQ1_BLOCK; ++b)
+        for (int i = 0; i < ORC_PTQ1_BLOCK; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < ORC_PTQ1_BLOCK; ++j) {
+                const double v = (double)x[b * ORC_PTQ1_BLOCK + j];
+                acc += orc_parity((unsigned)(i & j)) ? -v : v;
+            }
+            out[b * ORC_PTQ1_BLOCK + i] = (float)(acc / norm);
+        }
+}
+
+/* the activation of a PTQ1_0 projection: rotated, then quantized per 128 values */
+void orc_ptq1_activation(const float *x, int64_t K, float *rot, int8_t *qx, uint16_t *dx)
+{
+    orc_hadamard128(x, K, rot);
+    orc_quantize_blocks(rot, K, ORC_PTQ1_BLOCK, qx, dx);
+}
+
+void orc_ptq1_gemv(const uint8_t *w, const int8_t *qx, const uint16_t *dx, const float *residual, int64_t N,
+                   int64_t K, double *y, double *S)
+{
+    const int64_t nb = K / ORC_PTQ1_BLOCK;
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = w + (n * nb + b) * ORC_PTQ1_BYTES;
+            int32_t s = 0, sa = 0;
+            for (int i = 0; i < ORC_PTQ1_BLOCK; ++i) {
+                int32_t p = (int32_t)orc_ptq1_trit(blk, i) * (int32_t)qx[b * ORC_PTQ1_BLOCK + i];
+                s += p;
+                sa += p < 0 ? -p : p;
+            }
+            double scale = orc_f16_value(orc_ptq1_scale(blk)) * orc_f16_value(dx[b]);
+            acc += (double)s * scale;
+            mag += (double)sa * fabs(scale);
+        }
+        if (residual) {
+            acc += (double)residual[n];
+            mag += fabs((double)residual[n]);
+        }
+        y[n] = acc;
+        S[n] = mag;
+    }
+}
+
 /* ---- row-partitioned threading (same per-row arithmetic, so identical
  * results to the single-threaded calls) ------------------------------------ */
 typedef struct {
-    int bf16; /* 0: Q8_0, 1: bf16, 2: f16 */
+    int bf16; /* 0: Q8_0, 1: bf16, 2: f16, 3: PTQ1_0 */
     const void *w;
     const uint16_t *dw;
     const void *x;
@@ -314,6 +429,9 @@ static void *orc_run_job(void *arg)
     else if (j->bf16 == 2)
         orc_f16_gemv((const uint16_t *)j->w + j->n0 * j->K, (const uint16_t *)j->x, r, rows, j->K,
                      j->y + j->n0, j->S + j->n0);
+    else if (j->bf16 == 3)
+        orc_ptq1_gemv((const uint8_t *)j->w + j->n0 * (j->K / ORC_PTQ1_BLOCK) * ORC_PTQ1_BYTES,
+                      (const int8_t *)j->x, j->dx, r, rows, j->K, j->y + j->n0, j->S + j->n0);
     else
         orc_q8_gemv((const int8_t *)j->w + j->n0 * j->K, j->dw + j->n0 * (j->K / ORC_QBLOCK),
                     (const int8_t *)j->x, j->dx, r, rows, j->K, j->y + j->n0, j->S + j->n0);
@@ -373,5 +491,12 @@ int orc_f16_gemv_mt(const uint16_t *w, const uint16_t *x, const float *residual,
                     int64_t K, double *y, double *S, int nthreads)
 {
     orc_job p = {2, w, NULL, x, NULL, residual, 0, 0, K, y, S};
+    return orc_run_threads(p, N, nthreads);
+}
+
+int orc_ptq1_gemv_mt(const uint8_t *w, const int8_t *qx, const uint16_t *dx, const float *residual, int64_t N,
+                     int64_t K, double *y, double *S, int nthreads)
+{
+    orc_job p = {3, w, NULL, qx, dx, residual, 0, 0, K, y, S};
     return orc_run_threads(p, N, nthreads);
 }

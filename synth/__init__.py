@@ -20,6 +20,11 @@ on a GPU" (§Emitting for a GPU: the bf16 gate+up projection, 1024->7168 on the
 * residual: N(0, 1) in f32.
 * normalization input: N(0, 1) in f32; its weights gamma: 1 + 0.1 N(0, 1).
 * gated activation input [gate | up]: gate 2 N(0, 1), up N(0, 1), in f32.
+* PTQ1_0 ternary weights ("Filling in the blanks", §PrismML Ternary-Bonsai: weights -1, 0
+  or +1, 128 of them in 28 bytes): trits uniform over {-1, 0, +1}; one scale per 128
+  weights, |N(0, 1)| * 0.02 in f32 rounded to binary16; packed as 26 bytes of base-3 digits
+  (digit = trit + 1, five per byte, least significant first) followed by the scale bits,
+  little-endian (the layout reading is stated in the design notes).
 
 Every matrix j of workload `tag` draws from
 ``np.random.default_rng(np.random.SeedSequence([tag, j]))`` in the order
@@ -43,7 +48,11 @@ TAG_F16_GATEUP = 5
 TAG_Q8_BATCH = 6
 TAG_NEIGHBOUR = 7
 TAG_LAYERS = 8
+TAG_PTQ1 = 9
 TAG_TEST = 100
+
+PTQ1_BLOCK = 128  # weights per PTQ1_0 block
+PTQ1_BYTES = 28   # bytes per PTQ1_0 block: 26 of base-3 digits, 2 of binary16 scale
 
 
 def rng_for(tag: int, j: int) -> np.random.Generator:
@@ -74,6 +83,36 @@ def q8_weights(rng: np.random.Generator, n: int, k: int):
     s = np.abs(rng.standard_normal((n, k // QBLOCK), dtype=np.float32))
     s *= np.float32(0.02 / 127.0)
     return qw, f32_to_f16_bits(s)
+
+
+def ptq1_pack(trits: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Encode ternary weights trits int8 [n, k] (-1, 0, +1) with scale bits uint16
+    [n, k/128] into PTQ1_0 rows uint8 [n, 28 k/128]."""
+    n, k = trits.shape
+    if k % PTQ1_BLOCK:
+        raise ValueError("k must be a multiple of 128")
+    nb = k // PTQ1_BLOCK
+    digits = np.zeros((n, nb, 130), np.int32)  # 26 bytes of five digit slots
+    digits[..., :PTQ1_BLOCK] = trits.reshape(n, nb, PTQ1_BLOCK).astype(np.int32) + 1
+    place = np.array([1, 3, 9, 27, 81], np.int32)
+    packed = (digits.reshape(n, nb, 26, 5) * place).sum(axis=-1)
+    out = np.empty((n, nb, PTQ1_BYTES), np.uint8)
+    out[..., :26] = packed.astype(np.uint8)
+    sb = np.asarray(scale_bits, dtype=np.uint16).reshape(n, nb)
+    out[..., 26] = (sb & 0xFF).astype(np.uint8)
+    out[..., 27] = (sb >> 8).astype(np.uint8)
+    return out.reshape(n, nb * PTQ1_BYTES)
+
+
+def ptq1_weights(rng: np.random.Generator, n: int, k: int):
+    """(PTQ1_0 rows uint8 [n, 28 k/128], trits int8 [n, k], scale bits uint16 [n, k/128])."""
+    if k % PTQ1_BLOCK:
+        raise ValueError("k must be a multiple of 128")
+    t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+    s = np.abs(rng.standard_normal((n, k // PTQ1_BLOCK), dtype=np.float32))
+    s *= np.float32(0.02)
+    sb = f32_to_f16_bits(s)
+    return ptq1_pack(t, sb), t, sb
 
 
 def activation_f32(rng: np.random.Generator, k: int) -> np.ndarray:

@@ -4,7 +4,8 @@ Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch. The
 run against the real oracle (test_oracle.py) and against deliberately broken copies
 of it (test_oracle_mutants.py), which must each fail at least one pin.
 
-Independent references used here (none calls into the oracle):
+Independent references used here (none calls into the oracle; the PTQ1_0 packing of
+synth.ptq1_pack is the encoder the oracle's decoder is checked against):
   * numpy's own binary16 cast and f32 bit reinterpretation for bf16;
   * a numpy float32 quantizer (IEEE f32 division, np.rint ties-to-even);
   * Python integers and fractions.Fraction for exact block sums and dot products;
@@ -12,7 +13,12 @@ Independent references used here (none calls into the oracle):
   * closed forms that follow from the definitions ("Filling in the blanks: Inference
     using Phobos", section Fast Decode: 32 int8 values with their own scale, the
     block math in int8; "One level down: #002 the same compiler on a GPU", section
-    The numerical contract: bf16 in, f32 accumulate).
+    The numerical contract: bf16 in, f32 accumulate);
+  * for PTQ1_0 ("Filling in the blanks", section PrismML Ternary-Bonsai: ternary
+    weights, 128 in 28 bytes, a Hadamard-rotated activation): scipy's Sylvester
+    Hadamard matrix with exactly rounded sums (math.fsum), the rotation's closed forms
+    (one-hot and constant blocks, the rotation being its own inverse, norm kept), and
+    its stated purpose (an outlier spread over the block quantizes with less error).
 """
 from __future__ import annotations
 
@@ -36,9 +42,9 @@ def np_bf16(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def np_quantize(x):
+def np_quantize(x, block=QB):
     """Independent quantizer: numpy f32 division and np.rint (round half to even)."""
-    xb = np.asarray(x, dtype=np.float32).reshape(-1, QB)
+    xb = np.asarray(x, dtype=np.float32).reshape(-1, block)
     amax = np.abs(xb).max(axis=1)
     d = (amax / np.float32(127)).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -595,6 +601,166 @@ def pin_threads_match_single(o):
     for t in (3, 64):
         yt, St = o.f16_gemv(wf, xf, nthreads=t)
         assert np.array_equal(yt, y) and np.array_equal(St, S)
+
+
+# ----------------------------------------------------------------------------- PTQ1_0
+
+PB = 128  # weights per PTQ1_0 block
+
+
+def np_hadamard_rotate(x):
+    """H x / sqrt(128) per block with scipy's Sylvester matrix and exactly rounded sums."""
+    import math
+
+    from scipy.linalg import hadamard
+
+    H = hadamard(PB)
+    xb = np.asarray(x, dtype=np.float32).reshape(-1, PB).astype(np.float64)
+    out = np.empty(xb.shape, np.float32)
+    for b in range(xb.shape[0]):
+        for i in range(PB):
+            out[b, i] = np.float32(math.fsum(H[i] * xb[b]) / math.sqrt(PB))
+    return out.ravel()
+
+
+def _ptq1_case(j, n, k, resid=True):
+    g = rng(j)
+    w, t, sb = synth.ptq1_weights(g, n, k)
+    x = synth.activation_f32(g, k)
+    r = synth.residual_f32(g, n) if resid else None
+    return w, t, sb, x, r
+
+
+def pin_ptq1_decode_vs_encoder(o):
+    w, t, sb, _, _ = _ptq1_case(40, 9, 512)
+    tt, ss = o.ptq1_decode(w)
+    assert np.array_equal(tt, t) and np.array_equal(ss, sb)
+    # single bytes: base-3 digits, least significant first, digit = trit + 1
+    blk = np.zeros((1, 28), np.uint8)
+    for byte, want in ((0, [-1] * 5), (242, [1] * 5), (121, [0] * 5), (1, [0, -1, -1, -1, -1]),
+                       (3, [-1, 0, -1, -1, -1]), (81 * 2, [-1, -1, -1, -1, 1])):
+        blk[0, 7] = byte
+        tt, _ = o.ptq1_decode(blk)
+        assert list(tt[0, 35:40]) == want, (byte, list(tt[0, 35:40]))
+    # the last byte holds weights 125..127; scale bits little-endian after the trits
+    blk[0, 25], blk[0, 26], blk[0, 27] = 2 + 0 * 3 + 1 * 9, 0x34, 0x12
+    tt, ss = o.ptq1_decode(blk)
+    assert list(tt[0, 125:128]) == [1, -1, 0] and ss[0, 0] == 0x1234
+
+
+def pin_hadamard_closed_forms(o):
+    inv = np.float32(1.0 / np.sqrt(np.float64(PB)))
+    for k in (0, 1, 37, 127):
+        e = np.zeros(PB, np.float32)
+        e[k] = 1.0
+        h = o.hadamard128(e)
+        signs = np.array([(-1) ** bin(i & k).count("1") for i in range(PB)], np.float32)
+        assert np.array_equal(h, signs * inv), f"one-hot {k}"
+    c = np.full(PB, 0.75, np.float32)
+    h = o.hadamard128(c)
+    assert h[0] == np.float32(128 * 0.75 / np.sqrt(128.0)) and np.all(h[1:] == 0)
+    g = rng(41)
+    x = g.standard_normal(4 * PB).astype(np.float32)
+    y = o.hadamard128(x)
+    # a rotation: norms kept; H / sqrt(128) is symmetric and orthogonal, so applying it twice
+    # returns the input (up to the f32 roundings)
+    for b in range(4):
+        xb, yb = x[b * PB:(b + 1) * PB].astype(np.float64), y[b * PB:(b + 1) * PB].astype(np.float64)
+        assert abs(np.linalg.norm(yb) - np.linalg.norm(xb)) <= 1e-6 * np.linalg.norm(xb)
+    back = o.hadamard128(y)
+    assert np.max(np.abs(back.astype(np.float64) - x)) <= 1e-5 * np.max(np.abs(x))
+    # blocks are rotated independently
+    z = x.copy()
+    z[PB:] = 0
+    assert np.array_equal(o.hadamard128(z)[:PB], y[:PB])
+
+
+def pin_hadamard_vs_scipy(o):
+    g = rng(42)
+    x = np.concatenate([g.standard_normal(6 * PB), g.standard_normal(2 * PB) * 1e-3]).astype(np.float32)
+    ours = o.hadamard128(x)
+    ref = np_hadamard_rotate(x)
+    assert np.array_equal(ours, ref), f"{np.count_nonzero(ours != ref)} mismatches"
+
+
+def pin_ptq1_activation_quantizer(o):
+    g = rng(43)
+    x = np.concatenate([g.standard_normal(8 * PB), g.standard_normal(PB) * 1e-6, np.zeros(PB)]).astype(np.float32)
+    rot, q, d = o.ptq1_activation(x)
+    assert np.array_equal(rot, o.hadamard128(x))
+    rq, rd = np_quantize(rot, PB)
+    assert np.array_equal(q, rq) and np.array_equal(d, rd)
+    assert np.all(q[-PB:] == 0) and d[-1] == 0
+
+
+def pin_ptq1_rotation_spreads_outlier(o):
+    """[P] §PrismML Ternary-Bonsai: the rotation spreads an outlier over the whole block, so
+    quantization loses less. One 128-value block with a single large value: quantized
+    directly, the small values fall below one code step; rotated, quantized, dequantized and
+    rotated back, they survive."""
+    g = rng(44)
+    x = g.standard_normal(PB).astype(np.float32)
+    x[17] = 100.0
+    q, d = o.quantize_blocks(x, PB)
+    direct = q.astype(np.float64) * np_f16(d)[0]
+    rot, qr, dr = o.ptq1_activation(x)
+    back = o.hadamard128((qr.astype(np.float64) * np_f16(dr)[0]).astype(np.float32)).astype(np.float64)
+    keep = np.arange(PB) != 17
+    err_direct = np.sqrt(np.mean((direct[keep] - x[keep]) ** 2))
+    err_rot = np.sqrt(np.mean((back[keep] - x[keep]) ** 2))
+    assert err_rot < err_direct / 4, (err_rot, err_direct)
+
+
+def pin_ptq1_exact_rational(o):
+    w, t, sb, x, r = _ptq1_case(45, 3, 256)
+    _, qx, dx = o.ptq1_activation(x)
+    y, S = o.ptq1_gemv(w, qx, dx, r)
+    for row in range(3):
+        ex = Fraction(0)
+        for b in range(2):
+            isum = sum(int(t[row, PB * b + i]) * int(qx[PB * b + i]) for i in range(PB))
+            ex += isum * Fraction(float(np_f16(sb[row, b]))) * Fraction(float(np_f16(dx[b])))
+        ex += Fraction(float(r[row]))
+        assert abs(Fraction(y[row]) - ex) <= Fraction(4 * 2.0**-53) * Fraction(S[row])
+
+
+def pin_ptq1_vs_dense_dequant(o):
+    for j, (n, k) in enumerate(((40, 1024), (9, 3584), (5, 5120))):
+        w, t, sb, x, r = _ptq1_case(46 + j, n, k)
+        _, qx, dx = o.ptq1_activation(x)
+        y, S = o.ptq1_gemv(w, qx, dx, r)
+        W = t.astype(np.float64) * np.repeat(np_f16(sb), PB, axis=1)
+        xd = qx.astype(np.float64) * np.repeat(np_f16(dx), PB)
+        close_to(y, W @ xd + r.astype(np.float64), S, 1e-13)
+
+
+def pin_ptq1_closed_forms(o):
+    n, k = 4, 512
+    g = rng(49)
+    qx = g.integers(-127, 128, k).astype(np.int8)
+    one = np.full(k // PB, 0x3C00, np.uint16)  # binary16 1.0
+    r = synth.residual_f32(g, n)
+    zero = synth.ptq1_pack(np.zeros((n, k), np.int8), np.tile(one, (n, 1)))
+    y, S = o.ptq1_gemv(zero, qx, one, r)
+    assert np.array_equal(y, r.astype(np.float64))  # zero trits give the residual
+    ones = synth.ptq1_pack(np.ones((n, k), np.int8), np.tile(one, (n, 1)))
+    y, _ = o.ptq1_gemv(ones, qx, one)
+    assert np.all(y == float(qx.astype(np.int64).sum()))  # all +1 at unit scales: the sum of the codes
+    w, t, sb, x, _ = _ptq1_case(50, n, k, resid=False)
+    _, qx, dx = o.ptq1_activation(x)
+    y, _ = o.ptq1_gemv(w, qx, dx)
+    yn, _ = o.ptq1_gemv(synth.ptq1_pack(-t, sb), qx, dx)
+    assert np.array_equal(yn, -y)  # negated trits negate the output exactly
+    y2, _ = o.ptq1_gemv(w, qx, (np_f16(dx) * 2).astype(np.float16).view(np.uint16))
+    assert np.array_equal(y2, 2 * y)  # doubling every activation scale doubles the output
+
+
+def pin_ptq1_threads_match_single(o):
+    w, _, _, x, r = _ptq1_case(51, 333, 1024)
+    _, qx, dx = o.ptq1_activation(x)
+    y1, s1 = o.ptq1_gemv(w, qx, dx, r)
+    y4, s4 = o.ptq1_gemv(w, qx, dx, r, nthreads=4)
+    assert np.array_equal(y1, y4) and np.array_equal(s1, s4)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

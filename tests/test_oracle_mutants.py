@@ -32,13 +32,17 @@ MUTANTS = [
     ("quant_zero_block_scale", "dx[b] = 0;\n            continue;", "dx[b] = 0x3c00;\n            continue;"),
     ("quant_amax_signed", "float a = fabsf(xb[i]);", "float a = xb[i];"),
     ("isum_wrong_x_index", "(int32_t)qx[b * ORC_QBLOCK + i];\n            isum", "(int32_t)qx[i];\n            isum"),
-    ("gemv_wrong_dx_index", "orc_f16_value(dx[b]);", "orc_f16_value(dx[0]);"),
+    ("gemv_wrong_dx_index", "orc_f16_value(dw[n * nb + b]) * orc_f16_value(dx[b]);",
+     "orc_f16_value(dw[n * nb + b]) * orc_f16_value(dx[0]);"),
     ("gemv_reversed_dw", "orc_f16_value(dw[n * nb + b])", "orc_f16_value(dw[n * nb + (nb - 1 - b)])"),
     ("gemv_unsigned_weights", "int32_t p = (int32_t)qw[n * K + b * ORC_QBLOCK + i]",
      "int32_t p = (int32_t)(uint8_t)qw[n * K + b * ORC_QBLOCK + i]"),
     ("gemv_residual_sign", "acc += (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- bf16",
      "acc -= (double)residual[n];\n            mag += fabs((double)residual[n]);\n        }\n        y[n] = acc;\n        S[n] = mag;\n    }\n}\n\n/* ---- bf16"),
-    ("gemv_magnitude_signed", "sa += p < 0 ? -p : p;", "sa += p;"),
+    ("gemv_magnitude_signed", "* (int32_t)qx[b * ORC_QBLOCK + i];\n                s += p;\n                sa += p < 0 ? -p : p;",
+     "* (int32_t)qx[b * ORC_QBLOCK + i];\n                s += p;\n                sa += p;"),
+    ("ptq1_magnitude_signed", "* (int32_t)qx[b * ORC_PTQ1_BLOCK + i];\n                s += p;\n                sa += p < 0 ? -p : p;",
+     "* (int32_t)qx[b * ORC_PTQ1_BLOCK + i];\n                s += p;\n                sa += p;"),
     ("gemv_dropped_last_block", "for (int64_t b = 0; b < nb; ++b) {\n            int32_t s = 0, sa = 0;",
      "for (int64_t b = 0; b < nb - 1; ++b) {\n            int32_t s = 0, sa = 0;"),
     ("bf16_wrong_x_index", "orc_bf16_value(x[k]);", "orc_bf16_value(x[0]);"),
@@ -61,6 +65,23 @@ MUTANTS = [
     ("threads_f16_as_bf16", "orc_job p = {2, w, NULL, x, NULL, residual, 0, 0, K, y, S};",
      "orc_job p = {1, w, NULL, x, NULL, residual, 0, 0, K, y, S};"),
     ("threads_drop_row", "jobs[t].n1 = N * (t + 1) / nthreads;", "jobs[t].n1 = N * (t + 1) / nthreads - (t == 0);"),
+    # PTQ1_0: packing, scale, rotation
+    ("ptq1_digit_msb_first", "for (int k = 0; k < i % 5; ++k)", "for (int k = 0; k < 4 - i % 5; ++k)"),
+    ("ptq1_trit_offset", "return v % 3 - 1;", "return v % 3;"),
+    ("ptq1_six_per_byte", "int v = blk[i / 5];", "int v = blk[i / 6];"),
+    ("ptq1_block_stride_26", "const uint8_t *blk = w + (n * nb + b) * ORC_PTQ1_BYTES;",
+     "const uint8_t *blk = w + (n * nb + b) * ORC_PTQ1_TRIT_BYTES;"),
+    ("ptq1_scale_ignored", "double scale = orc_f16_value(orc_ptq1_scale(blk)) * orc_f16_value(dx[b]);",
+     "double scale = orc_f16_value(dx[b]);"),
+    ("ptq1_scale_big_endian", "return (uint16_t)(blk[ORC_PTQ1_TRIT_BYTES] | (blk[ORC_PTQ1_TRIT_BYTES + 1] << 8));",
+     "return (uint16_t)(blk[ORC_PTQ1_TRIT_BYTES + 1] | (blk[ORC_PTQ1_TRIT_BYTES] << 8));"),
+    ("hadamard_sign_or", "acc += orc_parity((unsigned)(i & j)) ? -v : v;", "acc += orc_parity((unsigned)(i | j)) ? -v : v;"),
+    ("hadamard_unnormalized", "out[b * ORC_PTQ1_BLOCK + i] = (float)(acc / norm);", "out[b * ORC_PTQ1_BLOCK + i] = (float)acc;"),
+    ("hadamard_norm_128", "const double norm = sqrt((double)ORC_PTQ1_BLOCK);", "const double norm = (double)ORC_PTQ1_BLOCK;"),
+    ("hadamard_f32_sum", "double acc = 0.0;\n            for (int j = 0; j < ORC_PTQ1_BLOCK; ++j) {",
+     "float acc = 0.0f;\n            for (int j = 0; j < ORC_PTQ1_BLOCK; ++j) {"),
+    ("ptq1_no_rotation", "    orc_hadamard128(x, K, rot);\n    orc_quantize_blocks(rot, K, ORC_PTQ1_BLOCK, qx, dx);",
+     "    for (int64_t i = 0; i < K; ++i)\n        rot[i] = x[i];\n    orc_quantize_blocks(rot, K, ORC_PTQ1_BLOCK, qx, dx);"),
 ]
 
 
