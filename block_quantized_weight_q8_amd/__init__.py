@@ -10,6 +10,9 @@ Storage conventions (as in the C header):
     torch.int16 or torch.uint16 tensors are all accepted as 16-bit storage);
   * quantized activation: codes int8 [K], scales binary16 bits [K/32];
   * bf16 weights / activation: torch.bfloat16 (or 16-bit integer storage of the bits);
+  * PTQ1_0 weights: uint8 [N, K/128 * 28] (28-byte blocks of 128 ternary weights); their
+    activation is the rotated codes int8 [K] with binary16 scales [K/128] of
+    ptq1_rotate_quantize_act;
   * outputs and residuals: torch.float32.
 """
 from __future__ import annotations
@@ -26,6 +29,10 @@ Q8G_Q8_0 = 0
 Q8G_BF16 = 1
 Q8G_Q8_0_F32 = 2
 Q8G_F16 = 3
+Q8G_PTQ1_0 = 4
+PTQ1_BLOCK = 128
+PTQ1_BYTES = 28
+PTQ1_MAX_K = 131072
 FUSED_MAX_K = 16384
 MAX_PARTS = 4
 BATCH_MAX = 16
@@ -105,6 +112,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8_gateup_rmsnorm_silu_quantize.argtypes = [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_float, _I64, _P, _P, _P]
     lib.q8_gateup_silu.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P]
     lib.q8_gateup_rmsnorm_silu.argtypes = [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_float, _I64, _P, _P]
+    lib.ptq1_rotate_quantize_act.argtypes = [_P, _P, _P, _P, _I64, _P]
+    lib.ptq1_gemv.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
     lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
@@ -119,7 +128,8 @@ def load_library(path: str = LIB_PATH):
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
                "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
                "q8_gateup_silu", "q8_gateup_rmsnorm_silu",
-               "q8_rmsnorm_quantize_act_batch", "q8_silu_mul_quantize_act_batch"):
+               "q8_rmsnorm_quantize_act_batch", "q8_silu_mul_quantize_act_batch",
+               "ptq1_rotate_quantize_act", "ptq1_gemv"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -174,6 +184,7 @@ _I8 = (torch.int8,)
 _H16 = (torch.float16, torch.int16, torch.uint16)
 _B16 = (torch.bfloat16, torch.int16, torch.uint16)
 _F32 = (torch.float32,)
+_U8 = (torch.uint8,)
 
 
 def q8_quantize_act(x, qx=None, dx=None, stream=None):
@@ -314,18 +325,56 @@ def f16_gemv(w, x, y=None, residual=None, stream=None):
     return y
 
 
+def ptq1_rotate_quantize_act(x, qx=None, dx=None, rot=None, stream=None):
+    """Rotate f32 x [K] per 128-value block by the normalized Hadamard matrix and quantize
+    the result per 128 values: returns (qx int8 [K], dx binary16 [K/128]). rot (f32 [K]),
+    if given, receives the rotated values."""
+    k = x.shape[0] if x.dim() == 1 else -1
+    if k < 0 or k % PTQ1_BLOCK:
+        raise ValueError("x must be 1-D with a length that is a multiple of 128")
+    if qx is None:
+        qx = torch.empty(k, dtype=torch.int8, device=x.device)
+    if dx is None:
+        dx = torch.empty(k // PTQ1_BLOCK, dtype=torch.float16, device=x.device)
+    st = load_library().ptq1_rotate_quantize_act(
+        _ptr(x, "x", _F32), _ptr(rot, "rot", _F32, (k,), optional=True), _ptr(qx, "qx", _I8, (k,)),
+        _ptr(dx, "dx", _H16, (k // PTQ1_BLOCK,)), k, _stream(stream))
+    _check("ptq1_rotate_quantize_act", st)
+    return qx, dx
+
+
+def ptq1_gemv(w, qx, dx, y=None, residual=None, stream=None):
+    """y = PTQ1_0(w) · (qx, dx) (+ residual). w uint8 [N, K/128 * 28]; qx int8 [K] and dx
+    binary16 [K/128] from ptq1_rotate_quantize_act. Returns y (f32 [N])."""
+    if w.dim() != 2 or w.shape[1] % PTQ1_BYTES:
+        raise ValueError("w must be [N, K/128 * 28]")
+    n = w.shape[0]
+    k = w.shape[1] // PTQ1_BYTES * PTQ1_BLOCK
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w.device)
+    st = load_library().ptq1_gemv(
+        _ptr(w, "w", _U8), _ptr(qx, "qx", _I8, (k,)), _ptr(dx, "dx", _H16, (k // PTQ1_BLOCK,)),
+        _ptr(residual, "residual", _F32, (n,), optional=True), _ptr(y, "y", _F32, (n,)), n, k, _stream(stream))
+    _check("ptq1_gemv", st)
+    return y
+
+
 def gemv_stacked(parts, x, dx=None, stream=None):
     """One launch over 1..4 matrices sharing the input.
 
-    parts: sequence of dicts with keys w (int8 [n, K] for Q8_0, bf16 [n, K]), dw (Q8_0
-    scales, omitted for bf16), y (f32 [n], allocated if absent), residual (optional).
+    parts: sequence of dicts with keys w (int8 [n, K] for Q8_0, bf16 [n, K], uint8
+    [n, K/128 * 28] for PTQ1_0), dw (Q8_0 scales, omitted otherwise), y (f32 [n], allocated
+    if absent), residual (optional).
     x: int8 codes [K] with dx binary16 scales [K/32] (Q8_0); or f32 [K] for Q8_0 weights
     (quantized inside the launch, dx None); or bf16 [K] / float16 [K] for bf16 / float16
-    weights (dx None). The weight dtype selects the kind.
+    weights (dx None); or the rotated codes int8 [K] with dx binary16 [K/128] (PTQ1_0).
+    The weight dtype selects the kind.
     Returns the list of outputs.
     """
     if not 1 <= len(parts) <= MAX_PARTS:
         raise ValueError("1 to 4 parts")
+    if parts[0]["w"].dtype == torch.uint8:
+        return _ptq1_stacked(parts, x, dx, stream)
     q8 = parts[0]["w"].dtype == torch.int8
     f16 = parts[0]["w"].dtype == torch.float16
     fused = q8 and x.dtype == torch.float32
@@ -350,6 +399,33 @@ def gemv_stacked(parts, x, dx=None, stream=None):
     pdx = _ptr(dx, "dx", _H16, (k // 32,)) if (q8 and not fused) else None
     dt = Q8G_Q8_0_F32 if fused else (Q8G_Q8_0 if q8 else (Q8G_F16 if f16 else Q8G_BF16))
     st = load_library().gemv_stacked(dt, arr, len(parts), px, pdx, k, _stream(stream))
+    _check("gemv_stacked", st)
+    return outs
+
+
+def _ptq1_stacked(parts, qx, dx, stream):
+    k = qx.shape[0]
+    if k % PTQ1_BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    row = k // PTQ1_BLOCK * PTQ1_BYTES
+    arr = (_Part * len(parts))()
+    outs = []
+    for i, p in enumerate(parts):
+        w = p["w"]
+        if w.dim() != 2 or w.shape[1] != row:
+            raise ValueError(f"part {i}: w must be [n, {row}]")
+        n = w.shape[0]
+        y = p.get("y")
+        if y is None:
+            y = torch.empty(n, dtype=torch.float32, device=w.device)
+        outs.append(y)
+        arr[i].w = _ptr(w, f"parts[{i}].w", _U8)
+        arr[i].dw = None
+        arr[i].n = n
+        arr[i].y = _ptr(y, f"parts[{i}].y", _F32, (n,))
+        arr[i].residual = _ptr(p.get("residual"), f"parts[{i}].residual", _F32, (n,), optional=True)
+    st = load_library().gemv_stacked(Q8G_PTQ1_0, arr, len(parts), _ptr(qx, "x", _I8, (k,)),
+                                     _ptr(dx, "dx", _H16, (k // PTQ1_BLOCK,)), k, _stream(stream))
     _check("gemv_stacked", st)
     return outs
 

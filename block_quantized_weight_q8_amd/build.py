@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq8gemv.so")
-SOURCES = ["q8gemv.hip", "batch.hip", "stack.hip", "probe.hip"]
+SOURCES = ["q8gemv.hip", "batch.hip", "stack.hip", "ptq1.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

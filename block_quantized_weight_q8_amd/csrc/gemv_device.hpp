@@ -247,4 +247,17 @@ __device__ __forceinline__ uint32_t quantize4(const float4 &v, float *d_out)
 
 __device__ __forceinline__ uint16_t scale_bits(float d) { return d != 0.0f ? f32_to_f16_bits(d) : (uint16_t)0; }
 
+// A barrier among the workgroup's waves that waits only for this wave's own LDS
+// operations, not for its global loads in flight: gfx950 puts no wait in front of
+// a bare s_barrier, and __syncthreads (a fence) would also wait for the weights a
+// wave has requested ahead of use. The empty asm statements keep the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace q8g

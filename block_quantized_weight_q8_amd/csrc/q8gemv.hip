@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include "gemv_device.hpp"
+#include "ptq1.hpp"
 #include "q8gemv.h"
 
 namespace {
@@ -985,6 +986,7 @@ q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual,
 q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, const void *x, const uint16_t *dx,
                         int64_t K, void *stream)
 {
+    if (dtype == Q8G_PTQ1_0) return q8g::ptq1_stacked(parts, nparts, static_cast<const int8_t *>(x), dx, K, stream);
     if (dtype != Q8G_Q8_0 && dtype != Q8G_BF16 && dtype != Q8G_Q8_0_F32 && dtype != Q8G_F16) return Q8G_ERR_ARG;
     return run(dtype, parts, nparts, x, dx, K, stream);
 }
@@ -1095,6 +1097,10 @@ q8g_status q8_gateup_rmsnorm_silu(const int8_t *qw_gate, const uint16_t *dw_gate
 
 q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows, int *waves)
 {
+    if (dtype == Q8G_PTQ1_0) {
+        if (!rows || !waves) return Q8G_ERR_NULL;
+        return q8g::ptq1_config(n_total, K, rows, waves);
+    }
     if (dtype != Q8G_Q8_0 && dtype != Q8G_BF16 && dtype != Q8G_Q8_0_F32 && dtype != Q8G_F16) return Q8G_ERR_ARG;
     if (n_total < 0 || K < 0) return Q8G_ERR_SHAPE;
     if (!rows || !waves) return Q8G_ERR_NULL;

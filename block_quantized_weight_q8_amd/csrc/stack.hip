@@ -162,19 +162,6 @@ __device__ __forceinline__ void wait_loads(u32x4 (&v)[N])
     for (int k = 0; k < N; ++k) asm volatile("" : "+v"(v[k]));
 }
 
-// A barrier among the workgroup's waves that waits only for this wave's own LDS
-// operations, not for its global loads in flight: gfx950 puts no wait in front of
-// a bare s_barrier, and __syncthreads (a fence) would also wait for the weights a
-// compute wave has requested for the next op. The empty asm statements keep the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // What a workgroup keeps of an op besides its descriptor: the row ends of the
 // parts and its own slice of rows, worked out once per launch (64-bit divisions
 // are long instruction sequences).

@@ -14,6 +14,11 @@
  *       16-byte chunks of eight bf16; the last row index guards the tail) and
  *       "The numerical contract" (bf16 weights and activations, f32
  *       accumulators).
+ *   [T] "Filling in the blanks: Inference using Phobos", section "PrismML
+ *       Ternary-Bonsai": ternary weights (-1, 0, +1), 128 of them in 28 bytes
+ *       (PTQ1_0), with the activation rotated by a Hadamard transform, which
+ *       spreads outliers over the block; the rotated activation is computed
+ *       once and shared by every projection that reads the same input.
  *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE pointers owned by the caller. The one exception
@@ -62,7 +67,9 @@ typedef enum {
 /* Q8G_Q8_0_F32: Q8_0 weights with an f32 activation that the launch itself
  * quantizes (exactly as q8_quantize_act) before the dot products; K <= 16384. */
 /* Q8G_F16: IEEE binary16 weights and activation, f32 accumulation. */
-typedef enum { Q8G_Q8_0 = 0, Q8G_BF16 = 1, Q8G_Q8_0_F32 = 2, Q8G_F16 = 3 } q8g_dtype;
+/* Q8G_PTQ1_0: PTQ1_0 ternary weights against a rotated, quantized activation
+ * (see the PTQ1_0 section below). */
+typedef enum { Q8G_Q8_0 = 0, Q8G_BF16 = 1, Q8G_Q8_0_F32 = 2, Q8G_F16 = 3, Q8G_PTQ1_0 = 4 } q8g_dtype;
 
 /* Quantize an activation once into the Q8_0 block format ([P] Fast Decode).
  * For each block b of 32 consecutive values of x (f32 [K]):
@@ -122,8 +129,9 @@ q8g_status q8g_batch_config(int64_t N, int *k_split, int *steps_in_flight);
 
 /* One matrix of a stacked projection. */
 typedef struct {
-    const void *w;         /* Q8_0: int8 codes [n][K]; bf16 / f16: uint16 [n][K] */
-    const uint16_t *dw;    /* Q8_0: binary16 scale bits [n][K/32]; bf16 / f16: ignored (may be NULL) */
+    const void *w;         /* Q8_0: int8 codes [n][K]; bf16 / f16: uint16 [n][K];
+                              PTQ1_0: blocks uint8 [n][K/128 * 28] */
+    const uint16_t *dw;    /* Q8_0: binary16 scale bits [n][K/32]; other kinds: ignored (may be NULL) */
     int64_t n;             /* output rows of this part (>= 0) */
     float *y;              /* f32 [n] */
     const float *residual; /* f32 [n] or NULL; may equal y */
@@ -137,11 +145,56 @@ typedef struct {
  * Q8G_Q8_0_F32 takes x = f32 [K] (16-byte aligned, K <= 16384), quantizes it
  * inside the launch, and ignores dx ([P] Fast Decode: quantize the activation
  * once and share it, here once per launch for all of its parts).
- * Part p's result is identical, bit for bit, to q8_gemv / bf16_gemv called on
- * that part alone (for Q8G_Q8_0_F32: to q8_quantize_act then q8_gemv).
- * 1 <= nparts <= 4. */
+ * Q8G_PTQ1_0 takes x = the rotated codes int8 [K] and dx = binary16 scale
+ * bits [K/128] of ptq1_rotate_quantize_act ([T]: the rotated activation shared
+ * by the projections that read it), with the rules of ptq1_gemv.
+ * Part p's result is identical, bit for bit, to q8_gemv / bf16_gemv /
+ * ptq1_gemv called on that part alone (for Q8G_Q8_0_F32: to q8_quantize_act
+ * then q8_gemv). 1 <= nparts <= 4. */
 q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, const void *x,
                         const uint16_t *dx, int64_t K, void *stream);
+
+/* ---- PTQ1_0 ternary weights ([T]) ----------------------------------------
+ * The pages fix the weight values (-1, 0, +1), the block size (128 weights in
+ * 28 bytes) and the rotation of the activation by a Hadamard transform; the
+ * layout below is this library's reading of the rest.
+ * Block (28 bytes, 128 weights):
+ *   bytes 0..25  base-3 digits, five per byte, least significant digit first:
+ *                weight i (0..127) is digit (i mod 5) of byte floor(i / 5), and
+ *                its trit is digit - 1 (byte 25 holds weights 125..127; its
+ *                digits 3 and 4 belong to no weight and are ignored);
+ *   bytes 26..27 the block scale s, IEEE binary16 bits, little-endian;
+ *   weight i of the block = s * trit_i.
+ * A row of K weights (K % 128 == 0) is K/128 blocks back to back, rows
+ * contiguous: w uint8 [N][K/128 * 28]. */
+#define Q8G_PTQ1_BLOCK 128
+#define Q8G_PTQ1_BYTES 28
+#define Q8G_PTQ1_MAX_K 131072
+#define Q8G_PTQ1_MAX_ROWS (1 << 30)
+
+/* Rotate an activation and quantize it for PTQ1_0 weights ([T]: computed once
+ * per input). For each block b of 128 consecutive values of x (f32 [K]):
+ *   r_i = fl32( (sum_{j<128} (-1)^popcount(i & j) * x_{128b+j}) / sqrt(128) )
+ *         (the sum in f64 in ascending j, sqrt(128) the nearest f64, the
+ *         quotient correctly rounded in f64, then rounded once to f32),
+ *   then the 128 values r are quantized as q8_quantize_act quantizes a block,
+ *   over 128 values instead of 32: d = fl32(max |r| / 127), q_i = rint(fl32(r_i / d)),
+ *   dx[b] = binary16(d); d == 0 gives codes 0 and scale bits 0.
+ * x f32 [K] (4-byte aligned); rot f32 [K] (4-byte aligned) or NULL: the values r;
+ * qx int8 [K]; dx uint16 [K/128]. K % 128 == 0 (K == 0: nothing is enqueued).
+ * No output may overlap x or another output. */
+q8g_status ptq1_rotate_quantize_act(const float *x, float *rot, int8_t *qx, uint16_t *dx, int64_t K, void *stream);
+
+/* PTQ1_0 GEMV ([T]):
+ *   isum[n][b] = sum_{i<128} trit(n, b, i) * qx[128b+i]            (exact int32, |isum| <= 16256)
+ *   y[n] = sum_b float(isum[n][b]) * (f16(s[n][b]) * f16(dx[b]))   (f32 accumulate)
+ *          (+ residual[n], added once after the dot; residual may be NULL)
+ * w uint8 [N][K/128 * 28] (4-byte aligned); qx int8 [K] (16-byte aligned) and
+ * dx uint16 [K/128] from ptq1_rotate_quantize_act; residual f32 [N] or NULL
+ * (may equal y); y f32 [N]. K % 128 == 0, K <= Q8G_PTQ1_MAX_K,
+ * N <= Q8G_PTQ1_MAX_ROWS. K == 0 gives y = residual (or 0). */
+q8g_status ptq1_gemv(const uint8_t *w, const int8_t *qx, const uint16_t *dx, const float *residual, float *y,
+                     int64_t N, int64_t K, void *stream);
 
 /* ---- neighbour steps folded into the projection --------------------------
  * [H] Emitting for a GPU: at decode the normalization runs fused with the
@@ -315,8 +368,8 @@ q8g_status q8_decode_stack_static(const q8g_stack_op *ops, const q8g_stack_op *o
                                   void *stream);
 
 /* Launch configuration the library picks for a GEMV over n_total rows of K
- * (all parts of a stacked call together): output rows per wave and waves per
- * workgroup. Pure host query; nothing is enqueued. Lets a profiler's per-kernel
+ * (all parts of a stacked call together): output rows per wave (for
+ * Q8G_PTQ1_0: rows per wave step) and waves per workgroup. Pure host query; nothing is enqueued. Lets a profiler's per-kernel
  * statistics be matched to the calls that produced them. */
 q8g_status q8g_gemv_config(q8g_dtype dtype, int64_t n_total, int64_t K, int *rows_per_wave,
                            int *waves_per_group);

@@ -57,6 +57,9 @@ def lib():
     L.q8g_status_str.restype = ctypes.c_char_p
     L.q8g_probe_read.argtypes = [P, I64, P, P]
     L.q8g_flush.argtypes = [P, I64, ctypes.c_uint32, P]
+    L.ptq1_rotate_quantize_act.argtypes = [P, P, P, P, I64, P]
+    L.ptq1_gemv.argtypes = [P, P, P, P, P, I64, I64, P]
+    L.q8g_gemv_config.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     return L
 
 
@@ -67,7 +70,8 @@ def test_every_declared_symbol_is_exported(lib):
                      "gemv_stacked_rmsnorm", "q8_gemv_silu_mul", "q8_gateup_silu_quantize",
                      "q8_gateup_rmsnorm_silu_quantize", "q8_gateup_silu", "q8_gateup_rmsnorm_silu",
                      "q8_rmsnorm_quantize_act_batch",
-                     "q8_silu_mul_quantize_act_batch", "q8g_probe_read", "q8g_flush"):
+                     "q8_silu_mul_quantize_act_batch", "q8g_probe_read", "q8g_flush",
+                     "ptq1_rotate_quantize_act", "ptq1_gemv"):
         assert expected in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -175,7 +179,7 @@ def test_stacked_validation(lib):
     assert s(0, one, 0, QX, DX, 64, None) == ERR_ARG
     assert s(0, one, 5, QX, DX, 64, None) == ERR_ARG
     assert s(7, one, 1, QX, DX, 64, None) == ERR_ARG
-    assert s(4, one, 1, QX, DX, 64, None) == ERR_ARG  # one past the last kind
+    assert s(5, one, 1, QX, DX, 64, None) == ERR_ARG  # one past the last kind
     assert s(3, parts((W, None, 8, Y, None)), 1, X, None, 20, None) == ERR_SHAPE  # f16: K % 8
     assert s(3, parts((W + 2, None, 8, Y, None)), 1, X, None, 64, None) == ERR_ALIGN
     assert s(0, None, 1, QX, DX, 64, None) == ERR_NULL
@@ -193,6 +197,64 @@ def test_stacked_validation(lib):
     assert s(0, two, 2, QX, DX, 64, None) == ERR_OVERLAP
     # all parts empty: nothing to do
     assert s(1, parts((None, None, 0, None, None), (None, None, 0, None, None)), 2, None, None, 16, None) == OK
+
+
+def test_ptq1_rotate_validation(lib):
+    q = lib.ptq1_rotate_quantize_act
+    assert q(X, None, QX, DX, 96, None) == ERR_SHAPE  # K % 128
+    assert q(X, None, QX, DX, -128, None) == ERR_SHAPE
+    assert q(None, None, None, None, 0, None) == OK  # empty: nothing enqueued
+    assert q(None, None, QX, DX, 128, None) == ERR_NULL
+    assert q(X, None, None, DX, 128, None) == ERR_NULL
+    assert q(X, None, QX, None, 128, None) == ERR_NULL
+    assert q(X + 2, None, QX, DX, 128, None) == ERR_ALIGN
+    assert q(X, R + 2, QX, DX, 128, None) == ERR_ALIGN
+    assert q(X, None, QX, DX + 1, 128, None) == ERR_ALIGN
+    assert q(X, None, X + 64, DX, 256, None) == ERR_OVERLAP  # codes inside x
+    assert q(X, None, QX, QX + 32, 256, None) == ERR_OVERLAP  # scales inside codes
+    assert q(X, X + 512, QX, DX, 256, None) == ERR_OVERLAP  # rotated values over x
+    assert q(X, QX - 512, QX, DX, 256, None) == ERR_OVERLAP  # rotated values over the codes
+
+
+def test_ptq1_gemv_validation(lib):
+    g = lib.ptq1_gemv
+    assert g(W, QX, DX, None, Y, 8, 96, None) == ERR_SHAPE  # K % 128
+    assert g(W, QX, DX, None, Y, 8, 131072 + 128, None) == ERR_SHAPE  # K > Q8G_PTQ1_MAX_K
+    assert g(W, QX, DX, None, Y, -1, 128, None) == ERR_SHAPE
+    assert g(W, QX, DX, None, Y, (1 << 30) + 1, 128, None) == ERR_SHAPE  # N > Q8G_PTQ1_MAX_ROWS
+    assert g(None, None, None, None, None, 0, 128, None) == OK  # N == 0
+    assert g(None, QX, DX, None, Y, 8, 128, None) == ERR_NULL
+    assert g(W, None, DX, None, Y, 8, 128, None) == ERR_NULL
+    assert g(W, QX, None, None, Y, 8, 128, None) == ERR_NULL
+    assert g(W, QX, DX, None, None, 8, 128, None) == ERR_NULL
+    assert g(W + 2, QX, DX, None, Y, 8, 128, None) == ERR_ALIGN  # blocks are read as dwords
+    assert g(W, QX + 8, DX, None, Y, 8, 128, None) == ERR_ALIGN
+    assert g(W, QX, DX + 1, None, Y, 8, 128, None) == ERR_ALIGN
+    assert g(W, QX, DX, R + 2, Y, 8, 128, None) == ERR_ALIGN
+    assert g(W, QX, DX, None, Y + 2, 8, 128, None) == ERR_ALIGN
+    assert g(W, QX, DX, None, W + 8 * 28 - 4, 8, 128, None) == ERR_OVERLAP  # y over the last block
+    assert g(W, QX, DX, None, QX, 8, 128, None) == ERR_OVERLAP
+    assert g(W, QX, DX, None, DX, 8, 128, None) == ERR_OVERLAP
+    assert g(W, QX, DX, Y + 4, Y, 8, 128, None) == ERR_OVERLAP  # partial residual alias
+
+
+def test_ptq1_stacked_validation(lib):
+    Part = lib.Part
+    s = lib.gemv_stacked
+    arr = (Part * 2)()
+    arr[0] = Part(W, None, 8, Y, None)
+    arr[1] = Part(W + 0x100000, None, 8, Y + 16, None)
+    assert s(4, arr, 2, QX, DX, 128, None) == ERR_OVERLAP  # outputs overlap
+    arr[1] = Part(W + 0x100000, None, 8, W + 32, None)
+    assert s(4, arr, 2, QX, DX, 128, None) == ERR_OVERLAP  # output over the other part's weights
+    arr[1] = Part(W + 0x100000, None, 8, Y + 4096, None)
+    assert s(4, arr, 2, QX, DX, 200, None) == ERR_SHAPE
+    assert s(4, arr, 2, QX, None, 128, None) == ERR_NULL
+    assert s(4, arr, 0, QX, DX, 128, None) == ERR_ARG
+    rows, waves = ctypes.c_int(), ctypes.c_int()
+    assert lib.q8g_gemv_config(4, 34816, 5120, ctypes.byref(rows), ctypes.byref(waves)) == OK
+    assert (rows.value, waves.value) == (8, 5)  # 8 block columns x 8 rows per wave, 5 waves per row
+    assert lib.q8g_gemv_config(4, 100, 100, ctypes.byref(rows), ctypes.byref(waves)) == ERR_SHAPE
 
 
 def test_rmsnorm_quantize_validation(lib):
