@@ -32,7 +32,7 @@ Q8G_F16 = 3
 Q8G_PTQ1_0 = 4
 PTQ1_BLOCK = 128
 PTQ1_BYTES = 28
-PTQ1_MAX_K = 131072
+PTQ1_MAX_K = 65536
 FUSED_MAX_K = 16384
 MAX_PARTS = 4
 BATCH_MAX = 16

@@ -23,21 +23,29 @@
 //        8 bytes per copy side by side, one copy per lane of a half-wave, so
 //        the lanes of one LDS cycle never share a bank; one v_perm places the
 //        weight byte at bits 8-15 and the lane's copy offset at bits 0-7;
-//      - lane l owns one block column c of the matrix for the whole launch.
-//        Its 128 activation codes are packed once into registers as the
-//        table entries need them: codes 5p..5p+3 in one dword and code 5p+4
-//        in another, for each of the 26 trit bytes p;
-//      - a wave covers C consecutive block columns of R = 64 / C rows per
-//        step (lane l: column l % C, row l / C), so each load instruction
-//        reads R runs of C * 28 contiguous bytes; W waves cover the nb block
-//        columns of a row, and a workgroup holds G such groups of W waves.
-//  * The block's exact int32 sum times f16(s) * f16(dx) (exact in f32: 11 +
-//    11 significant bits) is the lane's term. The C lanes of a row are summed
+//      - two lanes share a block: half 0 takes trit bytes 0-12, half 1 trit
+//        bytes 13-25 and the scale. Each reads 16 bytes per step (block bytes
+//        0-15, or 12-27 shifted down by one byte with v_alignbyte), so a lane
+//        holds 4 registers per step in flight;
+//      - a lane pair owns one block column c of the matrix for the whole
+//        launch. Each half's 65 activation codes are packed once into
+//        registers as the table entries need them: codes 5q..5q+3 in one
+//        dword and code 5q+4 in another, for each of its 13 trit bytes q;
+//      - a wave covers C consecutive block columns of R = 32 / C rows per
+//        step, so each load instruction reads R runs of C * 28 contiguous
+//        bytes; W waves cover the nb block columns of a row, and a workgroup
+//        holds G such groups of W waves (up to 16 waves).
+//    Small per-lane state (26 activation registers, 4 per step in flight)
+//    keeps about 30 waves per compute unit: the table reads and the weight
+//    loads of one wave wait while the others compute.
+//  * The two halves' int32 sums are joined (one DPP add) into the block's
+//    exact sum; times f16(s) * f16(dx) (exact in f32: 11 + 11 significant
+//    bits) it is the block's term, formed by half 1. The C lanes of a row are summed
 //    by a butterfly at lane distances 1, 2, ..., C/2; the W wave partials of
 //    a row go through LDS and are added in wave order, then the residual.
 //    C and W depend on K only, so a row's bits do not depend on N, on the
 //    tiling or on the row's part in a stacked call.
-//  * Each wave keeps two steps of weights in flight. Loads are unconditional
+//  * Each wave keeps four steps of weights in flight. Loads are unconditional
 //    except in the last steps (rows past the part's end re-read its last row
 //    and are masked), so the compiler can count them; no load goes past the
 //    group's rows, and the barriers wait for LDS only, not for loads.
@@ -56,20 +64,20 @@ namespace {
 constexpr int kPtqBlock = Q8G_PTQ1_BLOCK;  // weights per block
 constexpr int kPtqBytes = Q8G_PTQ1_BYTES;  // bytes per block
 constexpr int kTritBytes = 26;             // bytes of base-3 digits per block
+constexpr int kHalfBytes = kTritBytes / 2; // trit bytes per lane: two lanes share a block
 constexpr int kLutCopies = 32;             // table copies, one per lane of a half-wave
 constexpr int kLutStride = 8 * kLutCopies; // bytes per byte value: its entry in every copy
 constexpr int kLutBytes = 256 * kLutStride;
 constexpr int kMaxWaves = 16;              // waves per workgroup
+constexpr int kWaveCap = 8;                // waves per workgroup the launch shape aims for
 constexpr int kTargetGroups = 512;         // two workgroups per compute unit
 constexpr int kMaxPartialBytes = 16384;    // LDS for wave partials per workgroup
 constexpr int kMaxSteps = 1 << 16;         // wave steps per group
 constexpr int64_t kMaxRows = Q8G_PTQ1_MAX_ROWS;  // rows per part: row indexes stay 32-bit
-constexpr int kMaxCols = kMaxWaves * kWave;  // block columns: one per lane of 16 waves
+constexpr int kMaxCols = kMaxWaves * kWave / 2;  // block columns: one per lane pair of 16 waves
 constexpr int64_t kMaxK = (int64_t)kMaxCols * kPtqBlock;
-static_assert(kMaxK == Q8G_PTQ1_MAX_K, "the largest K is one block column per lane of 16 waves");
+static_assert(kMaxK == Q8G_PTQ1_MAX_K, "the largest K is one block column per lane pair of 16 waves");
 
-typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef int v3i_a4 __attribute__((ext_vector_type(3), aligned(4)));
 
 // Table entry of byte value v (0..255): the trits (digit - 1) of its base-3
 // digits 0..3 as four int8 (digit k in byte k), and of digit 4 as an int8 in
@@ -138,27 +146,6 @@ __global__ __launch_bounds__(kPtqBlock) void rotate_kernel(const float *__restri
         float *y2, float *y3, const float *r0, const float *r1, const float *r2, const float *r3, int n0, \
         int n1, int n2, int n3, int b1, int b2, int b3
 
-// One lane's block: 7 dwords (26 trit bytes, then the binary16 scale in the
-// upper half of dword 6).
-struct Blk {
-    uint32_t d[7];
-};
-
-__device__ __forceinline__ Blk load_blk(const uint8_t *p)
-{
-    const v4i_a4 a = __builtin_nontemporal_load(reinterpret_cast<const v4i_a4 *>(p));
-    const v3i_a4 b = __builtin_nontemporal_load(reinterpret_cast<const v3i_a4 *>(p + 16));
-    Blk k;
-    k.d[0] = (uint32_t)a.x;
-    k.d[1] = (uint32_t)a.y;
-    k.d[2] = (uint32_t)a.z;
-    k.d[3] = (uint32_t)a.w;
-    k.d[4] = (uint32_t)b.x;
-    k.d[5] = (uint32_t)b.y;
-    k.d[6] = (uint32_t)b.z;
-    return k;
-}
-
 // v_perm selector: byte 0 from src1 byte 0 (the copy offset), byte 1 from
 // src0 byte B (the weight byte), bytes 2 and 3 zero.
 template <int B>
@@ -167,47 +154,51 @@ constexpr uint32_t addr_sel()
     return 0x0C0C0000u | ((uint32_t)(4 + B) << 8);
 }
 
-// Exact int32 sum of one block against the lane's packed activation codes.
-__device__ __forceinline__ int block_isum(const Blk &k, const uint32_t (&ax)[kTritBytes],
-                                          const uint32_t (&ay)[kTritBytes], uint32_t copy_off,
-                                          const uint8_t *lut)
+// Exact int32 sum of one lane's 13 trit bytes (in w[0..3], byte q at w[q / 4]
+// byte q % 4) against its packed activation codes.
+__device__ __forceinline__ int half_isum(const uint32_t (&w)[4], const uint32_t (&ax)[kHalfBytes],
+                                         const uint32_t (&ay)[kHalfBytes], uint32_t copy_off, const uint8_t *lut)
 {
     int a0 = 0, a1 = 0;
 #pragma unroll
-    for (int p = 0; p < kTritBytes; ++p) {
+    for (int q = 0; q < kHalfBytes; ++q) {
         constexpr uint32_t sel[4] = {addr_sel<0>(), addr_sel<1>(), addr_sel<2>(), addr_sel<3>()};
-        const uint32_t addr = __builtin_amdgcn_perm(k.d[p >> 2], copy_off, sel[p & 3]);
+        const uint32_t addr = __builtin_amdgcn_perm(w[q >> 2], copy_off, sel[q & 3]);
         const uint2 e = *reinterpret_cast<const uint2 *>(lut + addr);
-        a0 = __builtin_amdgcn_sdot4((int)e.x, (int)ax[p], a0, false);
-        if (p + 1 < kTritBytes) a1 = __builtin_amdgcn_sdot4((int)e.y, (int)ay[p], a1, false);  // byte 25: no digit 4
+        a0 = __builtin_amdgcn_sdot4((int)e.x, (int)ax[q], a0, false);
+        a1 = __builtin_amdgcn_sdot4((int)e.y, (int)ay[q], a1, false);
     }
     return a0 + a1;
 }
 
-template <int C>
+// Sum over the L lanes of a row (lane bits 0 .. log2(L) - 1), in every lane.
+template <int L>
 __device__ __forceinline__ float row_sum(float v)
 {
-    if constexpr (C >= 2) v = xsum<1>(v);
-    if constexpr (C >= 4) v = xsum<2>(v);
-    if constexpr (C >= 8) v = xsum<4>(v);
-    if constexpr (C >= 16) v = xsum<8>(v);
-    if constexpr (C >= 32) v = xsum<16>(v);
-    if constexpr (C >= 64) v = xsum<32>(v);
+    if constexpr (L >= 2) v = xsum<1>(v);
+    if constexpr (L >= 4) v = xsum<2>(v);
+    if constexpr (L >= 8) v = xsum<4>(v);
+    if constexpr (L >= 16) v = xsum<8>(v);
+    if constexpr (L >= 32) v = xsum<16>(v);
+    if constexpr (L >= 64) v = xsum<32>(v);
     return v;
 }
 
-constexpr int kDepth = 2;          // wave steps whose weights are in flight while one is consumed
+constexpr int kDepth = 4;          // wave steps whose weights are in flight while one is consumed
 constexpr int kRing = kDepth + 1;  // weight buffers per lane
+
+typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // Workgroup = G groups of W waves over rows of one part; group g owns
 // rows_per_group consecutive rows starting at (workgroup index within the
-// part) * G * rows_per_group + g * rows_per_group.
+// part) * G * rows_per_group + g * rows_per_group. Lane l: half h = l & 1 of
+// block column j = (l / 2) % C of row slot l / (2C).
 template <int C>
 __global__ __launch_bounds__(kMaxWaves *kWave) void gemv_kernel(PTQ_PARTS_PARAMS, const int8_t *__restrict__ qx,
                                                                 const uint16_t *__restrict__ dx, int nb, int W,
                                                                 int steps)
 {
-    constexpr int R = kWave / C;  // rows per wave step
+    constexpr int R = kWave / (2 * C);  // rows per wave step
     __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
     __shared__ uint2 stage[256];
     extern __shared__ float partial[];  // [G * rows_per_group][W]
@@ -225,25 +216,29 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void gemv_kernel(PTQ_PARTS_PARAMS
     const int wave = threadIdx.x >> 6;
     const int G = blockDim.x / (kWave * W);
     const int g = wave / W, wg = wave - g * W;
-    const int c = wg * C + (lane & (C - 1));  // block column of this lane
-    const int rs = lane / C;                  // row slot within a step
+    const uint32_t h = lane & 1;                     // 0: trit bytes 0-12; 1: bytes 13-25 and the scale
+    const int c = wg * C + ((lane >> 1) & (C - 1));  // block column of this lane
+    const int rs = lane / (2 * C);                   // row slot within a step
     const bool col_ok = c < nb;
-    const int cl = col_ok ? c : nb - 1;       // clamped: always a valid column to read
+    const int cl = col_ok ? c : nb - 1;              // clamped: always a valid column to read
     const int rows_per_group = steps * R;
     const uint32_t row_bytes = (uint32_t)nb * kPtqBytes;
     const int wg_row0 = bp * G * rows_per_group;
     const int grp_row0 = wg_row0 + g * rows_per_group;
-    const uint8_t *lane_base = wp + (uint32_t)cl * kPtqBytes;
+    // half 0 reads block bytes 0-15, half 1 bytes 12-27 (then drops its first byte)
+    const uint8_t *lane_base = wp + (uint32_t)cl * kPtqBytes + 12 * h;
 
-    // the lane's block at step s (rows past the part's end re-read its last row)
+    // the lane's 16 bytes at step s (rows past the part's end re-read its last row)
     auto blk_at = [&](int s) {
         const int r = min(grp_row0 + s * R + rs, np - 1);
-        return load_blk(lane_base + (uint64_t)(uint32_t)r * row_bytes);
+        const v4i_a4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i_a4 *>(lane_base + (uint64_t)(uint32_t)r * row_bytes));
+        return v;
     };
 
-    // the lane's 128 activation codes and their scale: requested first, so that
+    // the column's 128 activation codes and scale: requested first, so that
     // waiting for them leaves the weight loads below in flight
-    uint32_t raw[33];
+    uint32_t raw[32];
     {
         const int4 *q4 = reinterpret_cast<const int4 *>(qx + (int64_t)cl * kPtqBlock);
 #pragma unroll
@@ -254,12 +249,11 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void gemv_kernel(PTQ_PARTS_PARAMS
             raw[4 * i + 2] = (uint32_t)v.z;
             raw[4 * i + 3] = (uint32_t)v.w;
         }
-        raw[32] = 0;  // positions 128 and up: no weight (digits 3, 4 of byte 25)
     }
     const uint16_t dxbits = dx[cl];
 
     // the first steps' weights are requested before the table is built
-    Blk b[kRing];  // step t lives in b[t % kRing]
+    v4i_a4 b[kRing];  // step t lives in b[t % kRing]
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) b[j] = blk_at(j < steps ? j : steps - 1);
 
@@ -274,28 +268,51 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void gemv_kernel(PTQ_PARTS_PARAMS
         *reinterpret_cast<uint4 *>(lut + 16 * e) = make_uint4(t.x, t.y, t.x, t.y);
     }
 
-    // packed for the table entries: codes 5p..5p+3 and code 5p+4 of trit byte p
-    uint32_t ax[kTritBytes], ay[kTritBytes];
+    // this half's codes (weights 65h .. 65h + 64), packed for the table entries:
+    // codes 5q..5q+3 and code 5q+4 of its trit byte q
+    uint32_t ax[kHalfBytes], ay[kHalfBytes];
+    {
+        uint32_t hs[18], sh[17];
 #pragma unroll
-    for (int p = 0; p < kTritBytes; ++p) {
-        const int o = 5 * p;
-        ax[p] = (o & 3) ? __builtin_amdgcn_alignbyte(raw[(o >> 2) + 1], raw[o >> 2], o & 3) : raw[o >> 2];
-        const int o4 = o + 4;
-        ay[p] = o4 < kPtqBlock ? raw[o4 >> 2] >> (8 * (o4 & 3)) : 0u;
+        for (int i = 0; i < 18; ++i) {
+            const uint32_t lo = i < 32 ? raw[i] : 0u, hi = 16 + i < 32 ? raw[16 + i] : 0u;
+            hs[i] = h ? hi : lo;  // codes from 64h
+        }
+#pragma unroll
+        for (int i = 0; i < 17; ++i) sh[i] = __builtin_amdgcn_alignbyte(hs[i + 1], hs[i], h);  // from 65h
+#pragma unroll
+        for (int q = 0; q < kHalfBytes; ++q) {
+            const int o = 5 * q, o4 = o + 4;
+            ax[q] = (o & 3) ? __builtin_amdgcn_alignbyte(sh[(o >> 2) + 1], sh[o >> 2], o & 3) : sh[o >> 2];
+            ay[q] = sh[o4 >> 2] >> (8 * (o4 & 3));
+        }
+        // half 1, byte 12 is block byte 25: its digits 3 and 4 belong to no weight
+        if (h) {
+            ax[kHalfBytes - 1] &= 0x00FFFFFFu;
+            ay[kHalfBytes - 1] = 0;
+        }
     }
     const float dxf = f16_bits_to_f32(dxbits);
     const uint32_t copy_off = (uint32_t)(lane & (kLutCopies - 1)) * 8;
+    const uint32_t term_mask = (h && col_ok) ? 0xFFFFFFFFu : 0u;
+    const bool leader = (lane & (2 * C - 1)) == 0;  // the lane that stores a row's wave partial
     lds_barrier();
 
-    // one step: the block sum of b[j] (step s) into the row's partial
-    auto consume = [&](const Blk &k, int s) {
-        const int isum = block_isum(k, ax, ay, copy_off, lut);
-        const float sd = f16_bits_to_f32((uint16_t)(k.d[6] >> 16)) * dxf;  // exact
-        float t = (float)isum * sd;
-        if (!col_ok) t = 0.0f;
-        t = row_sum<C>(t);
-        const int r = grp_row0 + s * R + rs;
-        if ((lane & (C - 1)) == 0 && r < np) partial[(r - wg_row0) * W + wg] = t;
+    // one step: this half's block sum, joined with the other half's; the half
+    // holding the scale forms the block's term; the row's terms are summed
+    auto consume = [&](const v4i_a4 &k, int s) {
+        const uint32_t d[5] = {(uint32_t)k.x, (uint32_t)k.y, (uint32_t)k.z, (uint32_t)k.w, 0u};
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], h);
+        int isum = half_isum(w, ax, ay, copy_off, lut);
+        isum += xchg_int<1>(isum);                                          // the block's exact sum
+        const float sd = f16_bits_to_f32((uint16_t)(w[3] >> 8)) * dxf;      // exact (half 1)
+        // half 0 (its scale bits are trit bytes) and columns past nb contribute +0
+        float t = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, (float)isum * sd) & term_mask);
+        t = row_sum<2 * C>(t);
+        // rows past the part's end have slots too (the finalize skips them)
+        if (leader) partial[(grp_row0 - wg_row0 + s * R + rs) * W + wg] = t;
     };
     // Each step first requests the weights of step s + kDepth into the buffer
     // consumed last, then consumes step s; the empty asm keeps the compiler from
@@ -359,13 +376,15 @@ struct PtqConfig {
 };
 
 // C: the largest share of useful lanes first (nb / (W * C)), then in the order
-// 8, 16, 4, 32, 64, 2, 1 (runs of 224 or 448 contiguous bytes per row and
-// a short butterfly first). W = ceil(nb / C) <= 16; G groups make up to 8
-// waves (W waves when W > 8). Steps: enough rows per group that about 512
-// workgroups cover all rows, within the LDS of the partials.
+// 8, 16, 4, 32, 2, 1 (runs of 224 or 448 contiguous bytes per row and a short
+// butterfly first). W = ceil(nb / C) <= 16; G groups make up to 8 waves (W
+// when W > 8): two such workgroups share a compute unit's LDS, and measured on
+// MI355X, 8-wave workgroups beat 12- and 16-wave ones on the decode shapes.
+// Steps: enough rows per group that about 512 workgroups cover all rows,
+// within the LDS of the partials.
 PtqConfig ptq_pick(int64_t nb, int64_t n_total)
 {
-    static const int pref[] = {8, 16, 4, 32, 64, 2, 1};
+    static const int pref[] = {8, 16, 4, 32, 2, 1};
     PtqConfig c{};
     double best = -1.0;
     for (int C : pref) {
@@ -378,8 +397,8 @@ PtqConfig ptq_pick(int64_t nb, int64_t n_total)
             c.W = (int)W;
         }
     }
-    c.G = c.W <= 8 ? 8 / c.W : 1;
-    const int64_t per_step = (int64_t)c.G * (kWave / c.C);  // rows of one workgroup step
+    c.G = c.W < kWaveCap ? kWaveCap / c.W : 1;
+    const int64_t per_step = (int64_t)c.G * (kWave / (2 * c.C));  // rows of one workgroup step
     int64_t steps = (n_total + kTargetGroups * per_step - 1) / (kTargetGroups * per_step);
     if (steps < 1) steps = 1;
     if (steps > kMaxSteps) steps = kMaxSteps;
@@ -389,7 +408,7 @@ PtqConfig ptq_pick(int64_t nb, int64_t n_total)
     return c;
 }
 
-int64_t rows_per_block(const PtqConfig &c) { return (int64_t)c.G * (kWave / c.C) * c.steps; }
+int64_t rows_per_block(const PtqConfig &c) { return (int64_t)c.G * (kWave / (2 * c.C)) * c.steps; }
 
 struct PtqParts {
     const uint8_t *w[4];
@@ -433,8 +452,7 @@ hipError_t launch_gemv(PtqParts p, int nparts, const int8_t *qx, const uint16_t 
     case 4: return launch_c<4>(p, qx, dx, nb, c, (int)blocks, s);
     case 8: return launch_c<8>(p, qx, dx, nb, c, (int)blocks, s);
     case 16: return launch_c<16>(p, qx, dx, nb, c, (int)blocks, s);
-    case 32: return launch_c<32>(p, qx, dx, nb, c, (int)blocks, s);
-    default: return launch_c<64>(p, qx, dx, nb, c, (int)blocks, s);
+    default: return launch_c<32>(p, qx, dx, nb, c, (int)blocks, s);
     }
 }
 
@@ -506,7 +524,7 @@ q8g_status ptq1_config(int64_t n_total, int64_t K, int *rows_per_wave, int *wave
 {
     if (n_total < 0 || K <= 0 || K % kPtqBlock || K > kMaxK) return Q8G_ERR_SHAPE;
     const PtqConfig c = ptq_pick(K / kPtqBlock, n_total);
-    if (rows_per_wave) *rows_per_wave = kWave / c.C;
+    if (rows_per_wave) *rows_per_wave = kWave / (2 * c.C);
     if (waves_per_group) *waves_per_group = c.G * c.W;
     return Q8G_OK;
 }

@@ -169,7 +169,7 @@ q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, cons
  * contiguous: w uint8 [N][K/128 * 28]. */
 #define Q8G_PTQ1_BLOCK 128
 #define Q8G_PTQ1_BYTES 28
-#define Q8G_PTQ1_MAX_K 131072
+#define Q8G_PTQ1_MAX_K 65536
 #define Q8G_PTQ1_MAX_ROWS (1 << 30)
 
 /* Rotate an activation and quantize it for PTQ1_0 weights ([T]: computed once

@@ -219,7 +219,7 @@ def test_ptq1_rotate_validation(lib):
 def test_ptq1_gemv_validation(lib):
     g = lib.ptq1_gemv
     assert g(W, QX, DX, None, Y, 8, 96, None) == ERR_SHAPE  # K % 128
-    assert g(W, QX, DX, None, Y, 8, 131072 + 128, None) == ERR_SHAPE  # K > Q8G_PTQ1_MAX_K
+    assert g(W, QX, DX, None, Y, 8, 65536 + 128, None) == ERR_SHAPE  # K > Q8G_PTQ1_MAX_K
     assert g(W, QX, DX, None, Y, -1, 128, None) == ERR_SHAPE
     assert g(W, QX, DX, None, Y, (1 << 30) + 1, 128, None) == ERR_SHAPE  # N > Q8G_PTQ1_MAX_ROWS
     assert g(None, None, None, None, None, 0, 128, None) == OK  # N == 0
@@ -253,7 +253,7 @@ def test_ptq1_stacked_validation(lib):
     assert s(4, arr, 0, QX, DX, 128, None) == ERR_ARG
     rows, waves = ctypes.c_int(), ctypes.c_int()
     assert lib.q8g_gemv_config(4, 34816, 5120, ctypes.byref(rows), ctypes.byref(waves)) == OK
-    assert (rows.value, waves.value) == (8, 5)  # 8 block columns x 8 rows per wave, 5 waves per row
+    assert (rows.value, waves.value) == (4, 5)  # 8 block columns x 4 rows per wave step, 5 waves per row
     assert lib.q8g_gemv_config(4, 100, 100, ctypes.byref(rows), ctypes.byref(waves)) == ERR_SHAPE
 
 

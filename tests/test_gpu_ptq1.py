@@ -116,10 +116,11 @@ def test_rotation_special_blocks(q8, orc):
 
 # --------------------------------------------------------------------------- GEMV
 
-# (N, K): block-column splits C x W = 8x1 (K 1024), 8x2, 4x5 (2560), 4x7 (3584), 8x4, 8x5 (5120),
-# 8x12, 16x9 (17408), 1x1 (128), 2x... ragged row counts and part tails
+# (N, K): block-column splits C x W = 1x1 (K 128), 2x1, 4x1 (384: 3 of 4 columns), 8x1 (1024),
+# 16x1, 4x5 (2560), 4x7 (3584), 32x1, 8x5 (5120), 32x3 (12288), 16x9 (17408), 32x16 (65536);
+# ragged row counts and part tails
 SHAPES = [(1, 128), (7, 256), (65, 384), (300, 1024), (1000, 2048), (777, 2560), (513, 3584), (4096, 4096),
-          (300, 5120), (257, 12288), (100, 17408), (3, 131072)]
+          (300, 5120), (257, 12288), (100, 17408), (3, 65536)]
 
 
 def ptq1_case(seed, n, k):
@@ -143,7 +144,7 @@ def test_gemv_vs_oracle(q8, orc, n, k, res):
     within(host(y), yr, S, f"{n}x{k}")
 
 
-@pytest.mark.parametrize("n,k", [(300, 1024), (777, 2560), (257, 12288), (64, 131072)])
+@pytest.mark.parametrize("n,k", [(300, 1024), (777, 2560), (257, 12288), (64, 65536)])
 def test_gemv_unit_scales_bit_exact(q8, orc, n, k):
     """Scales 1.0 on both sides: each block term is the integer block sum and every partial
     sum is an integer below 2^24, so the f32 result is exact whatever the order."""
