@@ -30,6 +30,8 @@ Q8G_BF16 = 1
 Q8G_Q8_0_F32 = 2
 Q8G_F16 = 3
 Q8G_PTQ1_0 = 4
+Q8G_LAYOUT_ROWS = 0
+Q8G_LAYOUT_TILE16 = 1
 PTQ1_BLOCK = 128
 PTQ1_BYTES = 28
 PTQ1_MAX_K = 65536
@@ -101,6 +103,9 @@ def load_library(path: str = LIB_PATH):
     lib.f16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
     lib.q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
     lib.q8g_batch_config.argtypes = [_I64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.q8_gemv_batch_layout.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+    lib.q8_tile16_sizes.argtypes = [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+    lib.q8_pack_tile16.argtypes = [_P, _P, _I64, _I64, _P, _P]
     lib.gemv_stacked.argtypes = [ctypes.c_int, ctypes.POINTER(_Part), ctypes.c_int, _P, _P, _I64, _P]
     lib.q8_rmsnorm_quantize_act.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I64, _P]
     lib.q8_silu_mul_quantize_act.argtypes = [_P, _P, _P, _I64, _P]
@@ -129,7 +134,8 @@ def load_library(path: str = LIB_PATH):
                "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
                "q8_gateup_silu", "q8_gateup_rmsnorm_silu",
                "q8_rmsnorm_quantize_act_batch", "q8_silu_mul_quantize_act_batch",
-               "ptq1_rotate_quantize_act", "ptq1_gemv"):
+               "ptq1_rotate_quantize_act", "ptq1_gemv", "q8_gemv_batch_layout", "q8_tile16_sizes",
+               "q8_pack_tile16"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -265,19 +271,72 @@ def q8_gemv(qw, dw, qx, dx, y=None, residual=None, stream=None):
 
 def q8_gemv_batch(qw, dw, qx, dx, y=None, residual=None, stream=None):
     """Small batch: y[b] = Q8_0(qw, dw) · (qx[b], dx[b]) (+ residual[b]) for B <= 16 activation
-    vectors sharing one pass over the weights. qx int8 [B, K], dx [B, K/32]; returns y (f32 [B, N])."""
-    if qw.dim() != 2 or qx.dim() != 2:
-        raise ValueError("qw must be [N, K] and qx [B, K]")
-    n, k = qw.shape
+    vectors sharing one pass over the weights. qw int8 [N, K] and dw [N, K/32], or a Tile16
+    (from pack_tile16); qx int8 [B, K], dx [B, K/32]; returns y (f32 [B, N])."""
+    if qx.dim() != 2:
+        raise ValueError("qx must be [B, K]")
+    if isinstance(qw, Tile16):
+        n, k, layout = qw.n, qw.k, Q8G_LAYOUT_TILE16
+        pw, pdw = _ptr(qw.codes, "codes", _I8), _ptr(qw.scales, "scales", _H16)
+    else:
+        if qw.dim() != 2:
+            raise ValueError("qw must be [N, K]")
+        n, k = qw.shape
+        layout = Q8G_LAYOUT_ROWS
+        pw, pdw = _ptr(qw, "qw", _I8), _ptr(dw, "dw", _H16, (n, k // 32))
     b = qx.shape[0]
     if y is None:
-        y = torch.empty((b, n), dtype=torch.float32, device=qw.device)
-    st = load_library().q8_gemv_batch(
-        _ptr(qw, "qw", _I8), _ptr(dw, "dw", _H16, (n, k // 32)), _ptr(qx, "qx", _I8, (b, k)),
-        _ptr(dx, "dx", _H16, (b, k // 32)), _ptr(residual, "residual", _F32, (b, n), optional=True),
-        _ptr(y, "y", _F32, (b, n)), n, k, b, _stream(stream))
-    _check("q8_gemv_batch", st)
+        y = torch.empty((b, n), dtype=torch.float32, device=qx.device)
+    st = load_library().q8_gemv_batch_layout(
+        layout, pw, pdw, _ptr(qx, "qx", _I8, (b, k)), _ptr(dx, "dx", _H16, (b, k // 32)),
+        _ptr(residual, "residual", _F32, (b, n), optional=True), _ptr(y, "y", _F32, (b, n)), n, k, b,
+        _stream(stream))
+    _check("q8_gemv_batch_layout", st)
     return y
+
+
+class Tile16:
+    """Q8_0 weights in the 16-row tiled layout of q8_gemv_batch (Q8G_LAYOUT_TILE16):
+    codes int8 and scales (16-bit) as 1-D device tensors of the sizes q8_tile16_sizes gives."""
+
+    def __init__(self, codes, scales, n, k):
+        self.codes, self.scales, self.n, self.k = codes, scales, int(n), int(k)
+
+
+def tile16_sizes(n, k):
+    """(code bytes, scale bytes) of the tiled layout of an n x k matrix."""
+    cb, sb = _I64(), _I64()
+    _check("q8_tile16_sizes", load_library().q8_tile16_sizes(n, k, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def pack_tile16_host(qw, dw):
+    """Host-side pack (numpy in, numpy out): qw int8 [N, K], dw uint16 [N, K/32] ->
+    (codes int8 [code bytes], scales uint16 [scale bytes / 2]) in the tiled layout."""
+    import numpy as np
+
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    dw = np.ascontiguousarray(dw).view(np.uint16)
+    n, k = qw.shape
+    if dw.shape != (n, k // 32):
+        raise ValueError("dw must be [N, K/32]")
+    cb, sb = tile16_sizes(n, k)
+    codes = np.empty(cb, np.int8)
+    scales = np.empty(sb // 2, np.uint16)
+    st = load_library().q8_pack_tile16(qw.ctypes.data if qw.size else None, dw.ctypes.data if dw.size else None,
+                                       n, k, codes.ctypes.data if codes.size else None,
+                                       scales.ctypes.data if scales.size else None)
+    _check("q8_pack_tile16", st)
+    return codes, scales
+
+
+def pack_tile16(qw, dw, device="cuda"):
+    """Pack host weights (numpy int8 [N, K] and uint16 [N, K/32]) into a device Tile16."""
+    import numpy as np
+
+    codes, scales = pack_tile16_host(qw, dw)
+    n, k = np.asarray(qw).shape
+    return Tile16(torch.from_numpy(codes).to(device), torch.from_numpy(scales.view(np.int16)).to(device), n, k)
 
 
 def batch_config(n):

@@ -41,6 +41,16 @@
 //  * S waves of a workgroup may split the K range of one 16-row tile (16 or 4
 //    for matrices with few tiles, so that enough waves exist); their partial
 //    sums are added in a fixed order through LDS.
+//  * Weight layouts ("Filling in the blanks", section GPU Performance
+//    Heisenbugs: weights stored in groups of columns, so that a decode warp
+//    reads whole cache lines). In the row layout a step's operand load is 16
+//    rows x 64 bytes, 16 cache lines per KiB, half of each line used by the
+//    step. The tiled layout (Q8G_LAYOUT_TILE16, written once by
+//    q8_pack_tile16) stores each 16-row x 64-column step operand as one
+//    contiguous KiB in the lane order of the load (lane l reads bytes
+//    [16l, 16l + 16)), and each block's 16 row scales side by side, so a step
+//    reads 8 whole cache lines. Only addresses differ: both layouts compute
+//    every output with the same instructions in the same order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -111,7 +121,7 @@ __device__ __forceinline__ void wait_counts()
     __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (lgkm << 8));
 }
 
-template <class SH>
+template <class SH, bool TILED>
 __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__restrict__ qw,
                                                             const uint16_t *__restrict__ dw,
                                                             const int8_t *__restrict__ qx,
@@ -140,6 +150,12 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
     const int jr = (int)((row_ok ? row : N - 1) - rbase);
     const int8_t *wbase = qw + rbase * K;
     const uint32_t woff = (uint32_t)jr * (uint32_t)K;
+    // tiled layout: tile tg's step st is the KiB at (tg * steps_row + st) * 1024; a
+    // tile wholly past N (in the last workgroup) re-reads the last tile
+    const int64_t ntiles = (N + kTileRows - 1) / kTileRows;
+    const int64_t tg = row0 / kTileRows < ntiles ? row0 / kTileRows : ntiles - 1;
+    const int64_t steps_row = (K + kStepK - 1) / kStepK;
+    const int8_t *tbase = qw + tg * steps_row * 1024 + 16 * lane;
 
     if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(s_lds) = make_uint4(0u, 0u, 0u, 0u);  // the zero slot
 
@@ -204,15 +220,23 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
             const int r = t / nbw, bo = t - r * nbw;
             const int64_t rr = row0 + r < N ? row0 + r : N - 1;
             const int64_t bk = blk0 + bo < nb ? blk0 + bo : blk0;
-            if (t < kTileRows * nbw) __builtin_amdgcn_global_load_lds(dw + rr * nb + bk, s_wsc + 4 * p0, 2, 0, 0);
+            // tiled: block bk of tile tg holds its 16 rows' scales side by side (rows
+            // past N are padding inside the tile)
+            const uint16_t *src = TILED ? dw + (tg * nb + bk) * kTileRows + r : dw + rr * nb + bk;
+            if (t < kTileRows * nbw) __builtin_amdgcn_global_load_lds(src, s_wsc + 4 * p0, 2, 0, 0);
         }
 
         // 2. the first window of weights (one load per step). Steps past the
         //    wave's share re-read its last step, so every issue is unconditional.
         int4 wv[P];
         auto issue = [&](int p, int st) {
-            const bool hi = st * kStepK + 32 < kt;  // the step's second block exists
-            wv[p] = load16_stream(wbase + (woff + ((q < 2 || hi) ? (uint32_t)(k0 + st * kStepK + 16 * q) : 0u)));
+            if (TILED) {
+                // a missing second block reads the tile's zero padding
+                wv[p] = load16_stream(tbase + (k0 / kStepK + st) * 1024);
+            } else {
+                const bool hi = st * kStepK + 32 < kt;  // the step's second block exists
+                wv[p] = load16_stream(wbase + (woff + ((q < 2 || hi) ? (uint32_t)(k0 + st * kStepK + 16 * q) : 0u)));
+            }
         };
         const int last = s_end > s_begin ? s_end - 1 : s_begin;
 #pragma unroll
@@ -318,21 +342,30 @@ bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 }
 
 template <class SH>
-hipError_t launch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx, const float *residual,
-                  float *y, int64_t N, int64_t K, int B, hipStream_t s)
+hipError_t launch(bool tiled, const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                  const float *residual, float *y, int64_t N, int64_t K, int B, hipStream_t s)
 {
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
     const int64_t groups = (tiles + SH::kTiles - 1) / SH::kTiles;
     void *args[] = {&qw, &dw, &qx, &dx, &residual, &y, &N, &K, &B};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&batch_kernel<SH>), dim3((unsigned)groups),
-                           dim3(SH::kThreads), args, 0, s);
+    const void *fn = tiled ? reinterpret_cast<const void *>(&batch_kernel<SH, true>)
+                           : reinterpret_cast<const void *>(&batch_kernel<SH, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(SH::kThreads), args, 0, s);
 }
 
-}  // namespace
-
-extern "C" q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
-                                    const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream)
+// bytes of the tiled codes and scales of an N x K matrix (rows padded to whole
+// 16-row tiles, each row's codes to whole 64-byte steps)
+int64_t tile16_code_bytes(int64_t N, int64_t K)
 {
+    return (N + kTileRows - 1) / kTileRows * kTileRows * ((K + kStepK - 1) / kStepK * kStepK);
+}
+int64_t tile16_scale_bytes(int64_t N, int64_t K) { return (N + kTileRows - 1) / kTileRows * kTileRows * (K / 32) * 2; }
+
+q8g_status batch_run(int layout, const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                     const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream)
+{
+    if (layout != Q8G_LAYOUT_ROWS && layout != Q8G_LAYOUT_TILE16) return Q8G_ERR_ARG;
+    const bool tiled = layout == Q8G_LAYOUT_TILE16;
     if (N < 0 || K < 0 || B < 0 || B > kBatchMax || N > kMaxElems || K > kMaxElems) return Q8G_ERR_SHAPE;
     if (K % 32 || K > kMaxK) return Q8G_ERR_SHAPE;
     if (N > 0 && K > 0 && N > kMaxElems / K) return Q8G_ERR_SHAPE;
@@ -343,17 +376,77 @@ extern "C" q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const 
         (residual && !aligned(residual, 4)))
         return Q8G_ERR_ALIGN;
     const int64_t ybytes = B * N * 4;
-    if (overlap(y, ybytes, qw, N * K) || overlap(y, ybytes, dw, N * (K / 32) * 2) || overlap(y, ybytes, qx, B * K) ||
+    const int64_t wbytes = tiled ? tile16_code_bytes(N, K) : N * K;
+    const int64_t dwbytes = tiled ? tile16_scale_bytes(N, K) : N * (K / 32) * 2;
+    if (overlap(y, ybytes, qw, wbytes) || overlap(y, ybytes, dw, dwbytes) || overlap(y, ybytes, qx, B * K) ||
         overlap(y, ybytes, dx, B * (K / 32) * 2))
         return Q8G_ERR_OVERLAP;
     // the residual may be y itself (each element is read, then written, by one lane)
     if (residual && residual != y && overlap(y, ybytes, residual, ybytes)) return Q8G_ERR_OVERLAP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
-    const hipError_t e = tiles <= kWideSplitTiles ? launch<WideSplitShape>(qw, dw, qx, dx, residual, y, N, K, (int)B, s)
-                         : tiles <= kSplitTiles   ? launch<SplitShape>(qw, dw, qx, dx, residual, y, N, K, (int)B, s)
-                                                  : launch<WholeShape>(qw, dw, qx, dx, residual, y, N, K, (int)B, s);
+    const hipError_t e =
+        tiles <= kWideSplitTiles ? launch<WideSplitShape>(tiled, qw, dw, qx, dx, residual, y, N, K, (int)B, s)
+        : tiles <= kSplitTiles   ? launch<SplitShape>(tiled, qw, dw, qx, dx, residual, y, N, K, (int)B, s)
+                                 : launch<WholeShape>(tiled, qw, dw, qx, dx, residual, y, N, K, (int)B, s);
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                                    const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream)
+{
+    return batch_run(Q8G_LAYOUT_ROWS, qw, dw, qx, dx, residual, y, N, K, B, stream);
+}
+
+extern "C" q8g_status q8_gemv_batch_layout(int layout, const int8_t *qw, const uint16_t *dw, const int8_t *qx,
+                                           const uint16_t *dx, const float *residual, float *y, int64_t N, int64_t K,
+                                           int64_t B, void *stream)
+{
+    return batch_run(layout, qw, dw, qx, dx, residual, y, N, K, B, stream);
+}
+
+extern "C" q8g_status q8_tile16_sizes(int64_t N, int64_t K, int64_t *code_bytes, int64_t *scale_bytes)
+{
+    if (N < 0 || K < 0 || K % 32 || K > kMaxK || N > kMaxElems || (N > 0 && K > 0 && N > kMaxElems / K))
+        return Q8G_ERR_SHAPE;
+    if (!code_bytes || !scale_bytes) return Q8G_ERR_NULL;
+    *code_bytes = tile16_code_bytes(N, K);
+    *scale_bytes = tile16_scale_bytes(N, K);
+    return Q8G_OK;
+}
+
+extern "C" q8g_status q8_pack_tile16(const int8_t *qw, const uint16_t *dw, int64_t N, int64_t K, int8_t *qw_tiled,
+                                     uint16_t *dw_tiled)
+{
+    if (N < 0 || K < 0 || K % 32 || K > kMaxK || N > kMaxElems || (N > 0 && K > 0 && N > kMaxElems / K))
+        return Q8G_ERR_SHAPE;
+    if (N == 0 || K == 0) return Q8G_OK;
+    if (!qw || !dw || !qw_tiled || !dw_tiled) return Q8G_ERR_NULL;
+    const int64_t cb = tile16_code_bytes(N, K), sb = tile16_scale_bytes(N, K);
+    if (overlap(qw_tiled, cb, qw, N * K) || overlap(qw_tiled, cb, dw, N * (K / 32) * 2) ||
+        overlap(dw_tiled, sb, qw, N * K) || overlap(dw_tiled, sb, dw, N * (K / 32) * 2) ||
+        overlap(qw_tiled, cb, dw_tiled, sb))
+        return Q8G_ERR_OVERLAP;
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows, steps = (K + kStepK - 1) / kStepK, nb = K / 32;
+    for (int64_t t = 0; t < tiles; ++t)
+        for (int64_t st = 0; st < steps; ++st) {
+            int8_t *o = qw_tiled + (t * steps + st) * 1024;
+            for (int q = 0; q < 4; ++q)
+                for (int j = 0; j < kTileRows; ++j)
+                    for (int b = 0; b < 16; ++b) {
+                        const int64_t row = t * kTileRows + j, col = st * kStepK + 16 * q + b;
+                        o[16 * (16 * q + j) + b] = row < N && col < K ? qw[row * K + col] : 0;
+                    }
+        }
+    for (int64_t t = 0; t < tiles; ++t)
+        for (int64_t blk = 0; blk < nb; ++blk)
+            for (int j = 0; j < kTileRows; ++j) {
+                const int64_t row = t * kTileRows + j;
+                dw_tiled[(t * nb + blk) * kTileRows + j] = row < N ? dw[row * nb + blk] : (uint16_t)0;
+            }
+    return Q8G_OK;
 }
 
 extern "C" q8g_status q8g_batch_config(int64_t N, int *k_split, int *steps_in_flight)

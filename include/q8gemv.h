@@ -21,9 +21,10 @@
  *       once and shared by every projection that reads the same input.
  *
  * Conventions for every entry point:
- *   - Data pointers are DEVICE pointers owned by the caller. The one exception
- *     is the `parts` array of gemv_stacked, which is host memory read during
- *     the call only.
+ *   - Data pointers are DEVICE pointers owned by the caller. The exceptions
+ *     are the `parts` array of gemv_stacked and the descriptors of
+ *     q8_decode_stack, host memory read during the call only, and the
+ *     weight packing call q8_pack_tile16, which works on host memory.
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; nothing is synchronized, allocated or freed, and no
  *     environment variable is read. The library holds no mutable global
@@ -121,6 +122,40 @@ q8g_status f16_gemv(const uint16_t *w, const uint16_t *x, const float *residual,
 #define Q8G_BATCH_MAX 16
 q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
                          const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream);
+
+/* ---- weight layout of the small-batch GEMV ----------------------------------
+ * [P] GPU Performance Heisenbugs: storing the weights in groups of columns lets
+ * a decode warp read whole cache lines. Q8G_LAYOUT_ROWS is the plain [N][K]
+ * codes and [N][K/32] scales of q8_gemv_batch. Q8G_LAYOUT_TILE16 groups 16 rows:
+ *   codes: tile t (rows 16t..16t+15) and step s (columns 64s..64s+63) form one
+ *          1024-byte unit at byte (t * S + s) * 1024, S = ceil(K / 64); inside
+ *          it, row j's columns 64s + 16c .. 64s + 16c + 15 are the 16 bytes at
+ *          16 * (16c + j) (c = 0..3);
+ *   scales: block b of tile t holds its 16 rows' binary16 scale bits side by
+ *          side at element (t * K/32 + b) * 16 + j;
+ *   rows past N (up to the next multiple of 16) and columns past K (up to the
+ *   next multiple of 64) are zero. q8_tile16_sizes gives the sizes. */
+typedef enum { Q8G_LAYOUT_ROWS = 0, Q8G_LAYOUT_TILE16 = 1 } q8g_layout;
+
+/* q8_gemv_batch with the weights in the given layout (qw, dw device pointers in
+ * that layout; every other argument and rule as for q8_gemv_batch). The results
+ * are identical, bit for bit, in both layouts: only the weight addresses differ.
+ * Q8G_ERR_ARG for an unknown layout. */
+q8g_status q8_gemv_batch_layout(int layout, const int8_t *qw, const uint16_t *dw, const int8_t *qx,
+                                const uint16_t *dx, const float *residual, float *y, int64_t N, int64_t K, int64_t B,
+                                void *stream);
+
+/* Bytes of the Q8G_LAYOUT_TILE16 codes and scales of an N x K matrix (K % 32 == 0).
+ * Pure host query. */
+q8g_status q8_tile16_sizes(int64_t N, int64_t K, int64_t *code_bytes, int64_t *scale_bytes);
+
+/* Rewrite row-layout Q8_0 weights (qw int8 [N][K], dw uint16 [N][K/32]) into
+ * Q8G_LAYOUT_TILE16 (qw_tiled, dw_tiled of the sizes above, padding written as
+ * zero). HOST pointers, unlike every other call: weights are packed once, when
+ * they are loaded, and then copied to the device. Synchronous; the outputs may
+ * not overlap the inputs or each other. */
+q8g_status q8_pack_tile16(const int8_t *qw, const uint16_t *dw, int64_t N, int64_t K, int8_t *qw_tiled,
+                          uint16_t *dw_tiled);
 
 /* Launch configuration q8_gemv_batch picks for N rows: how many waves split the K
  * range of one 16-row tile, and how many 64-column weight steps each wave keeps

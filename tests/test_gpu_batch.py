@@ -219,3 +219,72 @@ def test_batch_full_size_head(q8, orc):
         yr, S = orc.q8_gemv_batch(qw[rows], dw[rows], qxh, dxh)
         within(y[:, rows], yr, S, f"head {n}x{k} B={nb}")
         del qw, dw
+
+
+# ----------------------------------------------------------------- tiled weight layout
+# "Filling in the blanks", section GPU Performance Heisenbugs: weights in groups of
+# columns so that a decode warp reads whole cache lines (q8_pack_tile16, Q8G_LAYOUT_TILE16).
+# Only the addresses differ from the row layout, so the outputs must match it bit for bit.
+
+
+@pytest.mark.parametrize("n,k,nb", SHAPES)
+def test_batch_tiled_equals_rows(q8, orc, n, k, nb):
+    print_case("q8_gemv_batch tiled", n, k, nb)
+    qw, dw, x, r = batch_case(n, k, nb, 2 * n + k + nb)
+    qx, dx = quantize_batch(q8, x)
+    y_rows = host(q8.q8_gemv_batch(dev(qw), h16(dw), qx, dx, residual=dev(r)))
+    t16 = q8.pack_tile16(qw, dw)
+    y_tile = host(q8.q8_gemv_batch(t16, None, qx, dx, residual=dev(r)))
+    assert np.array_equal(y_rows.view(np.uint32), y_tile.view(np.uint32)), "tiled layout differs from rows"
+    yr, S = orc.q8_gemv_batch(qw, dw, host(qx), bits16(dx), r, nthreads=8)
+    within(y_tile, yr, S, f"tiled {n}x{k} B={nb}")
+
+
+@pytest.mark.parametrize("n,k,nb", [(100, 1024, 16), (40000, 1024, 7), (33, 96, 16)])
+def test_batch_tiled_unit_scales_bit_exact(q8, orc, n, k, nb):
+    print_case("tiled unit scales", n, k, nb)
+    g = synth.rng_for(synth.TAG_TEST, 951)
+    qw = g.integers(-128, 128, (n, k)).astype(np.int8)
+    qx = g.integers(-127, 128, (nb, k)).astype(np.int8)
+    dw = np.full((n, k // 32), 0x3C00, np.uint16)
+    dx = np.full((nb, k // 32), 0x3C00, np.uint16)
+    y = host(q8.q8_gemv_batch(q8.pack_tile16(qw, dw), None, dev(qx), h16(dx)))
+    yr, _ = orc.q8_gemv_batch(qw, dw, qx, dx, nthreads=8)
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("n,nb", [(1, 1), (17, 3), (4097, 16)])
+def test_batch_tiled_guards(q8, n, nb):
+    import torch
+
+    k = 96
+    print_case("tiled guards", n, nb)
+    qw, dw, x, r = batch_case(n, k, nb, 990 + n)
+    qx, dx = quantize_batch(q8, x)
+    buf = torch.full((nb * n + 128,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[:64] = 1234.5
+    buf[64 + nb * n:] = 1234.5
+    q8.q8_gemv_batch(q8.pack_tile16(qw, dw), None, qx, dx, y=buf[64:64 + nb * n].view(nb, n), residual=dev(r))
+    h = host(buf)
+    assert np.all(h[:64] == 1234.5) and np.all(h[64 + nb * n:] == 1234.5), "wrote outside y"
+    assert not np.isnan(h[64:64 + nb * n]).any(), "y not fully written"
+
+
+def test_batch_tiled_full_size_head(q8, orc):
+    """The 0.8B output head 151936 x 1024 at B = 16 in the tiled layout (the launch the
+    bench's tiled head line times): identical to the row layout, sampled rows vs the oracle."""
+    import torch
+
+    n, k, nb = 151936, 1024, 16
+    print_case("tiled full-size head", n, k, nb)
+    g = synth.rng_for(synth.TAG_Q8_HEAD, 200 + nb)
+    qw, dw = synth.q8_weights(g, n, k)
+    x = np.stack([synth.activation_f32(g, k) for _ in range(nb)])
+    qx, dx = quantize_batch(q8, x)
+    y_rows = host(q8.q8_gemv_batch(dev(qw), h16(dw), qx, dx))
+    y_tile = host(q8.q8_gemv_batch(q8.pack_tile16(qw, dw), None, qx, dx))
+    assert np.array_equal(y_rows.view(np.uint32), y_tile.view(np.uint32))
+    rows = np.unique(np.concatenate([np.arange(0, n, 1013), [n - 1]]))
+    yr, S = orc.q8_gemv_batch(qw[rows], dw[rows], host(qx), bits16(dx), nthreads=8)
+    within(y_tile[:, rows], yr, S, "tiled head")
+    torch.cuda.synchronize()
