@@ -206,6 +206,24 @@ def graph_trials(torch, fn, reps, trials):
     return out
 
 
+def same_shape_probe(torch, q8, bufs, reps, warmup, flush_buf=None):
+    """The read ceiling of the workload's own launch pattern: one plain-read probe launch
+    over each buffer (the weight planes the GEMV launches read), in the same order, as one
+    HIP graph (with flush_buf: one replay after a cache-evicting write, as the cold timing).
+    Returns (seconds per replay, bytes read per replay)."""
+    sink = torch.empty(q8.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    flat = [b.view(-1).view(torch.uint8) for b in bufs]
+
+    def fn():
+        for b in flat:
+            q8.probe_read(b, sink)
+
+    nbytes = sum(b.numel() for b in flat)
+    if flush_buf is not None:
+        return cold_seconds(torch, q8, fn, flush_buf), nbytes
+    return graph_seconds(torch, fn, reps, warmup), nbytes
+
+
 def cold_seconds(torch, q8, fn, flush_buf, reps=10):
     """A few launches (too few to amortize the events): one graph replay after a
     1 GiB cache-evicting write, bracketed by HIP events; median of reps."""
@@ -408,6 +426,13 @@ def run_stack(args, torch, q8, np):
             "graph": "hipGraph, q8_quantize_act + GEMV per projection (194 launches per token)",
             "decode_stack": "one q8_decode_stack launch per token"}[mode]
 
+    # the same-shape ceiling: one plain-read launch per projection over its code plane
+    # (96% of the step's bytes), in step order: 97 launches of the step's sizes, one graph
+    # per token, as the reported mode launches them
+    t_probe, probe_bytes = same_shape_probe(torch, q8, [b["qw"] for b in stack.bufs], args.steps, args.warmup)
+    log(f"[bench] same-shape probe: {len(ops)} projections' code planes read by {len(ops)} plain-read "
+        f"launches in one graph: {t_probe * 1e6:.1f} us per token, {probe_bytes / t_probe / 1e9:.0f} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_stack(ops, host, orc)
@@ -434,6 +459,12 @@ def run_stack(args, torch, q8, np):
         "tok_per_s": round(1.0 / t_step, 1),
         "probe_GBps": round(probe, 1),
         "pct_of_probe": round(100 * value / probe, 2),
+        "same_shape_probe": {"what": "plain reads of every projection's code plane, one launch per "
+                                     "projection, in one graph per token",
+                             "launches_per_token": len(ops), "bytes_per_token": probe_bytes,
+                             "ms_per_token": round(t_probe * 1e3, 4),
+                             "GBps": round(probe_bytes / t_probe / 1e9, 1),
+                             "step_time_over_probe_time": round(t_step / t_probe, 3)},
         "modes_ms_per_step": {"fused_graph": round(t_fused * 1e3, 4), "quantize_gemv_graph": round(t_graph * 1e3, 4),
                               "decode_stack": round(t_persist * 1e3, 4), "eager_no_graph": round(t_eager * 1e3, 4)},
         "trials_ms_per_step": {"trials": len(trials), "median": round(float(np.median(trials)) * 1e3, 4),
@@ -763,9 +794,19 @@ def run_single(args, torch, q8, np):
                 m["qx"], m["dx"] = m["qx"].view(nb, k), m["dx"].view(nb, k // 32)
                 m["y"] = torch.empty((nb, n), dtype=torch.float32, device="cuda")
 
+    if dt == "q8" and nb > 1:
+        # the weights also in the tiled layout (packed once on the host, as at load time);
+        # the reported call uses it, the row layout is timed beside it
+        t0 = time.time()
+        for m in mats:
+            hq = m["w"].cpu().numpy()
+            hd = m["dw"].cpu().view(torch.int16).numpy().view(np.uint16)
+            m["t16"] = q8.pack_tile16(hq, hd)
+        log(f"[bench] {copies} copies packed into the tiled layout in {time.time() - t0:.1f}s")
+
     def call(m):
         if dt == "q8" and nb > 1:
-            q8.q8_gemv_batch(m["w"], m["dw"], m["qx"], m["dx"], y=m["y"])
+            q8.q8_gemv_batch(m["t16"], None, m["qx"], m["dx"], y=m["y"])
         elif dt == "q8":
             q8.q8_gemv(m["w"], m["dw"], m["qx"], m["dx"], y=m["y"])
         else:
@@ -836,6 +877,26 @@ def run_single(args, torch, q8, np):
         torch.cuda.synchronize()
         calls = reps * copies
         t = a.elapsed_time(b) * 1e-3 / calls
+        t_rows = None
+        if dt == "q8" and nb > 1:
+            t_rows = graph_seconds(torch, lambda: [q8.q8_gemv_batch(m["w"], m["dw"], m["qx"], m["dx"], y=m["y"])
+                                                   for m in mats], reps, 1) / copies
+            log(f"[bench] row layout: {t_rows * 1e6:.2f} us per call, {per / t_rows / 1e9:.0f} GB/s; "
+                f"tiled layout: {t * 1e6:.2f} us, {per / t / 1e9:.0f} GB/s")
+    # the same-shape ceiling: a plain-read launch over each call's weight buffer(s), in the
+    # same order and timed the same way
+    pbufs = [t for m in mats for t in (([m["t16"].codes, m["t16"].scales] if nb > 1 else [m["w"], m["dw"]])
+                                       if dt == "q8" else [m["w"]])]
+    if cold:
+        tp, pbytes = same_shape_probe(torch, q8, pbufs[:2], 0, 0, flush_buf=flush_buf)
+        tp_call = tp
+    else:
+        tp, pbytes = same_shape_probe(torch, q8, pbufs, max(1, -(-args.steps // copies)),
+                                      max(1, -(-args.warmup // copies)))
+        tp_call = tp / copies
+        pbytes //= copies
+    log(f"[bench] same-shape probe: {pbytes} bytes per call read by plain-read launches: "
+        f"{tp_call * 1e6:.2f} us per call, {pbytes / tp_call / 1e9:.0f} GB/s")
     cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np, nb=nb)
     gbps = per / t / 1e9
     if nb > 1:
@@ -851,10 +912,16 @@ def run_single(args, torch, q8, np):
         "vs_baseline": None, "dtype": {"q8": "int8", "bf16": "bf16", "f16": "f16"}[dt], "data": "synthetic",
         "config": {"workload": wl, "n": n, "k": k, "vectors": nb, "copies": copies, "cold_cache": cold,
                    "bytes_per_call": per,
-                   "call": ("q8_gemv_batch" if nb > 1 else "q8_gemv") if dt == "q8" else "gemv_stacked, two halves",
+                   "call": ("q8_gemv_batch, tiled weight layout" if nb > 1 else "q8_gemv") if dt == "q8"
+                   else "gemv_stacked, two halves",
+                   "row_layout_us_per_call": round(t_rows * 1e6, 3) if (not cold and t_rows) else None,
                    "timing": "per call after a 1 GiB flush" if cold else "HIP graph over one pass of the copies"},
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
         "pct_of_probe": round(100 * gbps / probe, 2),
+        "same_shape_probe": {"what": "plain-read launches over each call's weight planes, same order and timing",
+                             "bytes_per_call": pbytes, "us_per_call": round(tp_call * 1e6, 3),
+                             "GBps": round(pbytes / tp_call / 1e9, 1),
+                             "call_time_over_probe_time": round(t / tp_call, 3)},
         "equiv_tok_per_s": round(gbps * 1e9 / stack_bytes, 1) if nb == 1 else None,
         "vectors_per_s": round(nb / t, 1),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,

@@ -14,19 +14,20 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(const int4 *__restrict_
                                                          uint32_t *__restrict__ sink)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint32_t acc = 0;
     constexpr int U = 8;
-    for (; i + (U - 1) * stride < n16; i += U * stride) {
+    // U strided loads in flight per thread in every round, the last round too: indexes
+    // past the end re-read the last element (cached) and are left out of the digest
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += U * stride) {
         int4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = q8g::load16_stream(src + i + u * stride);
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = i + u * stride;
+            v[u] = q8g::load16_stream(src + (j < n16 ? j : n16 - 1));
+        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc ^= (uint32_t)(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
-    }
-    for (; i < n16; i += stride) {
-        const int4 a = src[i];
-        acc ^= (uint32_t)(a.x ^ a.y ^ a.z ^ a.w);
+        for (int u = 0; u < U; ++u)
+            if (i + u * stride < n16) acc ^= (uint32_t)(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
     }
     // one digest word per block, written by a vector store from lane 0
     for (int off = 32; off > 0; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
@@ -63,7 +64,11 @@ q8g_status q8g_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *
     int64_t n16 = bytes / 16;
     uint32_t *k = sink;
     void *args[] = {&s, &n16, &k};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&probe_kernel), dim3(kBlocks),
+    // about eight 16-byte loads per thread, so that a small buffer is read by a grid
+    // of its own size (the same shape as a GEMV launch over it), at most kBlocks
+    int64_t blocks = (n16 + kThreads * 8 - 1) / (kThreads * 8);
+    blocks = blocks < 1 ? 1 : blocks > kBlocks ? kBlocks : blocks;
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&probe_kernel), dim3((unsigned)blocks),
                                          dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
