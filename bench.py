@@ -39,6 +39,8 @@ Other workloads (per-call figures; a step is one call):
   q8-layers-0.8b-b16    the same layers for 16 decode streams at once: per layer 4 q8_gemv_batch launches
                         and 4 batched neighbour-step launches (normalize+quantize, quantize,
                         normalize+quantize, silu*up+quantize); 194 launches per step of 16 tokens
+  ptq1-gateup-2x17408x5120  PTQ1_0 ternary gate+up (2 x 17408 rows, K 5120, 39 MB of 28-byte blocks):
+                        one rotate+quantize of the input and one stacked GEMV per step, rotating copies
 
 Timing: inputs are resident in HBM before the timed region; W untimed warm-up steps,
 then K timed steps between two synchronizations, measured with HIP events on the
@@ -62,7 +64,7 @@ METRIC = "achieved HBM GB/s (% of peak) for Q8_0/bf16 decode GEMV; equiv. tok/s"
 WORKLOADS = ["q8-stack-0.8b", "q8-stack-0.8b-b16", "q8-gateup-7168x1024", "q8-head-151936x1024-b16",
              "bf16-gateup-7168x1024", "f16-gateup-7168x1024", "bf16-gateup-18432x2560-x36", "q8-head-131072x5120",
              "q8-rmsnorm-qkv-4096x1024", "q8-silumul-down-1024x3584", "q8-mlp-0.8b", "q8-layers-0.8b",
-             "q8-layers-0.8b-b16"]
+             "q8-layers-0.8b-b16", "ptq1-gateup-2x17408x5120"]
 NORM_EPS = 1e-6  # RMS-normalization epsilon of the neighbour-step workloads
 BATCH = 16  # decode streams of the -b16 workloads
 
@@ -77,6 +79,7 @@ KERNEL_SOURCES = {
     "quantize_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
     "batch_kernel": ("batch.hip", "gemv_device.hpp", "q8gemv.h"),
     "stack_kernel": ("stack.hip", "gemv_device.hpp", "q8gemv.h"),
+    "ptq1_kernels": ("ptq1.hip", "gemv_device.hpp", "q8gemv.h"),
 }
 
 
@@ -1457,6 +1460,134 @@ def run_layers_b16(args, torch, q8, np):
     }
 
 
+def run_ptq1(args, torch, q8, np):
+    """PTQ1_0 gate+up of a 27B-class layer ("Filling in the blanks", section PrismML
+    Ternary-Bonsai: ternary weights, 128 in 28 bytes, the activation rotated once and shared
+    by the projections that read it): a step is one ptq1_rotate_quantize_act of the f32
+    input and one gemv_stacked over the gate and up halves (2 x 17408 rows, K = 5120),
+    rotating over >= 1 GiB of copies in one HIP graph."""
+    import oracle
+    import synth
+
+    orc = oracle.get()
+    n, k = 17408, 5120
+    nblk = k // synth.PTQ1_BLOCK
+    row = nblk * synth.PTQ1_BYTES
+    per = synth.ptq1_rotate_bytes(k) + 2 * synth.ptq1_gemv_bytes(n, k) - (k + 2 * nblk)  # codes read once by both halves
+    wbytes = 2 * n * row
+    copies = max(2, -(-(1 << 30) // wbytes))
+    t0 = time.time()
+    g = synth.rng_for(synth.TAG_PTQ1, 0)
+    w0g, _, _ = synth.ptq1_weights(g, n, k)
+    w0u, _, _ = synth.ptq1_weights(g, n, k)
+    x0 = synth.activation_f32(g, k)
+    tg = torch.Generator(device="cuda")
+    mats = []
+    for j in range(copies):
+        if j == 0:
+            w = torch.from_numpy(np.concatenate([w0g, w0u])).cuda()
+            x = torch.from_numpy(x0).cuda()
+        else:
+            # timing-only copies, the generator's distribution drawn on the device: a trit byte
+            # of five independent uniform trits is uniform over 0..242, byte 25 (three trits)
+            # over 0..26; scales |N(0,1)| * 0.02 rounded to binary16
+            tg.manual_seed(7919 * j + 17)
+            w = torch.randint(0, 243, (2 * n, nblk, synth.PTQ1_BYTES), dtype=torch.uint8, device="cuda",
+                              generator=tg)
+            w[:, :, 25] = torch.randint(0, 27, (2 * n, nblk), dtype=torch.uint8, device="cuda", generator=tg)
+            sc = (torch.randn((2 * n, nblk), device="cuda", generator=tg).abs() * 0.02).to(torch.float16)
+            w[:, :, 26:28] = sc.view(torch.uint8).view(2 * n, nblk, 2)
+            w = w.view(2 * n, row)
+            x = torch.randn(k, device="cuda", generator=tg)
+        mats.append({"w": w, "x": x, "qx": torch.empty(k, dtype=torch.int8, device="cuda"),
+                     "dx": torch.empty(nblk, dtype=torch.float16, device="cuda"),
+                     "y": torch.empty(2 * n, dtype=torch.float32, device="cuda")})
+    log(f"[bench] {copies} PTQ1_0 gate+up copies ({wbytes / 1e6:.1f} MB each) in {time.time() - t0:.1f}s")
+
+    def call(m):
+        q8.ptq1_rotate_quantize_act(m["x"], m["qx"], m["dx"])
+        q8.gemv_stacked([{"w": m["w"][:n], "y": m["y"][:n]}, {"w": m["w"][n:], "y": m["y"][n:]}], m["qx"], m["dx"])
+
+    call(mats[0])
+    torch.cuda.synchronize()
+    _, rq, rd = orc.ptq1_activation(x0)
+    if not (np.array_equal(mats[0]["qx"].cpu().numpy(), rq)
+            and np.array_equal(mats[0]["dx"].cpu().view(torch.int16).numpy().view(np.uint16), rd)):
+        raise SystemExit("parity: rotated, quantized activation differs from the oracle")
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(7).integers(0, n, 256)]))
+    worst = 0.0
+    yg = mats[0]["y"].cpu().numpy()
+    for half, wh in ((0, w0g), (1, w0u)):
+        yr, S = orc.ptq1_gemv(wh[rows], rq, rd)
+        rel = np.abs(yg[half * n + rows].astype(np.float64) - yr) / S
+        worst = max(worst, float(rel.max()))
+    if worst > 1e-5:
+        raise SystemExit(f"parity: sampled rows off by {worst:.2e} * S")
+    log(f"[bench] parity: rotated codes and scales bit-exact; {2 * len(rows)} sampled rows, worst |err|/S = "
+        f"{worst:.2e}")
+    probe = probe_gbps(q8, torch)
+    log(f"[bench] pure-read probe: {probe:.0f} GB/s")
+    reps = max(1, -(-args.steps // copies))
+    t = graph_seconds(torch, lambda: [call(m) for m in mats], reps, max(1, -(-args.warmup // copies))) / copies
+    t_rot = graph_seconds(torch, lambda: [q8.ptq1_rotate_quantize_act(m["x"], m["qx"], m["dx"]) for m in mats],
+                          reps, 1) / copies
+    t_gemv = graph_seconds(torch, lambda: [q8.gemv_stacked([{"w": m["w"][:n], "y": m["y"][:n]},
+                                                            {"w": m["w"][n:], "y": m["y"][n:]}], m["qx"], m["dx"])
+                                           for m in mats], reps, 1) / copies
+    tp, pbytes = same_shape_probe(torch, q8, [m["w"] for m in mats], reps, 1)
+    tp /= copies
+    pbytes //= copies
+    gbps = per / t / 1e9
+    gemv_bytes = 2 * synth.ptq1_gemv_bytes(n, k) - (k + 2 * nblk)
+    log(f"[bench] step (rotate + stacked GEMV): {t * 1e6:.2f} us, {gbps:.0f} GB/s; rotate alone {t_rot * 1e6:.2f} us, "
+        f"stacked GEMV alone {t_gemv * 1e6:.2f} us ({gemv_bytes / t_gemv / 1e9:.0f} GB/s); same-shape probe "
+        f"{tp * 1e6:.2f} us ({pbytes / tp / 1e9:.0f} GB/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle over a row sample of copy 0 (both halves), scaled to the step's bytes
+        nth = cpu_threads()
+        sample = 2048
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            orc.ptq1_activation(x0)
+            orc.ptq1_gemv(w0g[:sample], rq, rd, nthreads=nth)
+            orc.ptq1_gemv(w0u[:sample], rq, rd, nthreads=nth)
+            calls += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt_ = time.perf_counter() - t0
+        sb = synth.ptq1_rotate_bytes(k) + 2 * synth.ptq1_gemv_bytes(sample, k) - (k + 2 * nblk)
+        cg = calls * sb / dt_ / 1e9
+        log(f"[bench] oracle on {nth} host threads: {cg:.3f} GB/s ({calls} samples of 2 x {sample} rows)")
+        cpu = {"value": round(cg, 4), "unit": "GB/s", "cores": nth, "host_cores": os.cpu_count(),
+               "threads_note": f"min(host cores, {HOST_SHARE_THREADS}): one GPU's share of the host",
+               "kind": "oracle", "sample": f"{calls} x (rotate of the input + 2 x {sample} rows of gate and up), "
+                                           f"{calls * sb} algorithmic bytes in {dt_:.1f} s", "cpu": cpu_model()}
+    rows_pw, waves = q8.gemv_config(q8.Q8G_PTQ1_0, 2 * n, k)
+    kname = f"ptq1 gemv_kernel[rows_per_step={rows_pw},waves={waves}]"
+    return {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps * copies,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "ptq1-gateup-2x17408x5120", "n": 2 * n, "k": k, "format": "PTQ1_0",
+                   "copies": copies, "bytes_per_step": per,
+                   "call": "ptq1_rotate_quantize_act + gemv_stacked (gate, up)",
+                   "timing": "HIP graph over one pass of the copies"},
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "probe_GBps": round(probe, 1),
+        "pct_of_probe": round(100 * gbps / probe, 2),
+        "parts_us": {"rotate": round(t_rot * 1e6, 3), "stacked_gemv": round(t_gemv * 1e6, 3)},
+        "same_shape_probe": {"what": "plain-read launches over each step's weight blocks, same order and timing",
+                             "bytes_per_call": pbytes, "us_per_call": round(tp * 1e6, 3),
+                             "GBps": round(pbytes / tp / 1e9, 1), "step_time_over_probe_time": round(t / tp, 3)},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gemv_bytes / t_gemv / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gemv_bytes / t_gemv / 1e9 / HBM_PEAK_GBPS, 4),
+                     "avg_launch_us": round(t_gemv * 1e6, 3), "bytes_per_launch": gemv_bytes,
+                     "note": "the base-3 decode (table lookups and int8 dots), not the HBM stream, sets the time",
+                     "traffic": traffic_for(kname)},
+        "cpu_baseline": cpu,
+    }
+
+
 def counter_run(args, torch, q8, np):
     """A short, untimed run for hardware-counter passes: a 1 GiB pure read (probe) and a
     1 GiB write (flush) of known size to calibrate FETCH_SIZE / WRITE_SIZE, then two
@@ -1554,6 +1685,8 @@ def main():
         out = run_layers(args, torch, q8, np)
     elif args.workload == "q8-layers-0.8b-b16":
         out = run_layers_b16(args, torch, q8, np)
+    elif args.workload == "ptq1-gateup-2x17408x5120":
+        out = run_ptq1(args, torch, q8, np)
     else:
         out = run_single(args, torch, q8, np)
     print(json.dumps(out), flush=True)

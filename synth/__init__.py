@@ -281,6 +281,17 @@ def bf16_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
     return b + (n * 4 if residual else 0)
 
 
+def ptq1_rotate_bytes(k: int) -> int:
+    """Algorithmic bytes of one rotate + quantize of a PTQ1_0 input: f32 in, codes + scales out."""
+    return 4 * k + k + (k // PTQ1_BLOCK) * 2
+
+
+def ptq1_gemv_bytes(n: int, k: int, residual: bool = False) -> int:
+    """Algorithmic bytes of one PTQ1_0 GEMV: 28-byte blocks + rotated codes and scales + f32 out (+ residual)."""
+    b = n * (k // PTQ1_BLOCK) * PTQ1_BYTES + k + (k // PTQ1_BLOCK) * 2 + n * 4
+    return b + (n * 4 if residual else 0)
+
+
 def q8_stack_inputs(ops, tag: int = TAG_Q8_STACK):
     """Seeded host inputs for each projection j of a stack: codes, scale bits, f32 input,
     and a residual where the projection folds one in."""
