@@ -122,13 +122,14 @@ def load_library(path: str = LIB_PATH):
     lib.q8g_status_str.argtypes = [ctypes.c_int]
     lib.q8g_status_str.restype = ctypes.c_char_p
     lib.q8g_probe_read.argtypes = [_P, _I64, _P, _P]
+    lib.q8g_probe_read_cached.argtypes = [_P, _I64, _P, _P]
     lib.q8g_flush.argtypes = [_P, _I64, ctypes.c_uint32, _P]
     lib.q8_decode_stack.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
     lib.q8_decode_stack_static.argtypes = [ctypes.POINTER(_StackOp), _P, ctypes.c_int, _P, _P]
     lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
                                     ctypes.POINTER(ctypes.c_int)]
     for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
-               "q8g_probe_read", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
+               "q8g_probe_read", "q8g_probe_read_cached", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
                "q8_decode_stack_static",
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
                "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
@@ -599,6 +600,13 @@ def probe_read(buf, sink, stream=None):
     st = load_library().q8g_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
                                        _stream(stream))
     _check("q8g_probe_read", st)
+
+
+def probe_read_cached(buf, sink, stream=None):
+    """Read every byte of `buf` once with plain (cached) loads (counter calibration)."""
+    st = load_library().q8g_probe_read_cached(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                              _stream(stream))
+    _check("q8g_probe_read_cached", st)
 
 
 def flush(buf, value: int = 0, stream=None):

@@ -10,6 +10,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBlocks = Q8G_PROBE_SINK_WORDS;
 
+// NT: nontemporal (streaming) loads, as the GEMV weights; otherwise plain cached
+// loads, as the activations (the two calibrate the hardware read counters)
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void probe_kernel(const int4 *__restrict__ src, int64_t n16,
                                                          uint32_t *__restrict__ sink)
 {
@@ -23,7 +26,8 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(const int4 *__restrict_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t j = i + u * stride;
-            v[u] = q8g::load16_stream(src + (j < n16 ? j : n16 - 1));
+            const int4 *p = src + (j < n16 ? j : n16 - 1);
+            v[u] = NT ? q8g::load16_stream(p) : q8g::load16(p);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -51,11 +55,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(int4 *__restrict__ buf,
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-}  // namespace
-
-extern "C" {
-
-q8g_status q8g_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+q8g_status probe(bool nt, const void *src, int64_t bytes, uint32_t *sink, void *stream)
 {
     if (bytes < 0 || bytes % 16) return Q8G_ERR_SHAPE;
     if (!src || !sink) return Q8G_ERR_NULL;
@@ -68,9 +68,25 @@ q8g_status q8g_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *
     // of its own size (the same shape as a GEMV launch over it), at most kBlocks
     int64_t blocks = (n16 + kThreads * 8 - 1) / (kThreads * 8);
     blocks = blocks < 1 ? 1 : blocks > kBlocks ? kBlocks : blocks;
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&probe_kernel), dim3((unsigned)blocks),
-                                         dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+    const void *fn = nt ? reinterpret_cast<const void *>(&probe_kernel<true>)
+                        : reinterpret_cast<const void *>(&probe_kernel<false>);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0,
+                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+q8g_status q8g_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+{
+    return probe(true, src, bytes, sink, stream);
+}
+
+q8g_status q8g_probe_read_cached(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+{
+    return probe(false, src, bytes, sink, stream);
 }
 
 q8g_status q8g_flush(void *buf, int64_t bytes, uint32_t value, void *stream)

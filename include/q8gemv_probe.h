@@ -26,8 +26,14 @@ extern "C" {
 
 /* Read `bytes` of `src` once with 16-byte loads (bytes % 16 == 0, src 16-byte
  * aligned), with nontemporal loads, and write one xor digest per workgroup
- * into sink[0..16383], so the loads cannot be dropped. */
+ * into sink[0..16383], so the loads cannot be dropped. The grid is sized to
+ * the buffer (about eight loads per thread, at most 16384 workgroups). */
 q8g_status q8g_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
+/* The same read with plain (cached) loads, the kind the kernels use for data
+ * that other workgroups reuse; with the nontemporal probe it calibrates the
+ * hardware read counters for both kinds of load. */
+q8g_status q8g_probe_read_cached(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
 /* Overwrite `bytes` of `buf` (bytes % 16 == 0, 16-byte aligned) with `value`
  * in every 32-bit word. */
