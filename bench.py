@@ -1462,7 +1462,7 @@ def run_layers_b16(args, torch, q8, np):
 
 def run_ptq1(args, torch, q8, np):
     """PTQ1_0 gate+up of a 27B-class layer ("Filling in the blanks", section PrismML
-    Ternary-Bonsai: ternary weights, 128 in 28 bytes, the activation rotated once and shared
+    Ternary-Bonsai: ternary weights, 128 in 28 bytes, one rotation of the activation reused
     by the projections that read it): a step is one ptq1_rotate_quantize_act of the f32
     input and one gemv_stacked over the gate and up halves (2 x 17408 rows, K = 5120),
     rotating over >= 1 GiB of copies in one HIP graph."""

@@ -42,14 +42,14 @@
 //    for matrices with few tiles, so that enough waves exist); their partial
 //    sums are added in a fixed order through LDS.
 //  * Weight layouts ("Filling in the blanks", section GPU Performance
-//    Heisenbugs: weights stored in groups of columns, so that a decode warp
-//    reads whole cache lines). In the row layout a step's operand load is 16
+//    Heisenbugs: decode weights stored eight columns side by side, so a
+//    warp's loads span full 128-byte lines). In the row layout a step's operand load is 16
 //    rows x 64 bytes, 16 cache lines per KiB, half of each line used by the
 //    step. The tiled layout (Q8G_LAYOUT_TILE16, written once by
 //    q8_pack_tile16) stores each 16-row x 64-column step operand as one
 //    contiguous KiB in the lane order of the load (lane l reads bytes
 //    [16l, 16l + 16)), and each block's 16 row scales side by side, so a step
-//    reads 8 whole cache lines. Only addresses differ: both layouts compute
+//    covers 8 full 128-byte lines. Only addresses differ: both layouts compute
 //    every output with the same instructions in the same order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>

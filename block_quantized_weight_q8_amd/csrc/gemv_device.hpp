@@ -5,8 +5,8 @@
 // Row layout per wave (wave64): a row is streamed in 1 KiB chunks; lane l owns
 // bytes [16l, 16l+16) of every chunk. For Q8_0 a 32-byte block spans lanes 2j
 // and 2j+1 ("Filling in the blanks: Inference using Phobos", section Fast
-// Decode: a block of 32 int8 values carries its own scale; the block math is
-// done end to end in int8). For bf16 a lane's 16 bytes are eight values ("One
+// Decode: a block of 32 int8 values carries its own scale; block products and
+// sums stay in integers). For bf16 a lane's 16 bytes are eight values ("One
 // level down: #002 the same compiler on a GPU", section Emitting for a GPU:
 // rows read as 16-byte chunks of eight bf16).
 #pragma once

@@ -2,8 +2,8 @@
 //
 // What is computed is stated in include/q8gemv.h, after "Filling in the blanks:
 // Inference using Phobos", section PrismML Ternary-Bonsai: weights -1, 0 or +1,
-// 128 of them in 28 bytes, and an activation rotated by a Hadamard transform,
-// computed once per input and shared by every projection that reads it.
+// 128 of them in 28 bytes, against an activation rotated by a Hadamard
+// transform; one rotation per input serves every projection that consumes it.
 //
 // Design (MI355X, wave64):
 //  * Rotation: one workgroup per 128-value block, one output per thread. Each

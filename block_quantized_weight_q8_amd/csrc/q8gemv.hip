@@ -53,8 +53,8 @@ constexpr int kMaxParts = 4;
 // by every workgroup into LDS before use (one launch instead of two); F16:
 // binary16 weights and activation. Q8NORM and Q8SILU are Q8F32 with a neighbour
 // step folded into the prologue ("One level down: #002 the same compiler on a
-// GPU", section Emitting for a GPU: at decode the normalization is fused with
-// the projection after it, and the activation with the projection after it):
+// GPU", section Emitting for a GPU: for decode, two kernels each merge a
+// neighbour step into the next projection, the normalization and the activation):
 // Q8NORM quantizes (x * r) * gamma, r = 1/sqrt(mean(x^2) + eps); Q8SILU takes
 // x = [gate | up] (2K values) and quantizes silu(gate) * up.
 enum class Dt { Q8, BF16, Q8F32, F16, Q8NORM, Q8SILU };

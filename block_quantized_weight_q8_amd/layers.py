@@ -1,11 +1,12 @@
 """Decode layers with their neighbour steps, run through the C ABI.
 
-"One level down: #002 the same compiler on a GPU", section Emitting for a GPU: at
-decode the normalization is fused with the projection after it and the
-activation with the projection after it. "Filling in the blanks: Inference using
+"One level down: #002 the same compiler on a GPU", section Emitting for a GPU: for
+decode, two kernels each merge a neighbour step into the next projection, one the
+normalization and one the activation. "Filling in the blanks: Inference using
 Phobos", section Q4_K_M, names a block's operations: RMS normalization before the
-attention and MLP projections, and the gated MLP; section Fast Decode: quantize an
-activation once, fold the residual add into the matmul, replay the pass as a graph.
+attention and MLP projections, and the gated MLP; section Fast Decode: one activation
+quantization reused by all consumers, the residual added inside the matmul, the whole pass
+recorded once and replayed as a graph.
 
 Q8LayerChain runs the projections of every layer with the real data flow through
 the residual stream h (attention itself is not part of this path; its output is a

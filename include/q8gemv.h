@@ -4,11 +4,11 @@
  *
  * Sources (by page title and section):
  *   [P] "Filling in the blanks: Inference using Phobos", section "Fast Decode":
- *       decode reads every weight once per token with one multiply and one add
- *       per weight; a Q8_0 block is 32 int8 values carrying their own scale;
- *       the block math runs end to end in int8; an activation is quantized once
- *       and shared; projections reading the same input are stacked; the
- *       residual add is folded into the matmul.
+ *       a decode step touches each weight exactly once, for one fused
+ *       multiply-add (two flops) per weight; a Q8_0 block is 32 int8 values carrying their own scale;
+ *       block products and sums stay in integers; one quantization of an
+ *       activation serves all its consumers; the projections of one input run
+ *       as one launch; the matmul also adds the residual.
  *   [H] "One level down: #002 the same compiler on a GPU", sections "Emitting
  *       for a GPU" (gate and up computed in one go; a weight row read as
  *       16-byte chunks of eight bf16; the last row index guards the tail) and
@@ -17,8 +17,8 @@
  *   [T] "Filling in the blanks: Inference using Phobos", section "PrismML
  *       Ternary-Bonsai": ternary weights (-1, 0, +1), 128 of them in 28 bytes
  *       (PTQ1_0), with the activation rotated by a Hadamard transform, which
- *       spreads outliers over the block; the rotated activation is computed
- *       once and shared by every projection that reads the same input.
+ *       evens out large values across the block; one rotation per input
+ *       serves every projection that consumes that input.
  *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE pointers owned by the caller. The exceptions
@@ -124,8 +124,8 @@ q8g_status q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx,
                          const float *residual, float *y, int64_t N, int64_t K, int64_t B, void *stream);
 
 /* ---- weight layout of the small-batch GEMV ----------------------------------
- * [P] GPU Performance Heisenbugs: storing the weights in groups of columns lets
- * a decode warp read whole cache lines. Q8G_LAYOUT_ROWS is the plain [N][K]
+ * [P] GPU Performance Heisenbugs: decode weights stored eight columns side by
+ * side, so a warp's loads span full 128-byte lines. Q8G_LAYOUT_ROWS is the plain [N][K]
  * codes and [N][K/32] scales of q8_gemv_batch. Q8G_LAYOUT_TILE16 groups 16 rows:
  *   codes: tile t (rows 16t..16t+15) and step s (columns 64s..64s+63) form one
  *          1024-byte unit at byte (t * S + s) * 1024, S = ceil(K / 64); inside
@@ -172,17 +172,17 @@ typedef struct {
     const float *residual; /* f32 [n] or NULL; may equal y */
 } q8g_part;
 
-/* Stacked projection ([P] Fast Decode: stack projections that read the same
- * input; [H] Emitting for a GPU: gate and up in one go). One launch computes
+/* Stacked projection ([P] Fast Decode: the projections of one input run as
+ * one launch; [H] Emitting for a GPU: gate and up in one go). One launch computes
  * every part against the shared input: Q8_0 takes x = int8 codes [K] and
  * dx = binary16 scale bits [K/32]; bf16 and f16 take x = bf16 / f16 [K] and
  * ignore dx;
  * Q8G_Q8_0_F32 takes x = f32 [K] (16-byte aligned, K <= 16384), quantizes it
- * inside the launch, and ignores dx ([P] Fast Decode: quantize the activation
- * once and share it, here once per launch for all of its parts).
+ * inside the launch, and ignores dx ([P] Fast Decode: one quantization of the
+ * activation serves all its consumers; here, all the parts of the launch).
  * Q8G_PTQ1_0 takes x = the rotated codes int8 [K] and dx = binary16 scale
- * bits [K/128] of ptq1_rotate_quantize_act ([T]: the rotated activation shared
- * by the projections that read it), with the rules of ptq1_gemv.
+ * bits [K/128] of ptq1_rotate_quantize_act ([T]: one rotation per input for
+ * all the projections that consume it), with the rules of ptq1_gemv.
  * Part p's result is identical, bit for bit, to q8_gemv / bf16_gemv /
  * ptq1_gemv called on that part alone (for Q8G_Q8_0_F32: to q8_quantize_act
  * then q8_gemv). 1 <= nparts <= 4. */
@@ -207,7 +207,7 @@ q8g_status gemv_stacked(q8g_dtype dtype, const q8g_part *parts, int nparts, cons
 #define Q8G_PTQ1_MAX_K 65536
 #define Q8G_PTQ1_MAX_ROWS (1 << 30)
 
-/* Rotate an activation and quantize it for PTQ1_0 weights ([T]: computed once
+/* Rotate an activation and quantize it for PTQ1_0 weights ([T]: one rotation
  * per input). For each block b of 128 consecutive values of x (f32 [K]):
  *   r_i = fl32( (sum_{j<128} (-1)^popcount(i & j) * x_{128b+j}) / sqrt(128) )
  *         (the sum in f64 in ascending j, sqrt(128) the nearest f64, the
@@ -232,9 +232,9 @@ q8g_status ptq1_gemv(const uint8_t *w, const int8_t *qx, const uint16_t *dx, con
                      int64_t N, int64_t K, void *stream);
 
 /* ---- neighbour steps folded into the projection --------------------------
- * [H] Emitting for a GPU: at decode the normalization runs fused with the
- * projection that follows it, and the activation with the projection that
- * follows it. [P] Q4_K_M names the operations of a block's forward pass: RMS
+ * [H] Emitting for a GPU: for decode, two kernels each merge a neighbour step
+ * into the next projection, one the normalization and one the activation.
+ * [P] Q4_K_M names the operations of a block's forward pass: RMS
  * normalization before the attention and MLP projections, and the gated MLP.
  * The values that get quantized are formed in f32 exactly as follows:
  *   RMS normalization (x, gamma f32 [K], eps >= 0 finite):

@@ -10,11 +10,11 @@
  *
  * Sources (cited by page title and section):
  *   [P]  "Filling in the blanks: Inference using Phobos", section "Fast Decode":
- *        decode reads every weight once and does one multiply and one add per
- *        weight; a Q8_0 block is 32 int8 values that carry their own scale; the
- *        block math is done end to end in int8 (4-way int8 dot); an activation
- *        is quantized once and shared; projections that read the same input are
- *        stacked; the residual add is folded into the matmul.
+ *        a decode step touches each weight exactly once, for one fused
+ *        multiply-add (two flops) per weight; a Q8_0 block is 32 int8 values that carry their own scale; the
+ *        block products and sums stay in int8/int32 (4-way int8 dot); one
+ *        quantization of an activation serves all its consumers; projections of
+ *        one input run as one launch; the matmul also adds the residual.
  *   [H]  "One level down: #002 the same compiler on a GPU", sections "Emitting
  *        for a GPU" (the bf16 gate+up matvec, rows of 16-byte chunks; at
  *        decode the normalization and the activation are each fused with the
@@ -171,8 +171,8 @@ void orc_quantize_act(const float *x, int64_t K, int8_t *qx, uint16_t *dx)
 }
 
 /* ---- neighbour steps folded into a projection's prologue ([H] Emitting for a
- * GPU: at decode the normalization is fused with the projection after it, and
- * the activation with the projection after it; [P] Q4_K_M: a norm used inside
+ * GPU: for decode, two kernels each merge a neighbour step into the next
+ * projection, one the normalization and one the activation; [P] Q4_K_M: a norm used inside
  * the fused kernels). The pages name these steps without formulas; the
  * readings here are the standard ones of the models the pages run.
  *
@@ -202,7 +202,7 @@ void orc_silu_mul(const float *gu, int64_t K, float *a)
     }
 }
 
-/* ---- block integer dot ([P] Fast Decode: the block math end to end in int8) */
+/* ---- block integer dot ([P] Fast Decode: block products and sums kept in integers) */
 void orc_block_isums(const int8_t *qw, const int8_t *qx, int64_t N, int64_t K, int32_t *isum)
 {
     int64_t nb = K / ORC_QBLOCK;
@@ -300,9 +300,9 @@ void orc_q8_gemv_batch(const int8_t *qw, const uint16_t *dw, const int8_t *qx, c
 }
 
 /* ---- PTQ1_0 ternary blocks ([P] PrismML Ternary-Bonsai: weights -1, 0 or +1;
- * 128 weights in 28 bytes; the activation rotated by a Hadamard transform, which
- * spreads outliers over the whole block; the rotated activation computed once and
- * shared by every projection that reads the same input). The pages give no byte
+ * 128 weights in 28 bytes; a Hadamard rotation of the activation, which evens out
+ * large values across each block; one rotation per input serves every projection
+ * that consumes that input). The pages give no byte
  * layout; the readings (listed in the design notes) are:
  *   - a block is 26 bytes of base-3 digits followed by its binary16 scale s
  *     (2 bytes, little-endian); weight i (0..127) of the block is

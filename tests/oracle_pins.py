@@ -694,8 +694,8 @@ def pin_ptq1_activation_quantizer(o):
 
 
 def pin_ptq1_rotation_spreads_outlier(o):
-    """[P] §PrismML Ternary-Bonsai: the rotation spreads an outlier over the whole block, so
-    quantization loses less. One 128-value block with a single large value: quantized
+    """[P] §PrismML Ternary-Bonsai: the rotation evens out a large value across its block,
+    which makes quantization less lossy. One 128-value block with a single large value: quantized
     directly, the small values fall below one code step; rotated, quantized, dequantized and
     rotated back, they survive."""
     g = rng(44)

@@ -222,8 +222,9 @@ def test_batch_full_size_head(q8, orc):
 
 
 # ----------------------------------------------------------------- tiled weight layout
-# "Filling in the blanks", section GPU Performance Heisenbugs: weights in groups of
-# columns so that a decode warp reads whole cache lines (q8_pack_tile16, Q8G_LAYOUT_TILE16).
+# "Filling in the blanks", section GPU Performance Heisenbugs: the decode weights are stored
+# eight columns side by side, which makes a warp's loads span full 128-byte lines
+# (q8_pack_tile16, Q8G_LAYOUT_TILE16).
 # Only the addresses differ from the row layout, so the outputs must match it bit for bit.
 
 

@@ -1,8 +1,8 @@
 """PTQ1_0 HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
 
 "Filling in the blanks: Inference using Phobos", section PrismML Ternary-Bonsai:
-ternary weights, 128 in 28 bytes, and a Hadamard-rotated activation computed once
-and shared by the projections that read it.
+ternary weights, 128 in 28 bytes, against a Hadamard-rotated activation; one rotation
+per input serves all the projections that consume it.
 
 Bars: rotated values, codes and scale bits bit-exact (the rotation is an f64 sum in
 index order on both sides, rounded once to f32); unit-scale results bit-exact (every
@@ -186,7 +186,7 @@ def test_gemv_invalid_bytes(q8, orc):
 @pytest.mark.parametrize("k", [1024, 2560, 5120])
 def test_stacked_equals_single(q8, orc, k):
     """gemv_stacked over gate and up (and over 4 ragged parts) gives the bits of one
-    ptq1_gemv per part: the rotated activation is computed once and shared."""
+    ptq1_gemv per part: one rotation of the input serves every part."""
     print_case("ptq1 stacked", k)
     g = synth.rng_for(synth.TAG_TEST, 1300 + k)
     sizes = [300, 300, 7, 129]

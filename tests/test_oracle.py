@@ -35,7 +35,7 @@ def test_page_shape_constants():
 
 
 def test_decode_intensity_about_two_ops_per_byte():
-    """Decode does one multiply and one add per weight read once (Phobos, Fast Decode):
+    """A decode step touches each weight once, two flops per weight (Phobos, Fast Decode):
     with 1-byte codes plus a 2-byte scale per 32, the ratio sits just under 2."""
     n, k = 7168, 1024
     ops_per_byte = 2 * n * k / synth.q8_gemv_bytes(n, k)

@@ -1,7 +1,8 @@
 """The tiled weight layout of the small-batch GEMV (q8_pack_tile16), on the CPU.
 
-"Filling in the blanks: Inference using Phobos", section GPU Performance Heisenbugs:
-weights stored in groups of columns so that a decode warp reads whole cache lines.
+"Filling in the blanks: Inference using Phobos", section GPU Performance Heisenbugs, stores
+the decode weights eight columns side by side, which makes a warp's loads span full
+128-byte lines.
 The pack is a pure permutation with zero padding, checked here element by element
 against the layout built independently with numpy reshapes.
 """
