@@ -78,6 +78,7 @@ KERNEL_SOURCES = {
     "gemv_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
     "quantize_kernel": ("q8gemv.hip", "gemv_device.hpp", "q8gemv.h"),
     "batch_kernel": ("batch.hip", "gemv_device.hpp", "q8gemv.h"),
+    "stream_kernel": ("batch.hip", "gemv_device.hpp", "q8gemv.h"),
     "stack_kernel": ("stack.hip", "gemv_device.hpp", "q8gemv.h"),
     "ptq1_gemv_kernel": ("ptq1.hip", "gemv_device.hpp", "q8gemv.h"),
 }
@@ -903,8 +904,11 @@ def run_single(args, torch, q8, np):
     cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np, nb=nb)
     gbps = per / t / 1e9
     if nb > 1:
-        ks, sf = q8.batch_config(n)
-        kname = f"batch_kernel<{ks}, {sf}, tiled layout>"
+        if q8.batch_tiled_streams(n, k):
+            kname = f"stream_kernel<{-(-k // 64)} steps, tiled layout>"
+        else:
+            ks, sf = q8.batch_config(n)
+            kname = f"batch_kernel<{ks}, {sf}, tiled layout>"
     else:
         r, w_ = q8.gemv_config({"q8": q8.Q8G_Q8_0, "bf16": q8.Q8G_BF16, "f16": q8.Q8G_F16}[dt], n, k)
         kname = f"{dt}_gemv[rows_per_wave={r},waves={w_}]"

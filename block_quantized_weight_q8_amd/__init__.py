@@ -103,6 +103,7 @@ def load_library(path: str = LIB_PATH):
     lib.f16_gemv.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
     lib.q8_gemv_batch.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
     lib.q8g_batch_config.argtypes = [_I64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.q8g_batch_tiled_streams.argtypes = [_I64, _I64, ctypes.POINTER(ctypes.c_int)]
     lib.q8_gemv_batch_layout.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
     lib.q8_tile16_sizes.argtypes = [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     lib.q8_pack_tile16.argtypes = [_P, _P, _I64, _I64, _P, _P]
@@ -129,7 +130,8 @@ def load_library(path: str = LIB_PATH):
     lib.q8g_gemv_config.argtypes = [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_int),
                                     ctypes.POINTER(ctypes.c_int)]
     for fn in ("q8_quantize_act", "q8_gemv", "q8_gemv_batch", "bf16_gemv", "f16_gemv", "gemv_stacked",
-               "q8g_probe_read", "q8g_probe_read_cached", "q8g_flush", "q8g_gemv_config", "q8g_batch_config", "q8_decode_stack",
+               "q8g_probe_read", "q8g_probe_read_cached", "q8g_flush", "q8g_gemv_config", "q8g_batch_config",
+               "q8g_batch_tiled_streams", "q8_decode_stack",
                "q8_decode_stack_static",
                "q8_rmsnorm_quantize_act", "q8_silu_mul_quantize_act", "gemv_stacked_rmsnorm",
                "q8_gemv_silu_mul", "q8_gateup_silu_quantize", "q8_gateup_rmsnorm_silu_quantize",
@@ -345,6 +347,14 @@ def batch_config(n):
     ks, sf = ctypes.c_int(), ctypes.c_int()
     _check("q8g_batch_config", load_library().q8g_batch_config(n, ctypes.byref(ks), ctypes.byref(sf)))
     return ks.value, sf.value
+
+
+def batch_tiled_streams(n, k):
+    """True when q8_gemv_batch on an n x k Tile16 (16-byte aligned scales) streams whole
+    tiles per wave (the persistent form), False when it takes batch_config(n)'s shape."""
+    st = ctypes.c_int()
+    _check("q8g_batch_tiled_streams", load_library().q8g_batch_tiled_streams(n, k, ctypes.byref(st)))
+    return bool(st.value)
 
 
 def q8_gemv_f32(qw, dw, x, y=None, residual=None, stream=None):

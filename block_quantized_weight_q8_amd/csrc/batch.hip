@@ -121,6 +121,44 @@ __device__ __forceinline__ void wait_counts()
     __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (lgkm << 8));
 }
 
+// Direct copies of the activation codes and scales of columns [k0, k0 + kt)
+// into LDS, requested by every wave of the workgroup (one wave's loads
+// complete in issue order, so these are older than any weight request that
+// follows). Codes: LDS chunk position p -> vector p / rowc16, chunk
+// (p % rowc16) ^ vector; positions past the real chunks copy chunk 0 of their
+// vector and are never read. Scales: LDS dword t -> block t / 16, vector t % 16
+// (vectors past B copy vector B-1; their outputs are never stored).
+template <class SH>
+__device__ __forceinline__ void stage_activation(uint8_t *s_lds, const int8_t *__restrict__ qx,
+                                                 const uint16_t *__restrict__ dx, int64_t K, int64_t k0, int kt,
+                                                 int B, int wave, int lane)
+{
+    constexpr int W = SH::W;
+    uint8_t *const s_codes = s_lds + SH::kCodesOff;
+    const int64_t nb = K / 32;
+    const int nbt = kt / 32;
+    const int cpv = kt / 16;
+    const int rowc16 = (cpv + 15) & ~15;
+    const int code_pos = B * rowc16;
+    for (int p0 = wave * kWave; p0 < code_pos; p0 += W * kWave) {
+        const int p = p0 + lane;
+        const int b = p / rowc16, c = (p - b * rowc16) ^ (b & 15);
+        const int bb = b < B ? b : B - 1;
+        const int cc = c < cpv ? c : 0;
+        if (p < code_pos)
+            __builtin_amdgcn_global_load_lds(qx + (int64_t)bb * K + k0 + 16 * cc, s_codes + 16 * p0, 16, 0, 0);
+    }
+    const int dx_pos = nbt * kBatchMax;
+    for (int p0 = wave * kWave; p0 < dx_pos; p0 += W * kWave) {
+        const int t = p0 + lane;
+        const int blk = t / kBatchMax, b = t - blk * kBatchMax;
+        const int bb = b < B ? b : B - 1;
+        if (t < dx_pos)
+            __builtin_amdgcn_global_load_lds(dx + (int64_t)bb * nb + k0 / 32 + blk, s_lds + SH::kDxOff + 4 * p0, 2,
+                                             0, 0);
+    }
+}
+
 template <class SH, bool TILED>
 __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__restrict__ qw,
                                                             const uint16_t *__restrict__ dw,
@@ -129,7 +167,7 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
                                                             const float *residual, float *y, int64_t N, int64_t K,
                                                             int B)
 {
-    constexpr int W = SH::W, S = SH::S, P = SH::P, TK = SH::TK;
+    constexpr int S = SH::S, P = SH::P, TK = SH::TK;
     __shared__ __align__(16) uint8_t s_lds[SH::kLds];
     uint8_t *const s_codes = s_lds + SH::kCodesOff;
     const float *const s_dxf = reinterpret_cast<const float *>(s_lds + SH::kDxOff);
@@ -184,30 +222,9 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
         const int steps = (kt + kStepK - 1) / kStepK;
         const int s_begin = steps * split / S, s_end = steps * (split + 1) / S;
 
-        // 1. direct copies into LDS, requested first (one wave's loads complete
-        //    in issue order). Codes: LDS chunk position p -> vector p / rowc16,
-        //    chunk (p % rowc16) ^ vector; positions past the real chunks copy
-        //    chunk 0 of their vector and are never read.
-        const int code_pos = B * rowc16;
-        for (int p0 = wave * kWave; p0 < code_pos; p0 += W * kWave) {
-            const int p = p0 + lane;
-            const int b = p / rowc16, c = (p - b * rowc16) ^ (b & 15);
-            const int bb = b < B ? b : B - 1;
-            const int cc = c < cpv ? c : 0;
-            if (p < code_pos)
-                __builtin_amdgcn_global_load_lds(qx + (int64_t)bb * K + k0 + 16 * cc, s_codes + 16 * p0, 16, 0, 0);
-        }
-        //    Activation scales: LDS dword t -> block t / 16, vector t % 16
-        //    (vectors past B copy vector B-1; their outputs are never stored).
+        // 1. direct copies of the activation into LDS, requested first
+        stage_activation<SH>(s_lds, qx, dx, K, k0, kt, B, wave, lane);
         const int dx_pos = nbt * kBatchMax;
-        for (int p0 = wave * kWave; p0 < dx_pos; p0 += W * kWave) {
-            const int t = p0 + lane;
-            const int blk = t / kBatchMax, b = t - blk * kBatchMax;
-            const int bb = b < B ? b : B - 1;
-            if (t < dx_pos)
-                __builtin_amdgcn_global_load_lds(dx + (int64_t)bb * nb + k0 / 32 + blk,
-                                                 s_lds + SH::kDxOff + 4 * p0, 2, 0, 0);
-        }
         //    Weight scales of this wave's rows and steps, into its region of the
         //    tile's area: LDS dword t -> row t / nbw, block t % nbw of the
         //    wave's blocks (rows past N read row N-1; a missing second block of
@@ -332,6 +349,160 @@ __global__ __launch_bounds__(SH::kThreads) void batch_kernel(const int8_t *__res
     }
 }
 
+// Many tiles, K <= TK, tiled layout: the whole-row shape made persistent. Each
+// workgroup stages the activation once; each wave then streams its own tiles
+// (every GW-th tile from its global wave index, GW waves in all) back to back,
+// with one rolling window of P steps that runs across tile boundaries, so a
+// wave's requests never drain between tiles. A tile's 16 x nb weight scales
+// are nb * 32 contiguous bytes in the tiled layout: lane l < 2 nb requests
+// bytes [16 l, 16 l + 16) one tile ahead, and the wave writes them to its own
+// LDS area when the tile's first step is consumed (one wave's LDS accesses
+// complete in order, so no barrier is needed). The residuals are requested one
+// tile ahead as well. Every step runs the batched kernel's arithmetic in the
+// same order, so the outputs equal its outputs bit for bit. Eight waves per
+// workgroup and about eight per compute unit: measured on MI355X for the
+// 151936 x 1024 head at 16 vectors, more waves per unit (two workgroups on
+// one unit, or sixteen-wave workgroups) and four-wave workgroups were slower.
+using StreamShape = Shape<8, 1, 8, 1024>;
+constexpr int kStreamScaleBytes = kTileRows * (StreamShape::TK / 32) * 2;  // one tile's scales
+constexpr int kStreamLds = StreamShape::kWscOff + StreamShape::W * kStreamScaleBytes;
+static_assert(kStreamLds <= 160 * 1024, "LDS per workgroup");
+
+template <int STEPS, bool RES>
+__global__ __launch_bounds__(StreamShape::kThreads) void stream_kernel(const int8_t *__restrict__ qw,
+                                                                       const uint16_t *__restrict__ dw,
+                                                                       const int8_t *__restrict__ qx,
+                                                                       const uint16_t *__restrict__ dx,
+                                                                       const float *residual, float *y, int64_t N,
+                                                                       int64_t K, int B, int ntiles)
+{
+    using SH = StreamShape;
+    constexpr int W = SH::W, P = SH::P;
+    static_assert(STEPS % P == 0 && STEPS * kStepK <= SH::TK, "whole windows per tile, one staging pass");
+    __shared__ __align__(16) uint8_t s_lds[kStreamLds];
+    const float *const s_dxf = reinterpret_cast<const float *>(s_lds + SH::kDxOff);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int j = lane & 15;  // weight row in the tile / activation vector of the operand
+    const int q = lane >> 4;  // 16-byte k group of a step
+    const int gw = blockIdx.x * W + wave, GW = gridDim.x * W;
+    const int nt = gw < ntiles ? (ntiles - 1 - gw) / GW + 1 : 0;  // this wave's tiles
+    const int kt = (int)K;                                         // (STEPS - 1) * 64 < K <= STEPS * 64
+    const int nb = kt / 32;
+    const int rowc16 = (kt / 16 + 15) & ~15;
+    uint8_t *const s_wsc = s_lds + SH::kWscOff + wave * kStreamScaleBytes;
+    const uint16_t *const s_ws16 = reinterpret_cast<const uint16_t *>(s_wsc);
+    auto tile_of = [&](int i) { return gw + i * GW; };  // the wave's tile i (i < nt)
+
+    if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(s_lds) = make_uint4(0u, 0u, 0u, 0u);  // the zero slot
+    stage_activation<SH>(s_lds, qx, dx, K, 0, kt, B, wave, lane);
+
+    // Requests are unconditional, with clamped addresses: lanes past a tile's
+    // scale bytes re-read its first chunk, residuals of vectors past B and rows
+    // past N read clamped elements (never stored), requests past the wave's
+    // last tile re-read it, and a wave without tiles requests the last tile's
+    // first steps. So every path issues the same loads in the same order after
+    // the copies above, and the compiler's wait counts keep the window in flight.
+    const int sl = lane < 2 * nb ? lane : 0;
+    auto tile_scales = [&](int t) {
+        return *reinterpret_cast<const int4 *>(dw + (int64_t)t * nb * kTileRows + 8 * sl);
+    };
+    auto tile_residuals = [&](int t, float (&r)[4]) {
+        const int64_t row = (int64_t)t * kTileRows + j;
+        const int64_t rr = row < N ? row : N - 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = 4 * q + k < B ? 4 * q + k : B - 1;
+            r[k] = residual[(int64_t)b * N + rr];
+        }
+    };
+    auto weights = [&](int t, int st) {
+        return load16_stream(qw + ((int64_t)t * STEPS + st) * 1024 + 16 * lane);
+    };
+
+    const int t0 = nt > 0 ? gw : ntiles - 1;
+    int4 wv[P];
+    int4 sc = tile_scales(t0);
+    float res_nx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (RES) tile_residuals(t0, res_nx);
+#pragma unroll
+    for (int p = 0; p < P; ++p) wv[p] = weights(t0, p);
+
+    // the copies are older than the weight window: wait for them only, then a
+    // bare barrier
+    wait_counts<P + 1 + (RES ? 4 : 0), 0>();
+    __builtin_amdgcn_s_barrier();
+    const int dx_pos = nb * kBatchMax;
+    for (int t = threadIdx.x; t < dx_pos; t += SH::kThreads) {
+        uint32_t *v = reinterpret_cast<uint32_t *>(s_lds + SH::kDxOff) + t;
+        *v = __builtin_bit_cast(uint32_t, f16_bits_to_f32((uint16_t)*v));
+    }
+    wait_counts<63, 0>();
+    __builtin_amdgcn_s_barrier();
+
+    for (int i = 0; i < nt; ++i) {
+        // tile i: its scales into the wave's area (its earlier reads are
+        // complete: one wave's LDS accesses run in order); the next tile's
+        // scales and residuals requested
+        if (lane < 2 * nb) *reinterpret_cast<int4 *>(s_wsc + 16 * lane) = sc;
+        float res[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) res[k] = res_nx[k];
+        const bool more = i + 1 < nt;
+        const int t = tile_of(i), tn = tile_of(more ? i + 1 : i);
+        sc = tile_scales(tn);
+        if (RES) tile_residuals(tn, res_nx);
+
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int p = st % P;
+            const bool hi = st * kStepK + 32 < kt;
+            const v4i zero = {0, 0, 0, 0};
+            const int c = 4 * st + q;
+            const uint32_t at = SH::kCodesOff + 16u * (uint32_t)(j * rowc16 + (c ^ j));
+            const bool lo_ok = j < B && q < 2, hi_ok = j < B && q >= 2 && hi;
+            const v4i a_lo = *reinterpret_cast<const v4i *>(s_lds + (lo_ok ? at : 0u));
+            const v4i a_hi = *reinterpret_cast<const v4i *>(s_lds + (hi_ok ? at : 0u));
+            const v4i w = as_v4i(wv[p]);
+            const v4i i0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo, w, zero, 0, 0, 0);
+            const v4i i1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi, w, zero, 0, 0, 0);
+            const int blk = 2 * st;
+            const float4 x0 = *reinterpret_cast<const float4 *>(s_dxf + blk * kBatchMax + 4 * q);
+            const float4 x1 = hi ? *reinterpret_cast<const float4 *>(s_dxf + (blk + 1) * kBatchMax + 4 * q)
+                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            // a missing second block reads the first block's scale; its product is zero
+            const float w0 = f16_bits_to_f32(s_ws16[blk * kTileRows + j]);
+            const float w1 = f16_bits_to_f32(s_ws16[(hi ? blk + 1 : blk) * kTileRows + j]);
+            acc[0] = __builtin_fmaf((float)i0[0], w0 * x0.x, acc[0]);
+            acc[1] = __builtin_fmaf((float)i0[1], w0 * x0.y, acc[1]);
+            acc[2] = __builtin_fmaf((float)i0[2], w0 * x0.z, acc[2]);
+            acc[3] = __builtin_fmaf((float)i0[3], w0 * x0.w, acc[3]);
+            acc[0] = __builtin_fmaf((float)i1[0], w1 * x1.x, acc[0]);
+            acc[1] = __builtin_fmaf((float)i1[1], w1 * x1.y, acc[1]);
+            acc[2] = __builtin_fmaf((float)i1[2], w1 * x1.z, acc[2]);
+            acc[3] = __builtin_fmaf((float)i1[3], w1 * x1.w, acc[3]);
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+            // the step P ahead: in this tile, or the next (past the last tile, its
+            // last step again)
+            if (st + P < STEPS) {
+                wv[p] = weights(t, st + P);
+            } else {
+                wv[p] = weights(tn, more ? st + P - STEPS : STEPS - 1);
+            }
+        }
+        const int64_t row = (int64_t)t * kTileRows + j;
+        if (row < N) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int b = 4 * q + k;
+                if (b < B) y[(int64_t)b * N + row] = RES ? acc[k] + res[k] : acc[k];
+            }
+        }
+    }
+}
+
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
@@ -351,6 +522,51 @@ hipError_t launch(bool tiled, const int8_t *qw, const uint16_t *dw, const int8_t
     const void *fn = tiled ? reinterpret_cast<const void *>(&batch_kernel<SH, true>)
                            : reinterpret_cast<const void *>(&batch_kernel<SH, false>);
     return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(SH::kThreads), args, 0, s);
+}
+
+// The persistent streaming form serves the tiled layout of matrices with many
+// tiles whose K fits one staging pass (output heads of the small models); its
+// tile scales are read as 16-byte chunks, so dw must be 16-byte aligned.
+constexpr int kStreamWavesPerUnit = 8;  // waves per compute unit the tile split aims for
+constexpr int kUnits = 256;             // compute units of an MI355X
+
+bool stream_shape(int64_t N, int64_t K)
+{
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    const int64_t steps = (K + kStepK - 1) / kStepK;
+    return tiles > kSplitTiles && (steps == 8 || steps == 16) && tiles * steps <= (int64_t)INT32_MAX;
+}
+
+bool stream_fits(bool tiled, const uint16_t *dw, int64_t N, int64_t K)
+{
+    return tiled && stream_shape(N, K) && aligned(dw, 16);
+}
+
+// Every wave takes ceil(tiles / waves) or one tile fewer: the number of waves is
+// the fewest that give each at most ceil(tiles / (kUnits * kStreamWavesPerUnit))
+// tiles, rounded up to whole workgroups.
+int64_t stream_groups(int64_t tiles)
+{
+    const int64_t target = (int64_t)kUnits * kStreamWavesPerUnit;
+    const int64_t per_wave = (tiles + target - 1) / target;
+    const int64_t waves = (tiles + per_wave - 1) / per_wave;
+    return (waves + StreamShape::W - 1) / StreamShape::W;
+}
+
+q8g_status launch_stream(const int8_t *qw, const uint16_t *dw, const int8_t *qx, const uint16_t *dx,
+                         const float *residual, float *y, int64_t N, int64_t K, int B, hipStream_t s)
+{
+    int ntiles = (int)((N + kTileRows - 1) / kTileRows);
+    void *args[] = {&qw, &dw, &qx, &dx, &residual, &y, &N, &K, &B, &ntiles};
+    const bool r = residual != nullptr;
+    const void *fn = (K + kStepK - 1) / kStepK == 16
+                         ? (r ? reinterpret_cast<const void *>(&stream_kernel<16, true>)
+                              : reinterpret_cast<const void *>(&stream_kernel<16, false>))
+                         : (r ? reinterpret_cast<const void *>(&stream_kernel<8, true>)
+                              : reinterpret_cast<const void *>(&stream_kernel<8, false>));
+    const hipError_t e =
+        hipLaunchKernel(fn, dim3((unsigned)stream_groups(ntiles)), dim3(StreamShape::kThreads), args, 0, s);
+    return e == hipSuccess ? Q8G_OK : Q8G_ERR_LAUNCH;
 }
 
 // bytes of the tiled codes and scales of an N x K matrix (rows padded to whole
@@ -385,6 +601,7 @@ q8g_status batch_run(int layout, const int8_t *qw, const uint16_t *dw, const int
     if (residual && residual != y && overlap(y, ybytes, residual, ybytes)) return Q8G_ERR_OVERLAP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    if (stream_fits(tiled, dw, N, K)) return launch_stream(qw, dw, qx, dx, residual, y, N, K, (int)B, s);
     const hipError_t e =
         tiles <= kWideSplitTiles ? launch<WideSplitShape>(tiled, qw, dw, qx, dx, residual, y, N, K, (int)B, s)
         : tiles <= kSplitTiles   ? launch<SplitShape>(tiled, qw, dw, qx, dx, residual, y, N, K, (int)B, s)
@@ -457,5 +674,13 @@ extern "C" q8g_status q8g_batch_config(int64_t N, int *k_split, int *steps_in_fl
     *k_split = tiles <= kWideSplitTiles ? WideSplitShape::S : tiles <= kSplitTiles ? SplitShape::S : WholeShape::S;
     *steps_in_flight = tiles <= kWideSplitTiles ? WideSplitShape::P : tiles <= kSplitTiles ? SplitShape::P
                                                                                           : WholeShape::P;
+    return Q8G_OK;
+}
+
+extern "C" q8g_status q8g_batch_tiled_streams(int64_t N, int64_t K, int *streams)
+{
+    if (N < 0 || K < 0 || K % 32 || N > kMaxElems || K > kMaxK) return Q8G_ERR_SHAPE;
+    if (!streams) return Q8G_ERR_NULL;
+    *streams = stream_shape(N, K) ? 1 : 0;
     return Q8G_OK;
 }

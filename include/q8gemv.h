@@ -162,6 +162,15 @@ q8g_status q8_pack_tile16(const int8_t *qw, const uint16_t *dw, int64_t N, int64
  * in flight. Pure host query; nothing is enqueued. */
 q8g_status q8g_batch_config(int64_t N, int *k_split, int *steps_in_flight);
 
+/* Launch form q8_gemv_batch_layout picks for an N x K matrix in the tiled layout
+ * whose scales are 16-byte aligned: *streams = 1 when each wave streams whole
+ * 16-row tiles back to back with one staging of the activation (more than 2048
+ * tiles and K of 8 or 16 64-column steps: 448 < K <= 512 or 960 < K <= 1024),
+ * 0 when the launch takes the shape q8g_batch_config reports. Same outputs
+ * either way. Pure host query; Q8G_ERR_SHAPE for N < 0, K < 0 or K % 32 != 0,
+ * Q8G_ERR_NULL for a null streams. */
+q8g_status q8g_batch_tiled_streams(int64_t N, int64_t K, int *streams);
+
 /* One matrix of a stacked projection. */
 typedef struct {
     const void *w;         /* Q8_0: int8 codes [n][K]; bf16 / f16: uint16 [n][K];

@@ -271,6 +271,70 @@ def test_batch_tiled_guards(q8, n, nb):
     assert not np.isnan(h[64:64 + nb * n]).any(), "y not fully written"
 
 
+# The persistent streaming form of the tiled layout: more than 2048 tiles, K of 8 or 16
+# steps (K in (448, 512] or (960, 1024]) and 16-byte aligned scales. Each wave streams its
+# tiles back to back; every step keeps the batched kernel's arithmetic, so the outputs equal
+# the row layout's bit for bit.
+STREAM_SHAPES = [
+    (32785, 1024, 16),  # 2050 tiles, the last holding one row
+    (33000, 992, 5),    # 16 steps, the last a single block
+    (40000, 512, 1),    # 8 steps, one vector
+    (36017, 480, 16),   # 8 steps, the last a single block; ragged rows
+    (65536, 1024, 3),   # 4096 tiles: waves with unequal tile counts
+]
+
+
+@pytest.mark.parametrize("n,k,nb", STREAM_SHAPES)
+@pytest.mark.parametrize("resid", [False, True])
+def test_batch_tiled_stream(q8, orc, n, k, nb, resid):
+    print_case("tiled stream", n, k, nb, resid)
+    qw, dw, x, r = batch_case(n, k, nb, 7 * n + k + nb, resid)
+    qx, dx = quantize_batch(q8, x)
+    res = dev(r) if resid else None
+    y_rows = host(q8.q8_gemv_batch(dev(qw), h16(dw), qx, dx, residual=res))
+    y_tile = host(q8.q8_gemv_batch(q8.pack_tile16(qw, dw), None, qx, dx, residual=res))
+    assert np.array_equal(y_rows.view(np.uint32), y_tile.view(np.uint32)), "streamed tiles differ from rows"
+    g = np.random.default_rng(n + k)
+    last = (n - 1) // 16 * 16
+    rows = np.unique(np.concatenate([[0, 15, 16, last, n - 1], np.arange(last, n), g.integers(0, n, 200)]))
+    yr, S = orc.q8_gemv_batch(qw[rows], dw[rows], host(qx), bits16(dx), None if r is None else r[:, rows],
+                              nthreads=8)
+    within(y_tile[:, rows], yr, S, f"tiled stream {n}x{k} B={nb}")
+
+
+def test_batch_tiled_stream_unaligned_scales(q8):
+    """Scales that are not 16-byte aligned take the whole-row shape instead: same bits."""
+    import torch
+
+    n, k, nb = 32785, 1024, 4
+    print_case("tiled stream, unaligned scales", n, k, nb)
+    qw, dw, x, _ = batch_case(n, k, nb, 4242, resid=False)
+    qx, dx = quantize_batch(q8, x)
+    t16 = q8.pack_tile16(qw, dw)
+    y_a = host(q8.q8_gemv_batch(t16, None, qx, dx))
+    buf = torch.empty(t16.scales.numel() + 8, dtype=t16.scales.dtype, device="cuda")
+    sc = buf[1:1 + t16.scales.numel()]
+    sc.copy_(t16.scales)
+    y_u = host(q8.q8_gemv_batch(q8.Tile16(t16.codes, sc, n, k), None, qx, dx))
+    assert np.array_equal(y_a.view(np.uint32), y_u.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k,nb", [(32785, 1024, 3), (40001, 512, 16)])
+def test_batch_tiled_stream_guards(q8, n, k, nb):
+    import torch
+
+    print_case("tiled stream guards", n, k, nb)
+    qw, dw, x, r = batch_case(n, k, nb, 77 + n)
+    qx, dx = quantize_batch(q8, x)
+    buf = torch.full((nb * n + 128,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[:64] = 1234.5
+    buf[64 + nb * n:] = 1234.5
+    q8.q8_gemv_batch(q8.pack_tile16(qw, dw), None, qx, dx, y=buf[64:64 + nb * n].view(nb, n), residual=dev(r))
+    h = host(buf)
+    assert np.all(h[:64] == 1234.5) and np.all(h[64 + nb * n:] == 1234.5), "wrote outside y"
+    assert not np.isnan(h[64:64 + nb * n]).any(), "y not fully written"
+
+
 def test_batch_tiled_full_size_head(q8, orc):
     """The 0.8B output head 151936 x 1024 at B = 16 in the tiled layout (the launch the
     bench's tiled head line times): identical to the row layout, sampled rows vs the oracle."""

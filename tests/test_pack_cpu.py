@@ -26,6 +26,7 @@ def lib():
     L.q8_pack_tile16.argtypes = [P, P, I64, I64, P, P]
     L.q8_tile16_sizes.argtypes = [I64, I64, ctypes.POINTER(I64), ctypes.POINTER(I64)]
     L.q8_gemv_batch_layout.argtypes = [ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P]
+    L.q8g_batch_tiled_streams.argtypes = [I64, I64, ctypes.POINTER(ctypes.c_int)]
     return L
 
 
@@ -101,3 +102,21 @@ def test_layout_validation(lib):
     # the tiled codes of 8 x 64 take 16 x 64 bytes: y just past the row layout's end still overlaps
     assert g(1, W, DW, QX, DX, None, W + 8 * 64, 8, 64, 2, None) == ERR_OVERLAP
     assert g(1, None, None, None, None, None, None, 0, 64, 2, None) == OK
+
+
+def test_tiled_streams_query(lib):
+    """The persistent streaming form: more than 2048 tiles and K of 8 or 16 64-column steps."""
+    def q(n, k):
+        v = ctypes.c_int(-1)
+        assert lib.q8g_batch_tiled_streams(n, k, ctypes.byref(v)) == OK
+        return v.value
+
+    assert q(151936, 1024) == 1                         # the 0.8B output head
+    assert q(2049 * 16, 1024) == 1 and q(2048 * 16, 1024) == 0 and q(2048 * 16 + 1, 1024) == 1
+    assert q(40000, 992) == 1 and q(40000, 960) == 0    # 16 steps, 15 steps
+    assert q(40000, 512) == 1 and q(40000, 480) == 1 and q(40000, 448) == 0
+    assert q(40000, 2048) == 0 and q(40000, 5120) == 0 and q(0, 1024) == 0
+    v = ctypes.c_int()
+    assert lib.q8g_batch_tiled_streams(40000, 1000, ctypes.byref(v)) == ERR_SHAPE
+    assert lib.q8g_batch_tiled_streams(-1, 1024, ctypes.byref(v)) == ERR_SHAPE
+    assert lib.q8g_batch_tiled_streams(40000, 1024, None) == ERR_NULL
