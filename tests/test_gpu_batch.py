@@ -302,21 +302,25 @@ def test_batch_tiled_stream(q8, orc, n, k, nb, resid):
     within(y_tile[:, rows], yr, S, f"tiled stream {n}x{k} B={nb}")
 
 
-def test_batch_tiled_stream_unaligned_scales(q8):
-    """Scales that are not 16-byte aligned take the whole-row shape instead: same bits."""
+@pytest.mark.parametrize("n,k,nb,resid", [(32785, 1024, 4, False), (40001, 512, 16, True)])
+def test_batch_tiled_stream_unaligned_scales(q8, n, k, nb, resid):
+    """Tiled scales that are not 16-byte aligned take the whole-row shape instead: the same
+    bits as the streaming form, and as the row layout."""
     import torch
 
-    n, k, nb = 32785, 1024, 4
-    print_case("tiled stream, unaligned scales", n, k, nb)
-    qw, dw, x, _ = batch_case(n, k, nb, 4242, resid=False)
+    print_case("tiled stream vs whole-row shape (unaligned scales)", n, k, nb, resid)
+    qw, dw, x, r = batch_case(n, k, nb, 4242 + n, resid=resid)
     qx, dx = quantize_batch(q8, x)
+    res = dev(r) if resid else None
     t16 = q8.pack_tile16(qw, dw)
-    y_a = host(q8.q8_gemv_batch(t16, None, qx, dx))
+    y_a = host(q8.q8_gemv_batch(t16, None, qx, dx, residual=res))
     buf = torch.empty(t16.scales.numel() + 8, dtype=t16.scales.dtype, device="cuda")
     sc = buf[1:1 + t16.scales.numel()]
     sc.copy_(t16.scales)
-    y_u = host(q8.q8_gemv_batch(q8.Tile16(t16.codes, sc, n, k), None, qx, dx))
+    y_u = host(q8.q8_gemv_batch(q8.Tile16(t16.codes, sc, n, k), None, qx, dx, residual=res))
     assert np.array_equal(y_a.view(np.uint32), y_u.view(np.uint32))
+    y_r = host(q8.q8_gemv_batch(dev(qw), h16(dw), qx, dx, residual=res))
+    assert np.array_equal(y_a.view(np.uint32), y_r.view(np.uint32))
 
 
 @pytest.mark.parametrize("n,k,nb", [(32785, 1024, 3), (40001, 512, 16)])
