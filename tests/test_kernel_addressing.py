@@ -142,6 +142,85 @@ def test_batch_shape_constants_are_consistent():
         assert W * 64 * 4 * 4 <= K_BATCH_MAX * TK  # split partial sums fit the code area
 
 
+# --------------------------------------------------------------------------- stream_kernel
+
+
+def stream_constants():
+    src = open(os.path.join(CSRC, "batch.hip")).read()
+    m = re.search(r"using StreamShape = Shape<(\d+), (\d+), (\d+), (\d+)>;", src)
+    assert m
+    wpu = int(re.search(r"kStreamWavesPerUnit = (\d+);", src).group(1))
+    units = int(re.search(r"kUnits = (\d+);", src).group(1))
+    return tuple(int(v) for v in m.groups()), wpu, units
+
+
+def stream_model(N, K, B):
+    """The streaming form of the tiled layout: every tile taken by exactly one wave, every
+    consumed step reading the weights requested for it P requests earlier, every request,
+    scale chunk and residual inside its buffer, every scale read from LDS written first."""
+    (W, S, P, TK), wpu, units = stream_constants()
+    steps = (K + K_STEP_K - 1) // K_STEP_K
+    assert steps in (8, 16) and steps % P == 0 and steps * K_STEP_K <= TK
+    nb = K // 32
+    ntiles = (N + K_TILE_ROWS - 1) // K_TILE_ROWS
+    code_bytes = ntiles * K_TILE_ROWS * steps * K_STEP_K
+    scale_elems = ntiles * K_TILE_ROWS * nb
+    target = units * wpu
+    per_wave = (ntiles + target - 1) // target
+    groups = ((ntiles + per_wave - 1) // per_wave + W - 1) // W
+    GW = groups * W
+    scale_bytes = K_TILE_ROWS * (TK // 32) * 2
+    lds = 16 + (TK // 32) * K_BATCH_MAX * 4 + K_BATCH_MAX * TK + W * scale_bytes
+    assert lds <= 160 * 1024
+    covered = []
+    for gw in range(GW):
+        nt = (ntiles - 1 - gw) // GW + 1 if gw < ntiles else 0
+        assert nt <= per_wave
+        tiles = [gw + i * GW for i in range(nt)]
+        covered += tiles
+        t0 = gw if nt > 0 else ntiles - 1
+        requests = [(t0, p) for p in range(P)]
+        scale_tiles = [t0]
+        for i, t in enumerate(tiles):
+            more = i + 1 < nt
+            tn = tiles[i + 1] if more else t
+            scale_tiles.append(tn)
+            for st in range(steps):
+                requests.append((t, st + P) if st + P < steps else (tn, st + P - steps if more else steps - 1))
+        consumed = [(t, st) for t in tiles for st in range(steps)]
+        assert requests[:len(consumed)] == consumed
+        for t, st in requests:
+            assert 0 <= t < ntiles and 0 <= st < steps
+            assert (t * steps + st) * 1024 + 16 * 63 + 16 <= code_bytes
+        for t in scale_tiles:
+            for lane in range(64):
+                sl = lane if lane < 2 * nb else 0
+                assert t * nb * K_TILE_ROWS + 8 * sl + 8 <= scale_elems
+        # LDS: lanes < 2 nb write 16 bytes each (elements [0, 16 nb)); step st reads blocks
+        # 2 st and, when present, 2 st + 1 of row j
+        assert 32 * nb <= scale_bytes
+        for st in range(steps):
+            hi = st * K_STEP_K + 32 < K
+            for j in range(16):
+                for blk in ([2 * st, 2 * st + 1] if hi else [2 * st]):
+                    assert blk * K_TILE_ROWS + j < 16 * nb
+        for t in tiles:
+            for j in range(16):
+                row = t * K_TILE_ROWS + j
+                rr = row if row < N else N - 1
+                for q in range(4):
+                    for r in range(4):
+                        b = 4 * q + r if 4 * q + r < B else B - 1
+                        assert 0 <= b * N + rr < B * N
+    assert sorted(covered) == list(range(ntiles)), "every tile exactly once"
+
+
+@pytest.mark.parametrize("n,k,b", [(32785, 1024, 16), (2049 * 16, 512, 1), (40000, 992, 5), (36017, 480, 16),
+                                   (65536, 1024, 3), (151936, 1024, 16), (1 << 20, 512, 2)])
+def test_stream_kernel_addressing(n, k, b):
+    stream_model(n, k, b)
+
+
 # --------------------------------------------------------------------------- gemv_kernel
 
 
