@@ -621,6 +621,14 @@ def gpu_processes():
     return {"gpu_pids": pids, "gpu_pids_check": "ok" if not others else f"other processes on the GPU: {others}"}
 
 
+def batch_kname(q8, n, k, tiled):
+    """The profiler-facing name of the kernel q8_gemv_batch runs for an n x k matrix."""
+    if tiled and q8.batch_tiled_streams(n, k):
+        return f"stream_kernel<{-(-k // 64)} steps, tiled layout>"
+    ks, sf = q8.batch_config(n)
+    return f"batch_kernel<{ks}, {sf}{', tiled layout' if tiled else ''}>"
+
+
 # ----------------------------------------------------------------------------- 16 streams
 
 
@@ -674,10 +682,9 @@ def run_batch_stack(args, torch, q8, np):
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     groups = {}
     for i, op in enumerate(ops):
-        groups.setdefault(q8.batch_config(op.n), []).append(i)
+        groups.setdefault(batch_kname(q8, op.n, op.k, bs.tiled), []).append(i)
     per = {}
-    for (ks, sf), idx in groups.items():
-        name = f"batch_kernel<{ks}, {sf}>"
+    for name, idx in groups.items():
         fn = (lambda idx=idx: [bs.launch_gemv(i) for i in idx])
         t = (graph_seconds(torch, fn, max(5, args.steps // 2), args.warmup) if len(idx) >= 8
              else cold_seconds(torch, q8, fn, flush_buf)) / len(idx)
@@ -716,6 +723,7 @@ def run_batch_stack(args, torch, q8, np):
         "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "q8-stack-0.8b-b16", "streams": nb, "layers": 24, "hidden": 1024, "vocab": 151936,
+                   "weight_layout": "tiled" if bs.tiled else "rows",
                    "projections_per_step": len(ops), "launches_per_step": 2 * len(ops), "bytes_per_step": step_bytes,
                    "mode": "hipGraph, q8_quantize_act over 16 inputs + q8_gemv_batch per projection",
                    "accumulate": "int32 per block (matrix cores), f32"},
@@ -904,11 +912,7 @@ def run_single(args, torch, q8, np):
     cpu = None if args.no_cpu_baseline else cpu_baseline_single(dt, first, n, k, per, orc, np, nb=nb)
     gbps = per / t / 1e9
     if nb > 1:
-        if q8.batch_tiled_streams(n, k):
-            kname = f"stream_kernel<{-(-k // 64)} steps, tiled layout>"
-        else:
-            ks, sf = q8.batch_config(n)
-            kname = f"batch_kernel<{ks}, {sf}, tiled layout>"
+        kname = batch_kname(q8, n, k, True)
     else:
         r, w_ = q8.gemv_config({"q8": q8.Q8G_Q8_0, "bf16": q8.Q8G_BF16, "f16": q8.Q8G_F16}[dt], n, k)
         kname = f"{dt}_gemv[rows_per_wave={r},waves={w_}]"
@@ -1393,27 +1397,28 @@ def run_layers_b16(args, torch, q8, np):
         f"{t_step * 1e6:.1f} us/step, {nb / t_step:.0f} tok/s")
     # per GEMV launch group (the library's configuration for each shape)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    launches = []  # (config, fn, bytes)
+    launches = []  # (kernel name, fn, bytes)
     for l in range(L):
         launches += [
-            (q8.batch_config(4096), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l), bc.qx, bc.dx, y=bc.qkv),
+            (batch_kname(q8, 4096, k, bc.tiled), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l), bc.qx, bc.dx, y=bc.qkv),
              synth.q8_batch_gemv_bytes(4096, k, nb)),
-            (q8.batch_config(k), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 1), bc.qo, bc.do, y=bc.h, residual=bc.h),
+            (batch_kname(q8, k, 2048, bc.tiled),
+             lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 1), bc.qo, bc.do, y=bc.h, residual=bc.h),
              synth.q8_batch_gemv_bytes(k, 2048, nb, True)),
-            (q8.batch_config(2 * f), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 2), bc.qx, bc.dx, y=bc.gu),
+            (batch_kname(q8, 2 * f, k, bc.tiled), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 2), bc.qx, bc.dx, y=bc.gu),
              synth.q8_batch_gemv_bytes(2 * f, k, nb)),
-            (q8.batch_config(k), lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 3), bc.qa, bc.da, y=bc.h, residual=bc.h),
+            (batch_kname(q8, k, f, bc.tiled),
+             lambda l=l: q8.q8_gemv_batch(*bc._w(4 * l + 3), bc.qa, bc.da, y=bc.h, residual=bc.h),
              synth.q8_batch_gemv_bytes(k, f, nb, True)),
         ]
-    launches.append((q8.batch_config(ops[-1].n),
+    launches.append((batch_kname(q8, ops[-1].n, k, bc.tiled),
                      lambda: q8.q8_gemv_batch(*bc._w(len(ops) - 1), bc.qx, bc.dx, y=bc.logits),
                      synth.q8_batch_gemv_bytes(ops[-1].n, k, nb)))
     groups = {}
     for cfg, fn, b in launches:
         groups.setdefault(cfg, []).append((fn, b))
     per = {}
-    for (ks, sf), items in groups.items():
-        name = f"batch_kernel<{ks}, {sf}>"
+    for name, items in groups.items():
         fn = (lambda items=items: [it[0]() for it in items])
         tg = (graph_seconds(torch, fn, max(5, args.steps // 2), args.warmup) if len(items) >= 8
               else cold_seconds(torch, q8, fn, flush_buf)) / len(items)
@@ -1454,6 +1459,7 @@ def run_layers_b16(args, torch, q8, np):
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "q8-layers-0.8b-b16", "streams": nb, "layers": L, "hidden": k, "ffn": f,
                    "vocab": ops[-1].n, "launches_per_step": bc.launches_per_token_step(), "bytes_per_step": step_bytes,
+                   "weight_layout": "tiled" if bc.tiled else "rows",
                    "attention": "not part of this path: a seeded f32 stand-in per layer and stream"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2), "tok_per_s": round(nb / t_step, 1),
         "probe_GBps": round(probe, 1),

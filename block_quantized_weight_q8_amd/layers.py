@@ -154,13 +154,19 @@ class Q8BatchLayerChain:
     """nb decode streams through the layers of a Q8DecodeStack (weights shared, not copied).
     inputs: synth.layer_chain_inputs (its normalization weights serve every stream);
     batch_inputs: synth.layer_chain_batch_inputs (per stream the residual stream entering
-    layer 0, h f32 [nb, hidden], and per layer the attention stand-in, f32 [nb, attn_width])."""
+    layer 0, h f32 [nb, hidden], and per layer the attention stand-in, f32 [nb, attn_width]).
+    tiled: the GEMVs read the weights in the tiled layout (packed once here); the outputs are
+    the row layout's bit for bit."""
 
-    def __init__(self, stack, inputs, batch_inputs, eps: float = 1e-6):
+    def __init__(self, stack, inputs, batch_inputs, eps: float = 1e-6, tiled: bool = True):
         self.stack = stack
         self.eps = float(eps)
+        self.tiled = bool(tiled)
         dev = stack.device
         ops = stack.ops
+        if self.tiled:  # the weights packed once into the tiled layout (same outputs, faster)
+            for i in range(len(ops)):
+                stack.tiled(i)
         self.layers = (len(ops) - 1) // 4
         self.hidden = ops[0].k
         self.ffn = ops[2].parts[0]
@@ -184,6 +190,8 @@ class Q8BatchLayerChain:
         self.logits = torch.empty((nb, ops[-1].n), dtype=torch.float32, device=dev)
 
     def _w(self, i):
+        if self.tiled:
+            return self.stack.tiled(i), None
         b = self.stack.bufs[i]
         return b["qw"], b["dw"]
 

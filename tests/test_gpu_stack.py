@@ -260,3 +260,23 @@ def test_batch_stack_graph_replay(q8, orc):
             yr, S = orc.q8_gemv(h["qw"][rows], h["dw"][rows], rq, rd, hb["r"][v][rows] if op.residual else None)
             err = np.abs(r[v][rows].astype(np.float64) - yr)
             assert np.all(err <= 1e-5 * S), f"{op.name} stream {v}: {err.max()}"
+
+
+def test_batch_stack_tiled_equals_rows(q8):
+    """The 16-stream step on weights packed into the tiled layout (the default) equals the step
+    on the row layout bit for bit, the 40000-row head taking the streaming form."""
+    from block_quantized_weight_q8_amd.stack import Q8BatchStack, Q8DecodeStack
+
+    print("case: 1-layer stack + 40000-row head, 16 streams, tiled vs row layout", flush=True)
+    ops = synth.q8_stack_08b(layers=1, vocab=40000)
+    hostin = synth.q8_stack_inputs(ops, synth.TAG_TEST + 7)
+    batch = synth.q8_batch_inputs(ops, 16, synth.TAG_TEST + 8)
+    stack = Q8DecodeStack(ops, hostin)
+    rows = Q8BatchStack(stack, batch, tiled=False)
+    rows.step()
+    ref = [host(b["y"]).copy() for b in rows.bufs]
+    tiled = Q8BatchStack(stack, batch)
+    assert tiled.tiled
+    tiled.step()
+    for op, r, b in zip(ops, ref, tiled.bufs):
+        assert np.array_equal(host(b["y"]).view(np.uint32), r.view(np.uint32)), op.name
