@@ -35,9 +35,10 @@
 //        step, so each load instruction reads R runs of C * 28 contiguous
 //        bytes; W waves cover the nb block columns of a row, and a workgroup
 //        holds G such groups of W waves (up to 16 waves).
-//    Small per-lane state (26 activation registers, 4 per step in flight)
-//    keeps about 30 waves per compute unit: the table reads and the weight
-//    loads of one wave wait while the others compute.
+//    Small per-lane state (26 activation registers, 4 per step in flight,
+//    74 VGPRs in all) leaves the table as the occupancy limit: two workgroups
+//    per compute unit (10 waves at K = 5120), whose table reads and weight
+//    loads wait while the other waves compute.
 //  * The two halves' int32 sums are joined (one DPP add) into the block's
 //    exact sum; times f16(s) * f16(dx) (exact in f32: 11 + 11 significant
 //    bits) it is the block's term, formed by half 1. The C lanes of a row are summed
