@@ -51,6 +51,10 @@
 //    [16l, 16l + 16)), and each block's 16 row scales side by side, so a step
 //    covers 8 full 128-byte lines. Only addresses differ: both layouts compute
 //    every output with the same instructions in the same order.
+//  * Output heads in the tiled layout (many tiles, K of 8 or 16 steps) run a
+//    persistent form (stream_kernel): one 8-wave workgroup per compute unit
+//    stages the activation once, and each wave streams its tiles back to back
+//    with one window of loads across tile boundaries. Same arithmetic, same bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
