@@ -302,6 +302,21 @@ def test_batch_tiled_stream(q8, orc, n, k, nb, resid):
     within(y_tile[:, rows], yr, S, f"tiled stream {n}x{k} B={nb}")
 
 
+@pytest.mark.parametrize("n,k,nb", [(33000, 1024, 7), (40001, 512, 16)])
+def test_batch_tiled_stream_residual_in_place(q8, n, k, nb):
+    """The streaming form reads each tile's residuals a tile ahead of its stores: y aliasing the
+    residual gives the out-of-place bits."""
+    print_case("tiled stream in-place residual", n, k, nb)
+    qw, dw, x, r = batch_case(n, k, nb, 515 + n + nb)
+    qx, dx = quantize_batch(q8, x)
+    t16 = q8.pack_tile16(qw, dw)
+    assert q8.batch_tiled_streams(n, k)
+    oop = host(q8.q8_gemv_batch(t16, None, qx, dx, residual=dev(r)))
+    yr = dev(r)
+    q8.q8_gemv_batch(t16, None, qx, dx, y=yr, residual=yr)
+    assert np.array_equal(host(yr).view(np.uint32), oop.view(np.uint32))
+
+
 @pytest.mark.parametrize("n,k,nb,resid", [(32785, 1024, 4, False), (40001, 512, 16, True)])
 def test_batch_tiled_stream_unaligned_scales(q8, n, k, nb, resid):
     """Tiled scales that are not 16-byte aligned take the whole-row shape instead: the same
